@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the Mamba-2 SSM core at one Nemotron-H-8B layer on one MI355X.
+
+Primary line (the metric's decode half): decode tokens/s of one layer step
+(conv1d_update + state_update) for 256 sequences drawn from a 512-slot bf16
+state pool (128 heads x headdim 64 x d_state 128, 8 groups). The prefill half
+(conv1d_fwd + chunk_scan_fwd over 4 x 8192 tokens, chunk 128, bf16 inputs,
+fp32 state) is reported in the same JSON line under "prefill".
+
+Inputs are seeded synthetic tensors already resident in HBM when timing
+starts. Per-kernel durations come from HIP events on the stream the kernels
+are launched on (torch's current stream, which the binding passes down).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_bytes_per_row(d, state_bytes):
+    """Algorithmic HBM bytes of one decode row-layer, split by kernel."""
+    H, P, N, G, W = d.nheads, d.headdim, d.dstate, d.ngroups, d.conv_width
+    cdim = H * P + 2 * G * N
+    act = 2
+    su = 2 * H * P * N * state_bytes + cdim * act + H * act + H * P * act   # state r+w, x|B|C in, dt in, y out
+    cu = 2 * (W - 1) * cdim * state_bytes + cdim * act + cdim * act          # conv cache r+w, raw in, post out
+    minimum = 2 * H * P * N * state_bytes + 2 * (W - 1) * cdim * state_bytes + cdim * act + H * act + H * P * act
+    return su, cu, minimum
+
+
+def scan_algorithmic(d, tokens, nseq, xbc_bytes, y_bytes, state_bytes):
+    """Bytes and flops the chunk scan must move/compute (causal SSD, per token)."""
+    H, P, N, G, Q = d.nheads, d.headdim, d.dstate, d.ngroups, d.chunk_size
+    cdim = H * P + 2 * G * N
+    nbytes = tokens * (cdim * xbc_bytes + H * 2 + H * P * y_bytes) + nseq * H * P * N * state_bytes
+    # C.B^T (per group, causal) + intra-chunk output (causal) + chunk state + inter-chunk output
+    flops_per_tok = G * Q * N + H * Q * P + 2 * H * P * N + 2 * H * P * N
+    return nbytes, flops_per_tok * tokens
+
+
+def time_region(fn, iters, torch):
+    """Average ms of fn() over iters, HIP events on the current stream."""
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build's hot path runs on a single MI355X "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from state_space_model_ssm_amd import binding as B
+    from state_space_model_ssm_amd import synth
+    from state_space_model_ssm_amd.configs import F32, NEMOTRON_H_8B
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    B.lib()
+
+    def dev(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dt).cuda()
+
+    # ------------------------------------------------------------ decode workload
+    d = NEMOTRON_H_8B
+    rows, nslots = 256, 512
+    log(f"decode workload: {rows} rows, {nslots}-slot bf16 pool; generating inputs")
+    w = synth.decode_batch(d, seed=1, rows=rows, num_slots=nslots, with_z=False)
+    bf = torch.bfloat16
+    ssm = dev(w["ssm_pool"], bf)
+    conv = dev(w["conv_pool"], bf)
+    xbc, dt = dev(w["xbc"], bf), dev(w["dt_raw"], bf)
+    conv_w = dev(w["params"]["conv_w"], torch.float32)
+    A_log, dtb, D = (dev(w["params"][k], torch.float32) for k in ("A_log", "dt_bias", "D"))
+    idx = torch.from_numpy(w["slots"]).cuda()
+    post = torch.empty(rows, d.conv_dim, dtype=bf, device="cuda")
+    y = torch.empty(rows, d.d_inner, dtype=bf, device="cuda")
+    host_params = w["params"]
+    host_tok = {"xbc": w["xbc"][:64].copy(), "dt_raw": w["dt_raw"][:64].copy()}
+    host_slots = w["ssm_pool"][w["slots"][:64]].copy(), w["conv_pool"][w["slots"][:64]].copy()
+    del w
+
+    def conv_step():
+        B.mamba2_conv1d_update(d, xbc, conv_w, None, post, conv, idx)
+
+    def su_step():
+        B.mamba2_state_update(d, post, dt, A_log, dtb, D, None, y, ssm, idx)
+
+    def decode_step():
+        conv_step()
+        su_step()
+
+    for _ in range(args.warmup):
+        decode_step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} decode steps")
+    ms_step = time_region(decode_step, args.steps, torch)
+    ms_su = time_region(su_step, args.steps, torch)
+    ms_conv = time_region(conv_step, args.steps, torch)
+    su_b, cu_b, min_b = decode_bytes_per_row(d, 2)
+    su_gbs = su_b * rows / (ms_su * 1e-3) / 1e9
+    tok_s = rows / (ms_step * 1e-3)
+    log(f"decode: {ms_step * 1e3:.1f} us/step ({tok_s / 1e6:.3f} M tok/s); state_update {ms_su * 1e3:.1f} us "
+        f"= {su_gbs:.0f} GB/s; conv_update {ms_conv * 1e3:.1f} us")
+
+    result = {
+        "metric": "SSM decode tok/s + % HBM peak; chunk-scan prefill tok/s (Nemotron-H-8B layer)",
+        "value": round(tok_s, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded NumPy PCG64; random-init layer parameters)",
+        "config": {"workload": "Nemotron-H-8B Mamba-2 layer decode, T=1: 256 sequences from a 512-slot bf16 "
+                               "state pool (random-permutation slots), 128 heads x headdim 64 x d_state 128, "
+                               "8 groups, conv width 4; step = conv1d_update + state_update",
+                   "rows": rows, "pool_slots": nslots, "state_dtype": "bf16", "act_dtype": "bf16"},
+        "roofline": {"bound": "hbm", "kernel": "state_update_kernel", "achieved": round(su_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(su_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": su_b * rows,
+                     "avg_launch_us": round(ms_su * 1e3, 2)},
+        "decode_detail": {"us_per_step": round(ms_step * 1e3, 2), "state_update_us": round(ms_su * 1e3, 2),
+                          "conv_update_us": round(ms_conv * 1e3, 2),
+                          "step_algorithmic_bytes": min_b * rows,
+                          "step_hbm_frac": round(min_b * rows / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    del ssm, conv, xbc, dt, post, y
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ prefill workload
+    if not args.no_prefill:
+        d2 = NEMOTRON_H_8B.with_(state_dtype=F32)
+        log("prefill workload: 4 x 8192 tokens, chunk 128; generating inputs")
+        w2 = synth.prefill_batch(d2, seed=2, seqlens=[8192] * 4, num_slots=8, with_z=False)
+        T = int(w2["cu_seqlens"][-1])
+        xbc2, dt2 = dev(w2["xbc"], bf), dev(w2["dt_raw"], bf)
+        pool2 = torch.zeros(8, d2.nheads, d2.headdim, d2.dstate, device="cuda")
+        convp2 = torch.zeros(8, d2.conv_width - 1, d2.conv_dim, device="cuda")
+        cw2 = dev(w2["params"]["conv_w"], torch.float32)
+        A2, dtb2, D2 = (dev(w2["params"][k], torch.float32) for k in ("A_log", "dt_bias", "D"))
+        cu2 = torch.from_numpy(w2["cu_seqlens"]).cuda()
+        idx2 = torch.from_numpy(w2["slots"]).cuda()
+        hi2 = torch.zeros(4, dtype=torch.uint8, device="cuda")
+        post2 = torch.empty(T, d2.conv_dim, dtype=torch.float32, device="cuda")
+        y2 = torch.empty(T, d2.d_inner, dtype=bf, device="cuda")
+        host_pre = {"xbc": w2["xbc"][:256].copy(), "dt_raw": w2["dt_raw"][:256].copy(), "params": w2["params"]}
+        del w2
+
+        def conv_fwd():
+            B.mamba2_conv1d_fwd(d2, xbc2, cw2, None, post2, convp2, cu2, idx2, hi2)
+
+        def scan():
+            B.mamba2_chunk_scan_fwd(d2, post2, dt2, A2, dtb2, D2, None, y2, pool2, cu2, idx2, hi2)
+
+        def prefill_step():
+            conv_fwd()
+            scan()
+
+        for _ in range(2):
+            prefill_step()
+        torch.cuda.synchronize()
+        log(f"timing {args.prefill_steps} prefill steps")
+        ms_pre = time_region(prefill_step, args.prefill_steps, torch)
+        ms_scan = time_region(scan, args.prefill_steps, torch)
+        ms_cf = time_region(conv_fwd, args.prefill_steps, torch)
+        sb, sf = scan_algorithmic(d2, T, 4, 4, 2, 4)
+        scan_gbs = sb / (ms_scan * 1e-3) / 1e9
+        scan_tfs = sf / (ms_scan * 1e-3) / 1e12
+        pre_tok_s = T / (ms_pre * 1e-3)
+        log(f"prefill: {ms_pre * 1e3:.1f} us/step ({pre_tok_s / 1e6:.2f} M tok/s); chunk_scan {ms_scan * 1e3:.1f} us "
+            f"({scan_gbs:.0f} GB/s, {scan_tfs:.1f} TFLOP/s); conv1d_fwd {ms_cf * 1e3:.1f} us")
+        result["prefill"] = {
+            "value": round(pre_tok_s, 1), "unit": "tok/s", "ms_per_step": round(ms_pre, 4),
+            "steps": args.prefill_steps,
+            "workload": "Nemotron-H-8B layer prefill: 4 x 8192 tokens (cu_seqlens), chunk 128, bf16 inputs, "
+                        "fp32 post-conv xBC, fp32 state, bf16 y, zero initial state, final states to pool slots; "
+                        "step = conv1d_fwd + chunk_scan_fwd",
+            "chunk_scan_us": round(ms_scan * 1e3, 2), "conv1d_fwd_us": round(ms_cf * 1e3, 2),
+            "roofline": {"bound": "mfma", "kernel": "chunk_scan_kernel", "achieved": round(scan_tfs, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(scan_tfs / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "algorithmic_flops_per_launch": sf, "algorithmic_bytes_per_launch": sb,
+                         "hbm_achieved_gbs": round(scan_gbs, 1), "hbm_frac": round(scan_gbs / HBM_PEAK_GBS, 4)},
+        }
+        del xbc2, dt2, pool2, convp2, post2, y2
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ CPU baseline (oracle)
+    if not args.no_cpu_baseline:
+        import oracle
+        kw = dict(H=d.nheads, P=d.headdim, N=d.dstate, G=d.ngroups)
+        cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+        os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+        ssm_h = host_slots[0].astype(np.float64)
+        conv_h = host_slots[1].astype(np.float64)
+        t0 = time.perf_counter()
+        done = 0
+        while done < 64 and time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.decode(host_tok["xbc"][done:done + 1], host_tok["dt_raw"][done:done + 1], host_params, [0],
+                          conv_h[done:done + 1], ssm_h[done:done + 1], **kw)
+            done += 1
+        el = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(done / el, 2), "unit": "tok/s", "cores": cores, "kind": "oracle",
+                                  "sample": f"{done} of the 256 decode rows (one layer step each) through the fp64 "
+                                            f"C oracle, {el:.1f} s"}
+        log(f"cpu baseline: {done} rows in {el:.1f} s on {cores} threads")
+        if not args.no_prefill:
+            t0 = time.perf_counter()
+            n = 0
+            cs = np.zeros((d.conv_width - 1, d.conv_dim))
+            hs = np.zeros((d.nheads, d.headdim, d.dstate))
+            while n < 256 and time.perf_counter() - t0 < args.cpu_seconds:
+                _, _, cs, hs = oracle.layer_seq(host_pre["xbc"][n:n + 32], host_pre["dt_raw"][n:n + 32],
+                                                host_pre["params"], cs, hs, **kw)
+                n += 32
+            el = time.perf_counter() - t0
+            result["prefill"]["cpu_baseline"] = {
+                "value": round(n / el, 2), "unit": "tok/s", "cores": cores, "kind": "oracle",
+                "sample": f"first {n} tokens of one 8192-token sequence through the fp64 C oracle, {el:.1f} s"}
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,199 @@
+/*
+ * mamba2.h -- C ABI of the gfx950 (MI355X) Mamba-2 SSM core.
+ *
+ * The library computes the SSM core of the Mamba-2 mixer in hybrid
+ * Mamba-Transformer models:
+ *   - causal depthwise conv1d + SiLU over the x/B/C channels, as a prefill
+ *     form and a one-token decode form;
+ *   - the selective recurrence, as a chunked SSD scan for prefill and as a
+ *     one-token state update for decode;
+ *   - varlen (cu_seqlens) packing and mixed prefill + decode batches.
+ *
+ * Sources on the pages:
+ *   [record]  "Nemotron-H-8B-Base-8K" -- mixer tensors (A_log, D, conv1d,
+ *             dt_bias), n_groups 8, section "Recurrent state" (128 heads x
+ *             headdim 64 x d_state 128; 2 MiB per layer per sequence in bf16),
+ *             section "REQUIRED KERNEL CLASS" (a chunked scan kernel plus a
+ *             fixed-size recurrent-state allocator);
+ *   [vllm.cpp] "NemotronH runs the PREFILL mamba kernels at decode" --
+ *             section "The divergence" (decode ops take state/conv-state
+ *             indices and read+write the cache in place at the slot),
+ *             section "Cost, at T=1, chunk_size=128, nchunks=1" (the one-step
+ *             update: 1 launch, no allocation, no memset, no scratch),
+ *             section "Confirm or refute" (hpg = H/G; the chunk scan must
+ *             equal repeated single steps);
+ *   [TRT-LLM] "Hybrid GDN (Qwen3.5-class) at high concurrency: mixed
+ *             prefill+decode iterations..." -- mixed batches of context
+ *             chunks and decode rows in one iteration.
+ *
+ * Math (per sequence, tokens in order; g(h) = h / (H/G)):
+ *   conv:  v_t[c] = bias[c] + sum_k w[c][k] * u~[t-(W-1)+k][c],  x|B|C = SiLU(v)
+ *          (u~ = [cached W-1 raw inputs, oldest first || new tokens];
+ *           tap W-1 multiplies the current token)
+ *   dt = softplus(dt_raw + dt_bias[h]), A = -exp(A_log[h]), a = exp(dt * A)
+ *   h_t[h][p][n] = a * h_{t-1}[h][p][n] + dt * x_t[h][p] * B_t[g(h)][n]
+ *   y_t[h][p]    = sum_n C_t[g(h)][n] * h_t[h][p][n] + D[h] * x_t[h][p]
+ *                  (times SiLU(z_t[h][p]) when z is given)
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are caller-owned device memory (for example torch
+ *     tensors), contiguous, 16-byte aligned. The library keeps no pointer
+ *     after a call returns and never allocates, frees or memsets memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is
+ *     enqueued on it; results are valid once the stream reaches the call.
+ *     No entry point synchronises the host.
+ *   - Return value: MAMBA2_OK (0) or an error code. On error nothing was
+ *     enqueued; mamba2_last_error() gives a thread-local message.
+ *   - Layouts (N fastest in the SSM pool, channel fastest elsewhere):
+ *       xBC        [T][Cdim], Cdim = H*P + 2*G*N, channels x (h*P + p) || B (g*N + n) || C (g*N + n)
+ *       dt_raw     [T][H]          z, y  [T][H*P]
+ *       conv w     [Cdim][W] fp32  conv bias [Cdim] fp32 or NULL
+ *       A_log, dt_bias, D  [H] fp32
+ *       ssm pool   [slots][H][P][N]   (state_dtype)
+ *       conv pool  [slots][W-1][Cdim] (state_dtype; raw pre-conv inputs, oldest first)
+ *   - Slot index < 0 marks a padding row/sequence: its outputs are written as
+ *     zero and no slot is read or written. Two rows of one call on the same
+ *     slot race (undefined result).
+ *   - Sizes: a call with zero rows / zero tokens is valid and enqueues nothing.
+ */
+#ifndef MAMBA2_H
+#define MAMBA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MAMBA2_OK = 0,
+    MAMBA2_ERR_INVALID_ARG = 1,  /* null pointer, misalignment, negative size, H % G != 0 ... */
+    MAMBA2_ERR_UNSUPPORTED = 2,  /* dims or dtypes outside the compiled kernel set */
+    MAMBA2_ERR_WORKSPACE = 3,    /* workspace missing or too small */
+    MAMBA2_ERR_HIP = 4,          /* a HIP launch failed */
+    MAMBA2_ERR_NO_SLOT = 5       /* slot allocator: pool exhausted or slot not allocated */
+} mamba2_status;
+
+typedef enum { MAMBA2_F32 = 0, MAMBA2_BF16 = 1 } mamba2_dtype;
+
+/* Layer dimensions and storage dtypes.
+ *   act_dtype   raw xBC, dt_raw and z
+ *   xbc_dtype   post-conv xBC, written by the conv entry points and read by
+ *               the scan and the state update (F32 keeps fp32-state prefill
+ *               within 1e-3 of exact arithmetic)
+ *   state_dtype SSM pool and conv pool
+ *   out_dtype   y                                                            */
+typedef struct {
+    int32_t nheads, headdim, dstate, ngroups, conv_width, chunk_size;
+    int32_t act_dtype, xbc_dtype, state_dtype, out_dtype;
+} mamba2_dims;
+
+/* Returns MAMBA2_OK if every entry point supports `dims`, else
+ * MAMBA2_ERR_INVALID_ARG / MAMBA2_ERR_UNSUPPORTED (message in mamba2_last_error). */
+int mamba2_check_dims(const mamba2_dims *dims);
+
+/* Bytes of one SSM pool slot: H*P*N*sizeof(state). At Nemotron-H-8B dims in
+ * bf16 this is 2 MiB per layer per sequence ([record], "Recurrent state").
+ * Returns 0 for invalid dims. */
+size_t mamba2_ssm_slot_bytes(const mamba2_dims *dims);
+
+/* Bytes of one conv pool slot: (W-1)*Cdim*sizeof(state). 0 for invalid dims. */
+size_t mamba2_conv_slot_bytes(const mamba2_dims *dims);
+
+/* Workspace the chunk scan needs for `total_tokens` packed tokens in `nseq`
+ * sequences (written to *bytes). The gfx950 scan keeps chunk states on chip,
+ * so this is 0 for every supported shape. */
+int mamba2_chunk_scan_workspace_bytes(const mamba2_dims *dims, int64_t total_tokens, int32_t nseq,
+                                      size_t *bytes);
+
+/* Prefill conv1d + SiLU over packed sequences ([record] conv1d tensor).
+ *   xbc            [total_tokens][Cdim] act_dtype, raw inputs (not modified)
+ *   xbc_out        [total_tokens][Cdim] xbc_dtype, SiLU(conv); must not alias xbc
+ *   cu_seqlens     [nseq+1] int32 device, cu_seqlens[0] = 0, nondecreasing,
+ *                  cu_seqlens[nseq] = total_tokens
+ *   state_indices  [nseq] int32 device: conv pool slot of each sequence
+ *   has_initial_state [nseq] uint8 device or NULL (all 0): 1 = left context is
+ *                  the slot's cached inputs, 0 = zeros
+ * Afterwards each used slot holds the sequence's last W-1 raw inputs (taken
+ * from the old cache for sequences shorter than W-1). Rows of padding
+ * sequences (slot < 0) are written as zero. */
+int mamba2_conv1d_fwd(const mamba2_dims *dims, const void *xbc, const float *conv_w,
+                      const float *conv_b, void *xbc_out, void *conv_pool,
+                      const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens,
+                      const int32_t *state_indices, const uint8_t *has_initial_state,
+                      void *stream);
+
+/* One-token conv1d + SiLU per row, shifting the slot's cached inputs in place
+ * ([vllm.cpp], "The divergence": conv-state indices, in place at the slot).
+ *   xbc [batch][Cdim] act_dtype; xbc_out [batch][Cdim] xbc_dtype (may not alias xbc);
+ *   state_indices [batch] int32 device. */
+int mamba2_conv1d_update(const mamba2_dims *dims, const void *xbc, const float *conv_w,
+                         const float *conv_b, void *xbc_out, void *conv_pool,
+                         const int32_t *state_indices, int32_t batch, void *stream);
+
+/* Chunked SSD scan over packed sequences ([record], "REQUIRED KERNEL CLASS").
+ *   xbc   [total_tokens][Cdim] xbc_dtype, post-conv x||B||C
+ *   dt_raw [total_tokens][H] act_dtype;  z [total_tokens][H*P] act_dtype or NULL
+ *   y     [total_tokens][H*P] out_dtype
+ *   ssm_pool: the initial state is read from slot state_indices[i] when
+ *   has_initial_state[i] is 1 (zeros otherwise); the final state is written
+ *   to that slot. dims->chunk_size is the SSD chunk length.
+ *   workspace/workspace_bytes: as sized by mamba2_chunk_scan_workspace_bytes
+ *   (may be NULL/0 when that is 0). */
+int mamba2_chunk_scan_fwd(const mamba2_dims *dims, const void *xbc, const void *dt_raw,
+                          const float *A_log, const float *dt_bias, const float *D, const void *z,
+                          void *y, void *ssm_pool, const int32_t *cu_seqlens, int32_t nseq,
+                          int64_t total_tokens, const int32_t *state_indices,
+                          const uint8_t *has_initial_state, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* One-token selective state update per row, reading and writing
+ * ssm_pool[state_indices[i]] in place ([vllm.cpp], "The divergence" and the
+ * right-hand column of "Cost, at T=1, chunk_size=128, nchunks=1": one launch,
+ * no allocation, no memset, no scratch).
+ *   xbc [batch][Cdim] xbc_dtype (post-conv); dt_raw [batch][H] act_dtype;
+ *   z [batch][H*P] act_dtype or NULL; y [batch][H*P] out_dtype. */
+int mamba2_state_update(const mamba2_dims *dims, const void *xbc, const void *dt_raw,
+                        const float *A_log, const float *dt_bias, const float *D, const void *z,
+                        void *y, void *ssm_pool, const int32_t *state_indices, int32_t batch,
+                        void *stream);
+
+/* Mixed batch ([TRT-LLM] mixed prefill+decode iterations): the prefill
+ * segment (packed by cu_seqlens) runs conv1d_fwd + chunk_scan_fwd, the
+ * decode segment (`decode_batch` rows, one token each) runs conv1d_update +
+ * state_update, all on `stream` with no host synchronisation.
+ *   xbc/dt_raw/z/y hold prefill tokens in rows [0, total_tokens) and decode
+ *   rows in rows [total_tokens, total_tokens + decode_batch);
+ *   xbc_post [total_tokens + decode_batch][Cdim] xbc_dtype receives the conv output.
+ *   prefill_indices [nseq], decode_indices [decode_batch]: pool slots. */
+int mamba2_mixed_fwd(const mamba2_dims *dims, const void *xbc, const void *dt_raw, const void *z,
+                     const float *conv_w, const float *conv_b, const float *A_log,
+                     const float *dt_bias, const float *D, void *xbc_post, void *y,
+                     void *ssm_pool, void *conv_pool, const int32_t *cu_seqlens, int32_t nseq,
+                     int64_t total_tokens, const int32_t *prefill_indices,
+                     const uint8_t *has_initial_state, const int32_t *decode_indices,
+                     int32_t decode_batch, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* Fixed-size recurrent-state slot allocator ([record], "REQUIRED KERNEL
+ * CLASS": a fixed-size recurrent state allocator; "Recurrent state": the
+ * cost scales with concurrency, not context). Host-only: it hands out slot
+ * ids of a caller-owned pool in O(1); it never touches device memory. A new
+ * sequence starts from zero state by passing has_initial_state = 0, not by
+ * clearing its slot. Not thread-safe; one allocator per pool. */
+typedef struct mamba2_slots mamba2_slots;
+int mamba2_slots_create(int32_t num_slots, mamba2_slots **out);
+int mamba2_slot_alloc(mamba2_slots *s, int32_t *slot);      /* MAMBA2_ERR_NO_SLOT when full */
+int mamba2_slot_free(mamba2_slots *s, int32_t slot);        /* MAMBA2_ERR_NO_SLOT if not allocated */
+int32_t mamba2_slots_in_use(const mamba2_slots *s);
+void mamba2_slots_destroy(mamba2_slots *s);
+
+const char *mamba2_status_string(int status);
+const char *mamba2_last_error(void);
+const char *mamba2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MAMBA2_H */

@@ -1,0 +1,307 @@
+"""ctypes binding of libmamba2.so (the gfx950 HIP library), same names as the C ABI.
+
+Argument marshalling only: every function checks tensor devices, dtypes and
+shapes, turns torch tensors into device pointers and passes the current HIP
+stream. All computation runs in the library's kernels; there is no fallback.
+If the library is missing, calls raise immediately.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+from typing import Optional
+
+import torch
+
+from .configs import BF16, F32, Dims
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmamba2.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "mamba2.h")
+
+_DT_CODE = {F32: 0, BF16: 1}
+_TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_NO_SLOT = range(6)
+
+
+class Mamba2Error(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class CDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "nheads", "headdim", "dstate", "ngroups", "conv_width", "chunk_size",
+        "act_dtype", "xbc_dtype", "state_dtype", "out_dtype")]
+
+
+def cdims(d: Dims, xbc_dtype: Optional[str] = None) -> CDims:
+    """C struct for ``d``. The post-conv buffer dtype defaults to ``d.post_dtype``."""
+    if xbc_dtype is None:
+        xbc_dtype = d.post_dtype
+    return CDims(d.nheads, d.headdim, d.dstate, d.ngroups, d.conv_width, d.chunk_size,
+                 _DT_CODE[d.act_dtype], _DT_CODE[xbc_dtype], _DT_CODE[d.state_dtype], _DT_CODE[d.out_dtype])
+
+
+_lock = threading.Lock()
+_lib = None
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "mamba2_check_dims": (ctypes.c_int, [ctypes.POINTER(CDims)]),
+    "mamba2_ssm_slot_bytes": (ctypes.c_size_t, [ctypes.POINTER(CDims)]),
+    "mamba2_conv_slot_bytes": (ctypes.c_size_t, [ctypes.POINTER(CDims)]),
+    "mamba2_chunk_scan_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(CDims), ctypes.c_int64, ctypes.c_int32,
+                                                          ctypes.POINTER(ctypes.c_size_t)]),
+    "mamba2_conv1d_fwd": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                         ctypes.c_int64, _P, _P, _P]),
+    "mamba2_conv1d_update": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P]),
+    "mamba2_chunk_scan_fwd": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                             ctypes.c_int32, ctypes.c_int64, _P, _P, _P, ctypes.c_size_t, _P]),
+    "mamba2_state_update": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           ctypes.c_int32, _P]),
+    "mamba2_mixed_fwd": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                        _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P, ctypes.c_int32, _P,
+                                        ctypes.c_size_t, _P]),
+    "mamba2_slots_create": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(_P)]),
+    "mamba2_slot_alloc": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32)]),
+    "mamba2_slot_free": (ctypes.c_int, [_P, ctypes.c_int32]),
+    "mamba2_slots_in_use": (ctypes.c_int32, [_P]),
+    "mamba2_slots_destroy": (None, [_P]),
+    "mamba2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "mamba2_last_error": (ctypes.c_char_p, []),
+    "mamba2_version": (ctypes.c_char_p, []),
+}
+
+
+def lib():
+    """Load libmamba2.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m state_space_model_ssm_amd.build` "
+                                   "(the HIP library is the only implementation; there is no fallback)")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGS.items():
+                fn = getattr(L, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions declared in include/mamba2.h."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mamba2_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(status: int, fn: str):
+    if status != OK:
+        raise Mamba2Error(status, fn, lib().mamba2_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _want(t, name, dtype=None, shape=None, device=True, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _xdt(d: Dims, xbc_dtype):
+    return _TORCH_DT[xbc_dtype or d.post_dtype]
+
+
+# ------------------------------------------------------------------ queries
+
+def mamba2_check_dims(d: Dims, xbc_dtype=None) -> None:
+    c = cdims(d, xbc_dtype)
+    _check(lib().mamba2_check_dims(ctypes.byref(c)), "mamba2_check_dims")
+
+
+def mamba2_ssm_slot_bytes(d: Dims) -> int:
+    return int(lib().mamba2_ssm_slot_bytes(ctypes.byref(cdims(d))))
+
+
+def mamba2_conv_slot_bytes(d: Dims) -> int:
+    return int(lib().mamba2_conv_slot_bytes(ctypes.byref(cdims(d))))
+
+
+def mamba2_chunk_scan_workspace_bytes(d: Dims, total_tokens: int, nseq: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().mamba2_chunk_scan_workspace_bytes(ctypes.byref(cdims(d)), total_tokens, nseq, ctypes.byref(out)),
+           "mamba2_chunk_scan_workspace_bytes")
+    return int(out.value)
+
+
+# ------------------------------------------------------------------ compute
+
+def mamba2_conv1d_fwd(d: Dims, xbc, conv_w, conv_b, xbc_out, conv_pool, cu_seqlens, state_indices,
+                      has_initial_state=None, *, xbc_dtype=None, stream=None):
+    T = xbc.shape[0]
+    nseq = state_indices.shape[0]
+    _want(xbc, "xbc", _TORCH_DT[d.act_dtype], (T, d.conv_dim))
+    _want(conv_w, "conv_w", torch.float32, (d.conv_dim, d.conv_width))
+    _want(conv_b, "conv_b", torch.float32, (d.conv_dim,), optional=True)
+    _want(xbc_out, "xbc_out", _xdt(d, xbc_dtype), (T, d.conv_dim))
+    _want(conv_pool, "conv_pool", _TORCH_DT[d.state_dtype])
+    _want(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,))
+    _want(state_indices, "state_indices", torch.int32, (nseq,))
+    _want(has_initial_state, "has_initial_state", torch.uint8, (nseq,), optional=True)
+    c = cdims(d, xbc_dtype)
+    _check(lib().mamba2_conv1d_fwd(ctypes.byref(c), _ptr(xbc), _ptr(conv_w), _ptr(conv_b), _ptr(xbc_out),
+                                   _ptr(conv_pool), _ptr(cu_seqlens), nseq, T, _ptr(state_indices),
+                                   _ptr(has_initial_state), _stream(stream)), "mamba2_conv1d_fwd")
+
+
+def mamba2_conv1d_update(d: Dims, xbc, conv_w, conv_b, xbc_out, conv_pool, state_indices, *, xbc_dtype=None,
+                         stream=None):
+    Bd = state_indices.shape[0]
+    _want(xbc, "xbc", _TORCH_DT[d.act_dtype], (Bd, d.conv_dim))
+    _want(conv_w, "conv_w", torch.float32, (d.conv_dim, d.conv_width))
+    _want(conv_b, "conv_b", torch.float32, (d.conv_dim,), optional=True)
+    _want(xbc_out, "xbc_out", _xdt(d, xbc_dtype), (Bd, d.conv_dim))
+    _want(conv_pool, "conv_pool", _TORCH_DT[d.state_dtype])
+    _want(state_indices, "state_indices", torch.int32, (Bd,))
+    c = cdims(d, xbc_dtype)
+    _check(lib().mamba2_conv1d_update(ctypes.byref(c), _ptr(xbc), _ptr(conv_w), _ptr(conv_b), _ptr(xbc_out),
+                                      _ptr(conv_pool), _ptr(state_indices), Bd, _stream(stream)),
+           "mamba2_conv1d_update")
+
+
+def mamba2_chunk_scan_fwd(d: Dims, xbc, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, cu_seqlens, state_indices,
+                          has_initial_state=None, workspace=None, *, xbc_dtype=None, stream=None):
+    T = xbc.shape[0]
+    nseq = state_indices.shape[0]
+    H = d.nheads
+    _want(xbc, "xbc", _xdt(d, xbc_dtype), (T, d.conv_dim))
+    _want(dt_raw, "dt_raw", _TORCH_DT[d.act_dtype], (T, H))
+    for n, t in (("A_log", A_log), ("dt_bias", dt_bias), ("D", D)):
+        _want(t, n, torch.float32, (H,))
+    _want(z, "z", _TORCH_DT[d.act_dtype], (T, d.d_inner), optional=True)
+    _want(y, "y", _TORCH_DT[d.out_dtype], (T, d.d_inner))
+    _want(ssm_pool, "ssm_pool", _TORCH_DT[d.state_dtype])
+    if ssm_pool.dim() != 4 or tuple(ssm_pool.shape[1:]) != (H, d.headdim, d.dstate):
+        raise ValueError("ssm_pool must be [slots, H, P, N]")
+    _want(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,))
+    _want(state_indices, "state_indices", torch.int32, (nseq,))
+    _want(has_initial_state, "has_initial_state", torch.uint8, (nseq,), optional=True)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = cdims(d, xbc_dtype)
+    _check(lib().mamba2_chunk_scan_fwd(ctypes.byref(c), _ptr(xbc), _ptr(dt_raw), _ptr(A_log), _ptr(dt_bias),
+                                       _ptr(D), _ptr(z), _ptr(y), _ptr(ssm_pool), _ptr(cu_seqlens), nseq, T,
+                                       _ptr(state_indices), _ptr(has_initial_state), _ptr(workspace), ws_bytes,
+                                       _stream(stream)), "mamba2_chunk_scan_fwd")
+
+
+def mamba2_state_update(d: Dims, xbc, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, state_indices, *,
+                        xbc_dtype=None, stream=None):
+    Bd = state_indices.shape[0]
+    H = d.nheads
+    _want(xbc, "xbc", _xdt(d, xbc_dtype), (Bd, d.conv_dim))
+    _want(dt_raw, "dt_raw", _TORCH_DT[d.act_dtype], (Bd, H))
+    for n, t in (("A_log", A_log), ("dt_bias", dt_bias), ("D", D)):
+        _want(t, n, torch.float32, (H,))
+    _want(z, "z", _TORCH_DT[d.act_dtype], (Bd, d.d_inner), optional=True)
+    _want(y, "y", _TORCH_DT[d.out_dtype], (Bd, d.d_inner))
+    _want(ssm_pool, "ssm_pool", _TORCH_DT[d.state_dtype])
+    if ssm_pool.dim() != 4 or tuple(ssm_pool.shape[1:]) != (H, d.headdim, d.dstate):
+        raise ValueError("ssm_pool must be [slots, H, P, N]")
+    _want(state_indices, "state_indices", torch.int32, (Bd,))
+    c = cdims(d, xbc_dtype)
+    _check(lib().mamba2_state_update(ctypes.byref(c), _ptr(xbc), _ptr(dt_raw), _ptr(A_log), _ptr(dt_bias), _ptr(D),
+                                     _ptr(z), _ptr(y), _ptr(ssm_pool), _ptr(state_indices), Bd, _stream(stream)),
+           "mamba2_state_update")
+
+
+def mamba2_mixed_fwd(d: Dims, xbc, dt_raw, z, conv_w, conv_b, A_log, dt_bias, D, xbc_post, y, ssm_pool, conv_pool,
+                     cu_seqlens, prefill_indices, has_initial_state, decode_indices, workspace=None, *,
+                     xbc_dtype=None, stream=None):
+    nseq = prefill_indices.shape[0]
+    Bd = decode_indices.shape[0]
+    rows = xbc.shape[0]
+    T = rows - Bd
+    H = d.nheads
+    _want(xbc, "xbc", _TORCH_DT[d.act_dtype], (rows, d.conv_dim))
+    _want(dt_raw, "dt_raw", _TORCH_DT[d.act_dtype], (rows, H))
+    _want(z, "z", _TORCH_DT[d.act_dtype], (rows, d.d_inner), optional=True)
+    _want(conv_w, "conv_w", torch.float32, (d.conv_dim, d.conv_width))
+    _want(conv_b, "conv_b", torch.float32, (d.conv_dim,), optional=True)
+    for n, t in (("A_log", A_log), ("dt_bias", dt_bias), ("D", D)):
+        _want(t, n, torch.float32, (H,))
+    _want(xbc_post, "xbc_post", _xdt(d, xbc_dtype), (rows, d.conv_dim))
+    _want(y, "y", _TORCH_DT[d.out_dtype], (rows, d.d_inner))
+    _want(ssm_pool, "ssm_pool", _TORCH_DT[d.state_dtype])
+    _want(conv_pool, "conv_pool", _TORCH_DT[d.state_dtype])
+    _want(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,))
+    _want(prefill_indices, "prefill_indices", torch.int32, (nseq,))
+    _want(has_initial_state, "has_initial_state", torch.uint8, (nseq,), optional=True)
+    _want(decode_indices, "decode_indices", torch.int32, (Bd,))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = cdims(d, xbc_dtype)
+    _check(lib().mamba2_mixed_fwd(ctypes.byref(c), _ptr(xbc), _ptr(dt_raw), _ptr(z), _ptr(conv_w), _ptr(conv_b),
+                                  _ptr(A_log), _ptr(dt_bias), _ptr(D), _ptr(xbc_post), _ptr(y), _ptr(ssm_pool),
+                                  _ptr(conv_pool), _ptr(cu_seqlens), nseq, T, _ptr(prefill_indices),
+                                  _ptr(has_initial_state), _ptr(decode_indices), Bd, _ptr(workspace), ws_bytes,
+                                  _stream(stream)), "mamba2_mixed_fwd")
+
+
+# ------------------------------------------------------------------ slot allocator
+
+class SlotAllocator:
+    """Host-side O(1) free list of pool slots (``mamba2_slots_*``)."""
+
+    def __init__(self, num_slots: int):
+        h = ctypes.c_void_p()
+        _check(lib().mamba2_slots_create(num_slots, ctypes.byref(h)), "mamba2_slots_create")
+        self._h = h
+        self.num_slots = num_slots
+
+    def alloc(self) -> int:
+        s = ctypes.c_int32(-1)
+        _check(lib().mamba2_slot_alloc(self._h, ctypes.byref(s)), "mamba2_slot_alloc")
+        return int(s.value)
+
+    def free(self, slot: int) -> None:
+        _check(lib().mamba2_slot_free(self._h, slot), "mamba2_slot_free")
+
+    @property
+    def in_use(self) -> int:
+        return int(lib().mamba2_slots_in_use(self._h))
+
+    def close(self):
+        if self._h:
+            lib().mamba2_slots_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -10,6 +10,7 @@ chunk_size=128, nchunks=1").
 from __future__ import annotations
 
 from dataclasses import dataclass, replace
+from typing import Optional
 
 F32 = "f32"
 BF16 = "bf16"
@@ -26,7 +27,16 @@ class Dims:
     chunk_size: int = 128
     act_dtype: str = BF16    # xBC, dt_raw, z
     state_dtype: str = BF16  # SSM pool and conv pool
-    out_dtype: str = BF16    # y and post-conv xBC
+    out_dtype: str = BF16    # y
+    xbc_dtype: Optional[str] = None  # post-conv xBC; None -> fp32 if state or y is fp32, else act_dtype
+
+    @property
+    def post_dtype(self) -> str:
+        """Dtype of the post-conv xBC buffer. Rounding post-conv x/B/C to bf16 costs
+        ~3e-3 relative accuracy, so it stays fp32 whenever an fp32 result is stored."""
+        if self.xbc_dtype is not None:
+            return self.xbc_dtype
+        return F32 if F32 in (self.state_dtype, self.out_dtype) else self.act_dtype
 
     @property
     def d_inner(self) -> int:

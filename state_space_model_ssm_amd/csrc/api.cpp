@@ -1,0 +1,295 @@
+// C ABI of the gfx950 Mamba-2 SSM core: argument validation, dispatch to the
+// HIP kernels on the caller's stream, and the host-side slot allocator.
+// Nothing here allocates device memory, synchronises or memsets.
+#include "../../include/mamba2.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return MAMBA2_OK;
+}
+
+bool valid_dtype(int d) { return d == MAMBA2_F32 || d == MAMBA2_BF16; }
+size_t dtype_bytes(int d) { return d == MAMBA2_BF16 ? 2 : 4; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dims_basic(const mamba2_dims *d) {
+    if (!d) return fail(MAMBA2_ERR_INVALID_ARG, "dims is NULL");
+    if (d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->ngroups <= 0 || d->conv_width <= 0 ||
+        d->chunk_size <= 0)
+        return fail(MAMBA2_ERR_INVALID_ARG, "dims must be positive (H=%d P=%d N=%d G=%d W=%d Q=%d)", d->nheads,
+                    d->headdim, d->dstate, d->ngroups, d->conv_width, d->chunk_size);
+    if (d->nheads % d->ngroups != 0)
+        return fail(MAMBA2_ERR_INVALID_ARG, "nheads (%d) must be a multiple of ngroups (%d)", d->nheads, d->ngroups);
+    if (!valid_dtype(d->act_dtype) || !valid_dtype(d->xbc_dtype) || !valid_dtype(d->state_dtype) ||
+        !valid_dtype(d->out_dtype))
+        return fail(MAMBA2_ERR_INVALID_ARG, "unknown dtype code");
+    return MAMBA2_OK;
+}
+
+m2::LayerShape shape_of(const mamba2_dims *d) {
+    m2::LayerShape s;
+    s.H = d->nheads; s.P = d->headdim; s.N = d->dstate; s.G = d->ngroups; s.W = d->conv_width; s.Q = d->chunk_size;
+    s.act_dt = d->act_dtype; s.xbc_dt = d->xbc_dtype; s.state_dt = d->state_dtype; s.out_dt = d->out_dtype;
+    return s;
+}
+
+int check_conv(const mamba2_dims *d) {
+    int st = check_dims_basic(d);
+    if (st) return st;
+    if (!m2::conv_supported(shape_of(d)))
+        return fail(MAMBA2_ERR_UNSUPPORTED, "conv1d supports conv_width 2..4 and Cdim %% 8 == 0 (W=%d, Cdim=%lld)",
+                    d->conv_width, (long long)shape_of(d).cdim());
+    return MAMBA2_OK;
+}
+
+int check_state_update(const mamba2_dims *d) {
+    int st = check_dims_basic(d);
+    if (st) return st;
+    const m2::LayerShape s = shape_of(d);
+    if (!m2::state_update_supported(s) || s.cdim() % 8 != 0 || s.P % 4 != 0)
+        return fail(MAMBA2_ERR_UNSUPPORTED, "state update supports dstate in {16, 64, 128}, headdim %% 4 == 0 (N=%d)",
+                    d->dstate);
+    return MAMBA2_OK;
+}
+
+int check_scan(const mamba2_dims *d) {
+    int st = check_dims_basic(d);
+    if (st) return st;
+    if (!m2::scan_supported(shape_of(d)))
+        return fail(MAMBA2_ERR_UNSUPPORTED,
+                    "chunk scan supports (headdim, dstate, chunk) in {(16,16,16|32), (64,128,64|128)}; got (%d,%d,%d)",
+                    d->headdim, d->dstate, d->chunk_size);
+    return MAMBA2_OK;
+}
+
+#define REQUIRE_PTR(p) \
+    do { if (!(p)) return fail(MAMBA2_ERR_INVALID_ARG, "%s is NULL", #p); \
+         if (!aligned16(p)) return fail(MAMBA2_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); } while (0)
+#define OPT_PTR(p) \
+    do { if ((p) && !aligned16(p)) return fail(MAMBA2_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); } while (0)
+#define REQUIRE_IDX(p) \
+    do { if (!(p)) return fail(MAMBA2_ERR_INVALID_ARG, "%s is NULL", #p); \
+         if (reinterpret_cast<uintptr_t>(p) & 3u) return fail(MAMBA2_ERR_INVALID_ARG, "%s is not 4-byte aligned", #p); } while (0)
+
+int hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(MAMBA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mamba2_check_dims(const mamba2_dims *d) {
+    int st = check_conv(d);
+    if (st) return st;
+    st = check_state_update(d);
+    if (st) return st;
+    st = check_scan(d);
+    if (st) return st;
+    return ok();
+}
+
+size_t mamba2_ssm_slot_bytes(const mamba2_dims *d) {
+    if (check_dims_basic(d)) return 0;
+    return (size_t)d->nheads * d->headdim * d->dstate * dtype_bytes(d->state_dtype);
+}
+
+size_t mamba2_conv_slot_bytes(const mamba2_dims *d) {
+    if (check_dims_basic(d)) return 0;
+    return (size_t)(d->conv_width - 1) * (size_t)shape_of(d).cdim() * dtype_bytes(d->state_dtype);
+}
+
+int mamba2_chunk_scan_workspace_bytes(const mamba2_dims *d, int64_t total_tokens, int32_t nseq, size_t *bytes) {
+    int st = check_scan(d);
+    if (st) return st;
+    if (!bytes) return fail(MAMBA2_ERR_INVALID_ARG, "bytes is NULL");
+    if (total_tokens < 0 || nseq < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative size");
+    *bytes = 0;
+    return ok();
+}
+
+int mamba2_conv1d_fwd(const mamba2_dims *d, const void *xbc, const float *conv_w, const float *conv_b, void *xbc_out,
+                      void *conv_pool, const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens,
+                      const int32_t *state_indices, const uint8_t *has_initial_state, void *stream) {
+    int st = check_conv(d);
+    if (st) return st;
+    if (nseq < 0 || total_tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative nseq or total_tokens");
+    if (nseq == 0) {
+        if (total_tokens != 0) return fail(MAMBA2_ERR_INVALID_ARG, "tokens without sequences");
+        return ok();
+    }
+    REQUIRE_PTR(conv_w); OPT_PTR(conv_b); REQUIRE_PTR(conv_pool);
+    REQUIRE_IDX(cu_seqlens); REQUIRE_IDX(state_indices);
+    if (total_tokens > 0) { REQUIRE_PTR(xbc); REQUIRE_PTR(xbc_out); }
+    if (xbc && xbc == xbc_out) return fail(MAMBA2_ERR_INVALID_ARG, "xbc_out must not alias xbc");
+    m2::ConvFwdArgs a{xbc, conv_w, conv_b, xbc_out, conv_pool, cu_seqlens, state_indices, has_initial_state, nseq,
+                      total_tokens};
+    return hip_status(m2::launch_conv_fwd(shape_of(d), a, static_cast<hipStream_t>(stream)), "conv1d_fwd launch");
+}
+
+int mamba2_conv1d_update(const mamba2_dims *d, const void *xbc, const float *conv_w, const float *conv_b,
+                         void *xbc_out, void *conv_pool, const int32_t *state_indices, int32_t batch, void *stream) {
+    int st = check_conv(d);
+    if (st) return st;
+    if (batch < 0) return fail(MAMBA2_ERR_INVALID_ARG, "batch < 0");
+    if (batch == 0) return ok();
+    REQUIRE_PTR(xbc); REQUIRE_PTR(conv_w); OPT_PTR(conv_b); REQUIRE_PTR(xbc_out); REQUIRE_PTR(conv_pool);
+    REQUIRE_IDX(state_indices);
+    if (xbc == xbc_out) return fail(MAMBA2_ERR_INVALID_ARG, "xbc_out must not alias xbc");
+    m2::ConvUpdateArgs a{xbc, conv_w, conv_b, xbc_out, conv_pool, state_indices, batch};
+    return hip_status(m2::launch_conv_update(shape_of(d), a, static_cast<hipStream_t>(stream)), "conv1d_update launch");
+}
+
+int mamba2_chunk_scan_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw, const float *A_log,
+                          const float *dt_bias, const float *D, const void *z, void *y, void *ssm_pool,
+                          const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens, const int32_t *state_indices,
+                          const uint8_t *has_initial_state, void *workspace, size_t workspace_bytes, void *stream) {
+    (void)workspace;
+    (void)workspace_bytes;  // the scan keeps chunk states on chip: no workspace needed
+    int st = check_scan(d);
+    if (st) return st;
+    if (nseq < 0 || total_tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative nseq or total_tokens");
+    if (nseq == 0) {
+        if (total_tokens != 0) return fail(MAMBA2_ERR_INVALID_ARG, "tokens without sequences");
+        return ok();
+    }
+    REQUIRE_PTR(A_log); REQUIRE_PTR(dt_bias); REQUIRE_PTR(D); REQUIRE_PTR(ssm_pool);
+    REQUIRE_IDX(cu_seqlens); REQUIRE_IDX(state_indices);
+    if (total_tokens > 0) { REQUIRE_PTR(xbc); REQUIRE_PTR(dt_raw); REQUIRE_PTR(y); OPT_PTR(z); }
+    m2::ScanArgs a{xbc, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, cu_seqlens, state_indices, has_initial_state,
+                   nseq, total_tokens};
+    return hip_status(m2::launch_chunk_scan(shape_of(d), a, static_cast<hipStream_t>(stream)), "chunk_scan launch");
+}
+
+int mamba2_state_update(const mamba2_dims *d, const void *xbc, const void *dt_raw, const float *A_log,
+                        const float *dt_bias, const float *D, const void *z, void *y, void *ssm_pool,
+                        const int32_t *state_indices, int32_t batch, void *stream) {
+    int st = check_state_update(d);
+    if (st) return st;
+    if (batch < 0) return fail(MAMBA2_ERR_INVALID_ARG, "batch < 0");
+    if (batch == 0) return ok();
+    REQUIRE_PTR(xbc); REQUIRE_PTR(dt_raw); REQUIRE_PTR(A_log); REQUIRE_PTR(dt_bias); REQUIRE_PTR(D);
+    OPT_PTR(z); REQUIRE_PTR(y); REQUIRE_PTR(ssm_pool); REQUIRE_IDX(state_indices);
+    m2::StateUpdateArgs a{xbc, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, state_indices, batch};
+    return hip_status(m2::launch_state_update(shape_of(d), a, static_cast<hipStream_t>(stream)), "state_update launch");
+}
+
+int mamba2_mixed_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw, const void *z, const float *conv_w,
+                     const float *conv_b, const float *A_log, const float *dt_bias, const float *D, void *xbc_post,
+                     void *y, void *ssm_pool, void *conv_pool, const int32_t *cu_seqlens, int32_t nseq,
+                     int64_t total_tokens, const int32_t *prefill_indices, const uint8_t *has_initial_state,
+                     const int32_t *decode_indices, int32_t decode_batch, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    int st = mamba2_check_dims(d);
+    if (st) return st;
+    if (nseq < 0 || total_tokens < 0 || decode_batch < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative size");
+    const m2::LayerShape s = shape_of(d);
+    const int64_t cdim = s.cdim(), hp = (int64_t)s.H * s.P;
+    const size_t ab = dtype_bytes(d->act_dtype), xb = dtype_bytes(d->xbc_dtype), ob = dtype_bytes(d->out_dtype);
+    if (nseq > 0) {
+        st = mamba2_conv1d_fwd(d, xbc, conv_w, conv_b, xbc_post, conv_pool, cu_seqlens, nseq, total_tokens,
+                               prefill_indices, has_initial_state, stream);
+        if (st) return st;
+        st = mamba2_chunk_scan_fwd(d, xbc_post, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, cu_seqlens, nseq,
+                                   total_tokens, prefill_indices, has_initial_state, workspace, workspace_bytes,
+                                   stream);
+        if (st) return st;
+    }
+    if (decode_batch > 0) {
+        REQUIRE_PTR(xbc); REQUIRE_PTR(dt_raw); REQUIRE_PTR(xbc_post); REQUIRE_PTR(y);
+        const char *xin = static_cast<const char *>(xbc) + total_tokens * cdim * ab;
+        char *xpost = static_cast<char *>(xbc_post) + total_tokens * cdim * xb;
+        const char *dtd = static_cast<const char *>(dt_raw) + total_tokens * s.H * ab;
+        const char *zd = z ? static_cast<const char *>(z) + total_tokens * hp * ab : nullptr;
+        char *yd = static_cast<char *>(y) + total_tokens * hp * ob;
+        st = mamba2_conv1d_update(d, xin, conv_w, conv_b, xpost, conv_pool, decode_indices, decode_batch, stream);
+        if (st) return st;
+        st = mamba2_state_update(d, xpost, dtd, A_log, dt_bias, D, zd, yd, ssm_pool, decode_indices, decode_batch,
+                                 stream);
+        if (st) return st;
+    }
+    return ok();
+}
+
+// ------------------------------------------------------------ slot allocator
+struct mamba2_slots {
+    std::vector<int32_t> free_list;  // stack of free slot ids
+    std::vector<uint8_t> in_use;
+};
+
+int mamba2_slots_create(int32_t num_slots, mamba2_slots **out) {
+    if (!out) return fail(MAMBA2_ERR_INVALID_ARG, "out is NULL");
+    if (num_slots <= 0) return fail(MAMBA2_ERR_INVALID_ARG, "num_slots must be positive");
+    auto *s = new mamba2_slots;
+    s->free_list.reserve(num_slots);
+    for (int32_t i = num_slots - 1; i >= 0; --i) s->free_list.push_back(i);  // slot 0 is handed out first
+    s->in_use.assign(num_slots, 0);
+    *out = s;
+    return ok();
+}
+
+int mamba2_slot_alloc(mamba2_slots *s, int32_t *slot) {
+    if (!s || !slot) return fail(MAMBA2_ERR_INVALID_ARG, "NULL argument");
+    if (s->free_list.empty()) return fail(MAMBA2_ERR_NO_SLOT, "all %zu slots are in use", s->in_use.size());
+    *slot = s->free_list.back();
+    s->free_list.pop_back();
+    s->in_use[*slot] = 1;
+    return ok();
+}
+
+int mamba2_slot_free(mamba2_slots *s, int32_t slot) {
+    if (!s) return fail(MAMBA2_ERR_INVALID_ARG, "NULL allocator");
+    if (slot < 0 || (size_t)slot >= s->in_use.size() || !s->in_use[slot])
+        return fail(MAMBA2_ERR_NO_SLOT, "slot %d is not allocated", slot);
+    s->in_use[slot] = 0;
+    s->free_list.push_back(slot);
+    return ok();
+}
+
+int32_t mamba2_slots_in_use(const mamba2_slots *s) {
+    return s ? (int32_t)(s->in_use.size() - s->free_list.size()) : 0;
+}
+
+void mamba2_slots_destroy(mamba2_slots *s) { delete s; }
+
+const char *mamba2_status_string(int status) {
+    switch (status) {
+        case MAMBA2_OK: return "ok";
+        case MAMBA2_ERR_INVALID_ARG: return "invalid argument";
+        case MAMBA2_ERR_UNSUPPORTED: return "unsupported dims or dtype";
+        case MAMBA2_ERR_WORKSPACE: return "workspace too small";
+        case MAMBA2_ERR_HIP: return "HIP error";
+        case MAMBA2_ERR_NO_SLOT: return "no slot";
+        default: return "unknown status";
+    }
+}
+
+const char *mamba2_last_error(void) { return g_last_error.c_str(); }
+
+const char *mamba2_version(void) { return "mamba2-gfx950 0.1"; }
+
+}  // extern "C"

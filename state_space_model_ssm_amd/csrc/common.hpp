@@ -1,0 +1,104 @@
+// Shared device helpers for the gfx950 Mamba-2 kernels: storage types, bf16
+// conversion, 16-byte vector access and the scalar activations.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m2 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum Dt : int { DT_F32 = 0, DT_BF16 = 1 };
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// float -> bf16, round to nearest even (the conversion clang defines for __bf16).
+__device__ __forceinline__ bf16 f32_to_bf16(float v) { return (bf16)v; }
+
+template <typename T> struct Io;
+
+template <> struct Io<float> {
+    static constexpr int kVec = 4;  // elements per 16-byte access
+    __device__ static __forceinline__ void load(const float *p, float *out) {
+        f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+        out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+    }
+    __device__ static __forceinline__ void store(float *p, const float *in) {
+        f32x4 v = {in[0], in[1], in[2], in[3]};
+        *reinterpret_cast<f32x4 *>(p) = v;
+    }
+    __device__ static __forceinline__ float get(const float *p, int64_t i) { return p[i]; }
+    __device__ static __forceinline__ void put(float *p, int64_t i, float v) { p[i] = v; }
+};
+
+template <> struct Io<bf16> {
+    static constexpr int kVec = 8;
+    __device__ static __forceinline__ void load(const bf16 *p, float *out) {
+        uint4 v = *reinterpret_cast<const uint4 *>(p);
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(w[i] << 16);
+            out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    __device__ static __forceinline__ void store(bf16 *p, const float *in) {
+        bf16x8 v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = f32_to_bf16(in[i]);
+        *reinterpret_cast<bf16x8 *>(p) = v;
+    }
+    __device__ static __forceinline__ float get(const bf16 *p, int64_t i) { return (float)p[i]; }
+    __device__ static __forceinline__ void put(bf16 *p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// K consecutive elements (K a multiple of 4) with the widest aligned vector access.
+template <typename T, int K> __device__ __forceinline__ void load_k(const T *p, float *out) {
+    static_assert(K % 4 == 0, "load_k: K must be a multiple of 4");
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int i = 0; i < K / 4; ++i) Io<float>::load(reinterpret_cast<const float *>(p) + 4 * i, out + 4 * i);
+    } else if constexpr (K % 8 == 0) {
+#pragma unroll
+        for (int i = 0; i < K / 8; ++i) Io<bf16>::load(p + 8 * i, out + 8 * i);
+    } else {
+#pragma unroll
+        for (int i = 0; i < K / 4; ++i) {
+            uint2 v = *reinterpret_cast<const uint2 *>(p + 4 * i);
+            out[4 * i + 0] = __uint_as_float(v.x << 16);
+            out[4 * i + 1] = __uint_as_float(v.x & 0xffff0000u);
+            out[4 * i + 2] = __uint_as_float(v.y << 16);
+            out[4 * i + 3] = __uint_as_float(v.y & 0xffff0000u);
+        }
+    }
+}
+
+template <typename T, int K> __device__ __forceinline__ void store_k(T *p, const float *in) {
+    static_assert(K % 4 == 0, "store_k: K must be a multiple of 4");
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int i = 0; i < K / 4; ++i) Io<float>::store(reinterpret_cast<float *>(p) + 4 * i, in + 4 * i);
+    } else if constexpr (K % 8 == 0) {
+#pragma unroll
+        for (int i = 0; i < K / 8; ++i) Io<bf16>::store(p + 8 * i, in + 8 * i);
+    } else {
+#pragma unroll
+        for (int i = 0; i < K; ++i) p[i] = f32_to_bf16(in[i]);
+    }
+}
+
+// Runtime-dtype scalar access for small per-row tensors (dt_raw, z, y, x).
+__device__ __forceinline__ float ld(const void *p, int dt, int64_t i) {
+    return dt == DT_BF16 ? (float)static_cast<const bf16 *>(p)[i] : static_cast<const float *>(p)[i];
+}
+__device__ __forceinline__ void st(void *p, int dt, int64_t i, float v) {
+    if (dt == DT_BF16) static_cast<bf16 *>(p)[i] = f32_to_bf16(v);
+    else static_cast<float *>(p)[i] = v;
+}
+
+__device__ __forceinline__ float softplus_f(float v) { return fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v))); }
+__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + expf(-v)); }
+
+}  // namespace m2

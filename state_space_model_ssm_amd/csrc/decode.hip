@@ -1,0 +1,215 @@
+// One-token decode kernels for gfx950: the selective state update, which reads
+// and writes the SSM pool in place at each row's slot, and the conv1d update,
+// which shifts the slot's cached raw inputs in place.
+//
+// The in-place, index-addressed form is the one the vllm.cpp issue "NemotronH
+// runs the PREFILL mamba kernels at decode" asks for (section "The
+// divergence"); its cost table ("Cost, at T=1, chunk_size=128, nchunks=1")
+// gives the target: one launch, no allocation, no memset, no scratch.
+//
+// State update, per (row, head): the [P][N] state tile (N fastest) is streamed
+// once from HBM and written back once. It is HBM bound (about 5 flops per
+// state element), so the layout work is all about the stream:
+//   * each lane owns 16 contiguous bytes of one p-row (8 bf16 or 4 fp32
+//     values of n); kLpr = N / kVec lanes cover a row, 256 / kLpr rows are in
+//     flight per pass, and ITERS passes are issued before any use so that a
+//     workgroup keeps ITERS x 4 KiB of loads outstanding;
+//   * y[p] = sum_n C[n] h[p][n] is a butterfly over the kLpr lanes of a row;
+//   * B and C of the row's group and the per-head scalars are read once per
+//     lane (they hit L2: the 16 heads of a group share them);
+//   * a head's tile is split across `psplit` workgroups when rows x heads alone
+//     would not fill the 256 CUs.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace m2 {
+
+template <typename ST, typename XT, int N, int ITERS>
+__global__ __launch_bounds__(256) void state_update_kernel(StateUpdateArgs a, int H, int P, int G,
+                                                           int act_dt, int out_dt, int psplit) {
+    constexpr int kVec = Io<ST>::kVec;
+    constexpr int kLpr = N / kVec;   // lanes per p-row
+    constexpr int kRpi = 256 / kLpr; // p-rows per pass
+    static_assert(kLpr >= 1 && kLpr <= 64 && (kLpr & (kLpr - 1)) == 0, "row must fit a wavefront");
+
+    const int tid = threadIdx.x;
+    const int head = blockIdx.x / psplit;
+    const int pblk = blockIdx.x - head * psplit;
+    const int row = blockIdx.y;
+    const int lr = tid & (kLpr - 1);
+    const int r = tid / kLpr;
+    const int n0 = lr * kVec;
+    const int64_t HP = (int64_t)H * P;
+    const int64_t cdim = HP + 2LL * G * N;
+    const int p_first = pblk * kRpi * ITERS + r;
+    const int64_t yrow = (int64_t)row * HP + (int64_t)head * P;
+
+    const int slot = a.idx[row];
+    if (slot < 0) {  // padding row: y = 0, no state access
+        if (lr == 0) {
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) {
+                const int p = p_first + it * kRpi;
+                if (p < P) st(a.y, out_dt, yrow + p, 0.0f);
+            }
+        }
+        return;
+    }
+
+    ST *tile = static_cast<ST *>(a.pool) + ((int64_t)slot * H + head) * (int64_t)P * N;
+    ST h[ITERS][kVec];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int p = p_first + it * kRpi;
+        if (p < P) *reinterpret_cast<uint4 *>(&h[it][0]) = *reinterpret_cast<const uint4 *>(tile + (int64_t)p * N + n0);
+    }
+
+    const int g = head / (H / G);
+    const XT *xrow = static_cast<const XT *>(a.xbc) + (int64_t)row * cdim;
+    float Bv[kVec], Cv[kVec];
+    load_k<XT, kVec>(xrow + HP + (int64_t)g * N + n0, Bv);
+    load_k<XT, kVec>(xrow + HP + (int64_t)G * N + (int64_t)g * N + n0, Cv);
+    const float dt = softplus_f(ld(a.dt_raw, act_dt, (int64_t)row * H + head) + a.dt_bias[head]);
+    const float decay = expf(dt * -expf(a.A_log[head]));
+    const float Dh = a.D[head];
+
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int p = p_first + it * kRpi;
+        if (p < P) {
+            const float xv = (float)xrow[(int64_t)head * P + p];
+            const float dx = dt * xv;
+            float acc = 0.0f;
+            float out[kVec];
+#pragma unroll
+            for (int j = 0; j < kVec; ++j) {
+                const float s = decay * (float)h[it][j] + dx * Bv[j];
+                out[j] = s;
+                acc += Cv[j] * s;
+            }
+            store_k<ST, kVec>(tile + (int64_t)p * N + n0, out);
+#pragma unroll
+            for (int m = kLpr / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+            if (lr == 0) {
+                float yv = acc + Dh * xv;
+                if (a.z) yv *= silu_f(ld(a.z, act_dt, yrow + p));
+                st(a.y, out_dt, yrow + p, yv);
+            }
+        }
+    }
+}
+
+template <typename ST, typename XT, int N, int ITERS>
+static hipError_t launch_su(const LayerShape &s, const StateUpdateArgs &a, hipStream_t stream, int rows_needed) {
+    const int psplit = (rows_needed + ITERS - 1) / ITERS;
+    dim3 grid(s.H * psplit, a.batch);
+    hipLaunchKernelGGL((state_update_kernel<ST, XT, N, ITERS>), grid, dim3(256), 0, stream, a, s.H, s.P, s.G,
+                       s.act_dt, s.out_dt, psplit);
+    return hipGetLastError();
+}
+
+template <typename ST, typename XT, int N>
+static hipError_t dispatch_su_iters(const LayerShape &s, const StateUpdateArgs &a, hipStream_t stream) {
+    constexpr int kRpi = 256 / (N / Io<ST>::kVec);
+    const int rows_needed = (s.P + kRpi - 1) / kRpi;  // passes that cover one head tile
+    // Deepest pipelining that still leaves >= 2048 workgroups (8 per CU).
+    int iters = 1;
+    for (int cand : {8, 4, 2}) {
+        if (cand > rows_needed) continue;
+        const int64_t wgs = (int64_t)a.batch * s.H * ((rows_needed + cand - 1) / cand);
+        if (wgs >= 2048) { iters = cand; break; }
+    }
+    switch (iters) {
+        case 8: return launch_su<ST, XT, N, 8>(s, a, stream, rows_needed);
+        case 4: return launch_su<ST, XT, N, 4>(s, a, stream, rows_needed);
+        case 2: return launch_su<ST, XT, N, 2>(s, a, stream, rows_needed);
+        default: return launch_su<ST, XT, N, 1>(s, a, stream, rows_needed);
+    }
+}
+
+template <typename ST, typename XT>
+static hipError_t dispatch_su_n(const LayerShape &s, const StateUpdateArgs &a, hipStream_t stream) {
+    switch (s.N) {
+        case 16: return dispatch_su_iters<ST, XT, 16>(s, a, stream);
+        case 64: return dispatch_su_iters<ST, XT, 64>(s, a, stream);
+        case 128: return dispatch_su_iters<ST, XT, 128>(s, a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+bool state_update_supported(const LayerShape &s) { return s.N == 16 || s.N == 64 || s.N == 128; }
+
+hipError_t launch_state_update(const LayerShape &s, const StateUpdateArgs &a, hipStream_t stream) {
+    if (a.batch == 0) return hipSuccess;
+    if (s.state_dt == DT_BF16) {
+        return s.xbc_dt == DT_BF16 ? dispatch_su_n<bf16, bf16>(s, a, stream) : dispatch_su_n<bf16, float>(s, a, stream);
+    }
+    return s.xbc_dt == DT_BF16 ? dispatch_su_n<float, bf16>(s, a, stream) : dispatch_su_n<float, float>(s, a, stream);
+}
+
+// ----------------------------------------------------------------- conv update
+// One thread per 8 channels of one row: window = [cached W-1 inputs || u],
+// out = SiLU(bias + sum_k w[k] * window[k]); the cache shifts by one.
+template <typename AT, typename ST, typename XT, int W>
+__global__ __launch_bounds__(256) void conv_update_kernel(ConvUpdateArgs a, int64_t cdim) {
+    const int row = blockIdx.y;
+    const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (c0 >= cdim) return;
+    XT *out = static_cast<XT *>(a.out) + (int64_t)row * cdim + c0;
+    const int slot = a.idx[row];
+    float o[8];
+    if (slot < 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = 0.0f;
+        store_k<XT, 8>(out, o);
+        return;
+    }
+    float u[8], win[W - 1][8], w[8 * W];
+    load_k<AT, 8>(static_cast<const AT *>(a.xbc) + (int64_t)row * cdim + c0, u);
+    ST *cache = static_cast<ST *>(a.pool) + (int64_t)slot * (W - 1) * cdim + c0;
+#pragma unroll
+    for (int k = 0; k < W - 1; ++k) load_k<ST, 8>(cache + k * cdim, win[k]);
+    load_k<float, 8 * W>(a.w + c0 * W, w);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float v = a.b ? a.b[c0 + j] : 0.0f;
+#pragma unroll
+        for (int k = 0; k < W - 1; ++k) v += w[j * W + k] * win[k][j];
+        v += w[j * W + W - 1] * u[j];
+        o[j] = silu_f(v);
+    }
+    store_k<XT, 8>(out, o);
+#pragma unroll
+    for (int k = 0; k < W - 2; ++k) store_k<ST, 8>(cache + k * cdim, win[k + 1]);
+    store_k<ST, 8>(cache + (W - 2) * cdim, u);
+}
+
+template <typename AT, typename ST, typename XT>
+static hipError_t launch_cu_w(const LayerShape &s, const ConvUpdateArgs &a, hipStream_t stream) {
+    const int64_t cdim = s.cdim();
+    dim3 grid((unsigned)((cdim / 8 + 255) / 256), a.batch);
+    switch (s.W) {
+        case 2: hipLaunchKernelGGL((conv_update_kernel<AT, ST, XT, 2>), grid, dim3(256), 0, stream, a, cdim); break;
+        case 3: hipLaunchKernelGGL((conv_update_kernel<AT, ST, XT, 3>), grid, dim3(256), 0, stream, a, cdim); break;
+        case 4: hipLaunchKernelGGL((conv_update_kernel<AT, ST, XT, 4>), grid, dim3(256), 0, stream, a, cdim); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename AT, typename ST>
+static hipError_t launch_cu_x(const LayerShape &s, const ConvUpdateArgs &a, hipStream_t stream) {
+    return s.xbc_dt == DT_BF16 ? launch_cu_w<AT, ST, bf16>(s, a, stream) : launch_cu_w<AT, ST, float>(s, a, stream);
+}
+
+template <typename AT>
+static hipError_t launch_cu_s(const LayerShape &s, const ConvUpdateArgs &a, hipStream_t stream) {
+    return s.state_dt == DT_BF16 ? launch_cu_x<AT, bf16>(s, a, stream) : launch_cu_x<AT, float>(s, a, stream);
+}
+
+hipError_t launch_conv_update(const LayerShape &s, const ConvUpdateArgs &a, hipStream_t stream) {
+    if (a.batch == 0) return hipSuccess;
+    return s.act_dt == DT_BF16 ? launch_cu_s<bf16>(s, a, stream) : launch_cu_s<float>(s, a, stream);
+}
+
+}  // namespace m2

@@ -1,0 +1,71 @@
+// Host-side launch interface between the C ABI (api.cpp) and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m2 {
+
+struct LayerShape {
+    int H, P, N, G, W, Q;
+    int act_dt, xbc_dt, state_dt, out_dt;
+    int64_t cdim() const { return (int64_t)H * P + 2LL * G * N; }
+};
+
+struct StateUpdateArgs {
+    const void *xbc;      // [batch][Cdim] post-conv
+    const void *dt_raw;   // [batch][H]
+    const float *A_log, *dt_bias, *D;
+    const void *z;        // [batch][H*P] or null
+    void *y;              // [batch][H*P]
+    void *pool;           // [slots][H][P][N]
+    const int32_t *idx;   // [batch]
+    int batch;
+};
+
+struct ConvUpdateArgs {
+    const void *xbc;      // [batch][Cdim] raw
+    const float *w, *b;   // [Cdim][W], [Cdim] or null
+    void *out;            // [batch][Cdim]
+    void *pool;           // [slots][W-1][Cdim]
+    const int32_t *idx;
+    int batch;
+};
+
+struct ConvFwdArgs {
+    const void *xbc;      // [T][Cdim] raw
+    const float *w, *b;
+    void *out;            // [T][Cdim]
+    void *pool;
+    const int32_t *cu;    // [nseq+1]
+    const int32_t *idx;   // [nseq]
+    const uint8_t *has_init;  // [nseq] or null
+    int nseq;
+    int64_t T;
+};
+
+struct ScanArgs {
+    const void *xbc;      // [T][Cdim] post-conv
+    const void *dt_raw;   // [T][H]
+    const float *A_log, *dt_bias, *D;
+    const void *z;        // [T][H*P] or null
+    void *y;              // [T][H*P]
+    void *pool;           // [slots][H][P][N]
+    const int32_t *cu, *idx;
+    const uint8_t *has_init;
+    int nseq;
+    int64_t T;
+};
+
+// Each returns hipSuccess or the launch error. `supported` queries return
+// false for shapes outside the compiled set (no launch happens).
+bool state_update_supported(const LayerShape &s);
+hipError_t launch_state_update(const LayerShape &s, const StateUpdateArgs &a, hipStream_t st);
+
+bool conv_supported(const LayerShape &s);
+hipError_t launch_conv_update(const LayerShape &s, const ConvUpdateArgs &a, hipStream_t st);
+hipError_t launch_conv_fwd(const LayerShape &s, const ConvFwdArgs &a, hipStream_t st);
+
+bool scan_supported(const LayerShape &s);
+hipError_t launch_chunk_scan(const LayerShape &s, const ScanArgs &a, hipStream_t st);
+
+}  // namespace m2

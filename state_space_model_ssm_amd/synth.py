@@ -31,11 +31,11 @@ def round_to_dtype(a: np.ndarray, dtype: str) -> np.ndarray:
     a = np.ascontiguousarray(a, dtype=np.float32)
     if dtype != BF16:
         return a
-    bits = a.view(np.uint32).astype(np.uint64)
-    # round-to-nearest-even on the upper 16 bits (finite inputs only)
-    bias = ((bits >> 16) & 1) + 0x7FFF
-    out = ((bits + bias) >> 16) << 16
-    return out.astype(np.uint32).view(np.float32)
+    bits = a.view(np.uint32)
+    # round-to-nearest-even on the upper 16 bits; cannot overflow uint32 for finite inputs
+    out = bits + (np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1)))
+    out &= np.uint32(0xFFFF0000)
+    return out.view(np.float32)
 
 
 def _normal(rng, shape, std=1.0):

@@ -1,0 +1,77 @@
+"""Shared helpers for the GPU parity tests (not collected by pytest)."""
+import numpy as np
+import torch
+
+import oracle
+from state_space_model_ssm_amd.configs import BF16, F32
+
+TD = {F32: torch.float32, BF16: torch.bfloat16}
+TOL = {F32: 1e-3, BF16: 2e-2}   # max relative error bound by stored dtype
+
+
+def dev(a, dtype):
+    """Upload float32 values (exactly representable in ``dtype``) to the GPU."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(TD[dtype]).cuda()
+
+
+def dev_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def max_rel(got, ref):
+    """max_i |got_i - ref_i| / max_i |ref_i| (per compared tensor)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if got.size == 0:
+        return 0.0
+    assert np.all(np.isfinite(got)), "non-finite values in GPU output"
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+def assert_close(got, ref, dtype, what):
+    err = max_rel(got, ref)
+    assert err <= TOL[dtype], f"{what}: max relative error {err:.3e} > {TOL[dtype]:.0e} ({dtype})"
+    return err
+
+
+def params_dev(p):
+    return {"conv_w": dev(p["conv_w"], F32), "conv_b": None if p["conv_b"] is None else dev(p["conv_b"], F32),
+            "A_log": dev(p["A_log"], F32), "dt_bias": dev(p["dt_bias"], F32), "D": dev(p["D"], F32)}
+
+
+def oracle_kw(d):
+    return dict(H=d.nheads, P=d.headdim, N=d.dstate, G=d.ngroups)
+
+
+def compact_pools(w, slots):
+    """fp64 copies of the listed slots (the oracle's pools), in list order."""
+    s = np.asarray(slots, np.int64)
+    return (w["conv_pool"][s].astype(np.float64), w["ssm_pool"][s].astype(np.float64))
+
+
+def oracle_head_seq(d, params, xbc_raw, dt_raw, head, z=None, conv_state=None, ssm_state=None):
+    """Oracle restricted to one head of one sequence (conv is per channel, heads are
+    independent): slice the head's x channels and its group's B/C channels."""
+    H, P, N, G = d.nheads, d.headdim, d.dstate, d.ngroups
+    g = head // (H // G)
+    ch = np.concatenate([np.arange(head * P, head * P + P), H * P + g * N + np.arange(N),
+                         H * P + G * N + g * N + np.arange(N)])
+    sub = {"conv_w": params["conv_w"][ch], "conv_b": None if params["conv_b"] is None else params["conv_b"][ch],
+           "A_log": params["A_log"][head:head + 1], "dt_bias": params["dt_bias"][head:head + 1],
+           "D": params["D"][head:head + 1]}
+    cs = np.zeros((d.conv_width - 1, len(ch))) if conv_state is None else conv_state[:, ch]
+    hs = np.zeros((1, P, N)) if ssm_state is None else ssm_state[head:head + 1]
+    zz = None if z is None else z[:, head * P:(head + 1) * P]
+    y, post, cs2, hs2 = oracle.layer_seq(xbc_raw[:, ch], dt_raw[:, head:head + 1], sub, cs, hs, H=1, P=P, N=N, G=1,
+                                         z=zz)
+    return y, hs2[0]

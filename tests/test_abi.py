@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol,
+sizes match the pages' arithmetic, invalid arguments are rejected before any HIP
+call, the slot allocator works, and the library links no allocator or memset."""
+import ctypes
+import json
+import os
+import subprocess
+
+import pytest
+
+from state_space_model_ssm_amd import binding as B
+from state_space_model_ssm_amd.configs import BF16, F32, NEMOTRON_H_8B, NEMOTRON_H_8B_MAMBA_LAYERS, TINY, Dims
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from state_space_model_ssm_amd import build
+        build.build()
+    return B.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = B.header_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    assert set(names) <= exported
+
+
+def test_library_links_no_allocator_or_memset(lib):
+    """Decode and scan entry points never allocate or clear device memory (the vllm.cpp issue's
+    cost table: 0 alloc/free, 0 memset per layer per token)."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", B.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    bad = [ln for ln in out.splitlines() if any(k in ln for k in ("hipMalloc", "hipFree", "hipMemset",
+                                                                   "hipDeviceSynchronize", "hipStreamSynchronize"))]
+    assert not bad, bad
+
+
+def test_slot_sizes_match_page_arithmetic(lib):
+    g = json.load(open(os.path.join(GOLDEN, "page_sizes.json")))
+    d = Dims(g["nheads"], g["headdim"], g["dstate"], g["ngroups"], state_dtype=BF16)
+    assert B.mamba2_ssm_slot_bytes(d) == g["ssm_bytes_per_layer_per_seq"]
+    assert B.mamba2_ssm_slot_bytes(d) * NEMOTRON_H_8B_MAMBA_LAYERS == g["ssm_bytes_per_seq"]
+    assert NEMOTRON_H_8B_MAMBA_LAYERS == g["mamba_layers"]
+    assert B.mamba2_ssm_slot_bytes(d.with_(state_dtype=F32)) == 2 * g["ssm_bytes_per_layer_per_seq"]
+    assert B.mamba2_conv_slot_bytes(d) == 3 * (128 * 64 + 2 * 8 * 128) * 2
+    assert B.mamba2_chunk_scan_workspace_bytes(NEMOTRON_H_8B, 32768, 4) == 0
+
+
+def test_check_dims(lib):
+    B.mamba2_check_dims(NEMOTRON_H_8B)
+    B.mamba2_check_dims(TINY)
+    with pytest.raises(B.Mamba2Error) as e:
+        B.mamba2_check_dims(NEMOTRON_H_8B.with_(ngroups=3))
+    assert e.value.status == B.ERR_INVALID_ARG
+    with pytest.raises(B.Mamba2Error) as e:
+        B.mamba2_check_dims(NEMOTRON_H_8B.with_(chunk_size=256))
+    assert e.value.status == B.ERR_UNSUPPORTED
+    with pytest.raises(B.Mamba2Error) as e:
+        B.mamba2_check_dims(NEMOTRON_H_8B.with_(dstate=48))
+    assert e.value.status == B.ERR_UNSUPPORTED
+
+
+def _cd(d=NEMOTRON_H_8B):
+    return ctypes.byref(B.cdims(d))
+
+
+def test_invalid_arguments_rejected_without_gpu(lib):
+    P = ctypes.c_void_p
+    good = P(0x10000)
+    mis = P(0x10004)
+    # NULL required pointer
+    st = lib.mamba2_state_update(_cd(), None, good, good, good, good, None, good, good, good, 4, None)
+    assert st == B.ERR_INVALID_ARG and b"xbc" in lib.mamba2_last_error()
+    # misaligned pointer
+    st = lib.mamba2_state_update(_cd(), mis, good, good, good, good, None, good, good, good, 4, None)
+    assert st == B.ERR_INVALID_ARG and b"aligned" in lib.mamba2_last_error()
+    # negative batch
+    st = lib.mamba2_state_update(_cd(), good, good, good, good, good, None, good, good, good, -1, None)
+    assert st == B.ERR_INVALID_ARG
+    # zero rows: valid, nothing enqueued
+    assert lib.mamba2_state_update(_cd(), None, None, None, None, None, None, None, None, None, 0, None) == B.OK
+    assert lib.mamba2_conv1d_update(_cd(), None, None, None, None, None, None, 0, None) == B.OK
+    assert lib.mamba2_conv1d_fwd(_cd(), None, None, None, None, None, None, 0, 0, None, None, None) == B.OK
+    # aliasing conv output
+    st = lib.mamba2_conv1d_update(_cd(), good, good, None, good, good, good, 2, None)
+    assert st == B.ERR_INVALID_ARG and b"alias" in lib.mamba2_last_error()
+    # tokens without sequences
+    st = lib.mamba2_chunk_scan_fwd(_cd(), good, good, good, good, good, None, good, good, good, 0, 5, good, None,
+                                   None, 0, None)
+    assert st == B.ERR_INVALID_ARG
+    # unsupported chunk
+    st = lib.mamba2_chunk_scan_fwd(_cd(NEMOTRON_H_8B.with_(chunk_size=96)), good, good, good, good, good, None, good,
+                                   good, good, 1, 5, good, None, None, 0, None)
+    assert st == B.ERR_UNSUPPORTED
+    assert lib.mamba2_status_string(B.ERR_UNSUPPORTED) == b"unsupported dims or dtype"
+
+
+def test_slot_allocator(lib):
+    a = B.SlotAllocator(3)
+    got = [a.alloc(), a.alloc(), a.alloc()]
+    assert sorted(got) == [0, 1, 2] and a.in_use == 3
+    with pytest.raises(B.Mamba2Error) as e:
+        a.alloc()
+    assert e.value.status == B.ERR_NO_SLOT
+    a.free(1)
+    assert a.in_use == 2 and a.alloc() == 1
+    with pytest.raises(B.Mamba2Error):
+        a.free(7)
+    a.free(2)
+    with pytest.raises(B.Mamba2Error):
+        a.free(2)  # double free
+    a.close()
+
+
+def test_binding_rejects_host_tensors(lib):
+    import torch
+    d = TINY
+    x = torch.zeros(2, d.conv_dim)
+    with pytest.raises(ValueError, match="device tensor"):
+        B.mamba2_conv1d_update(d, x, torch.zeros(d.conv_dim, 4), None, x.clone(), torch.zeros(4, 3, d.conv_dim),
+                               torch.zeros(2, dtype=torch.int32))

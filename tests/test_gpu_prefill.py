@@ -1,0 +1,220 @@
+"""GPU parity of the prefill path (conv1d_fwd + chunk_scan_fwd), the equivalence
+contract (chunk scan == repeated single steps) and mixed batches, against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _helpers import (assert_close, compact_pools, dev, dev_i32, dev_u8, host, oracle_head_seq, oracle_kw,
+                      params_dev)
+from state_space_model_ssm_amd import binding as B
+from state_space_model_ssm_amd import synth
+from state_space_model_ssm_amd.configs import BF16, F32, NEMOTRON_H_8B, TINY
+
+pytestmark = pytest.mark.gpu
+
+# Nemotron-H-8B head shape (P=64, N=128) with fewer heads so the oracle stays fast.
+D16 = NEMOTRON_H_8B.with_(nheads=16, ngroups=2, chunk_size=64, state_dtype=F32, out_dtype=F32)
+
+
+def run_prefill(d, w, has_init=None, slots=None):
+    pd = params_dev(w["params"])
+    T = w["xbc"].shape[0]
+    slots = w["slots"] if slots is None else slots
+    has_init = w["has_initial_state"] if has_init is None else has_init
+    ssm = dev(w["ssm_pool"], d.state_dtype)
+    conv = dev(w["conv_pool"], d.state_dtype)
+    xbc, dt = dev(w["xbc"], d.act_dtype), dev(w["dt_raw"], d.act_dtype)
+    z = None if w["z"] is None else dev(w["z"], d.act_dtype)
+    post = torch.empty(T, d.conv_dim, dtype=B._TORCH_DT[d.post_dtype], device="cuda")
+    y = torch.empty(T, d.d_inner, dtype=B._TORCH_DT[d.out_dtype], device="cuda")
+    cu, idx, hi = dev_i32(w["cu_seqlens"]), dev_i32(slots), dev_u8(has_init)
+    B.mamba2_conv1d_fwd(d, xbc, pd["conv_w"], pd["conv_b"], post, conv, cu, idx, hi)
+    B.mamba2_chunk_scan_fwd(d, post, dt, pd["A_log"], pd["dt_bias"], pd["D"], z, y, ssm, cu, idx, hi)
+    torch.cuda.synchronize()
+    return y, post, ssm, conv
+
+
+def oracle_prefill(d, w, has_init=None, slots=None):
+    slots = w["slots"] if slots is None else slots
+    has_init = w["has_initial_state"] if has_init is None else has_init
+    used = [s for s in slots if s >= 0]
+    cp, sp = compact_pools(w, used)
+    pos = {int(s): i for i, s in enumerate(used)}
+    cidx = np.array([pos[int(s)] if s >= 0 else -1 for s in slots])
+    y, post = oracle.prefill(w["xbc"], w["dt_raw"], w["params"], w["cu_seqlens"], cidx, has_init, cp, sp, z=w["z"],
+                             **oracle_kw(d))
+    return y, post, cp, sp, used
+
+
+def check_prefill(d, w, has_init=None, slots=None):
+    y, post, ssm, conv = run_prefill(d, w, has_init, slots)
+    y_ref, post_ref, cp, sp, used = oracle_prefill(d, w, has_init, slots)
+    e_post = assert_close(host(post), post_ref, d.post_dtype, "post-conv xBC")
+    e_y = assert_close(host(y), y_ref, d.out_dtype, "y")
+    u = torch.tensor(used, dtype=torch.long, device="cuda")
+    e_h = assert_close(host(ssm[u]), sp, d.state_dtype, "final ssm state")
+    assert np.array_equal(host(conv[u]), cp), "conv cache must hold the exact raw inputs"
+    return y, ssm, conv, (e_post, e_y, e_h)
+
+
+def test_tiny_prefill_then_decode():
+    """Tiny fp32 layer: 64-token prefill (chunk 16) then 8 single-token steps."""
+    d = TINY
+    w = synth.tiny(d, seed=0)
+    pre = {**w["prefill"], "params": w["params"], "slots": w["slots"], "cu_seqlens": w["cu_seqlens"],
+           "has_initial_state": w["has_initial_state"], "ssm_pool": w["ssm_pool"], "conv_pool": w["conv_pool"]}
+    y, post, ssm, conv = run_prefill(d, pre)
+    cp, sp = compact_pools(w, w["slots"])
+    cp[:] = 0.0
+    sp[:] = 0.0
+    kw = oracle_kw(d)
+    y_ref, _ = oracle.prefill(pre["xbc"], pre["dt_raw"], w["params"], w["cu_seqlens"], [0], None, cp, sp,
+                              z=pre["z"], **kw)
+    assert_close(host(y), y_ref, F32, "prefill y")
+    slot = int(w["slots"][0])
+    assert_close(host(ssm[slot:slot + 1]), sp, F32, "state after prefill")
+    pd = params_dev(w["params"])
+    idx = dev_i32(w["slots"])
+    for step in w["decode"]:
+        xb, dt, z = dev(step["xbc"], F32), dev(step["dt_raw"], F32), dev(step["z"], F32)
+        post1 = torch.empty(1, d.conv_dim, device="cuda")
+        y1 = torch.empty(1, d.d_inner, device="cuda")
+        B.mamba2_conv1d_update(d, xb, pd["conv_w"], None, post1, conv, idx)
+        B.mamba2_state_update(d, post1, dt, pd["A_log"], pd["dt_bias"], pd["D"], z, y1, ssm, idx)
+        yr, _ = oracle.decode(step["xbc"], step["dt_raw"], w["params"], [0], cp, sp, z=step["z"], **kw)
+        torch.cuda.synchronize()
+        assert_close(host(y1), yr, F32, "decode y")
+    assert_close(host(ssm[slot:slot + 1]), sp, F32, "state after decode")
+    assert np.array_equal(host(conv[slot:slot + 1]), cp)
+
+
+@pytest.mark.parametrize("out_dtype", [F32, BF16])
+@pytest.mark.parametrize("state_dtype", [F32, BF16])
+def test_varlen_prefill_matches_oracle(out_dtype, state_dtype):
+    """Several chunks per sequence with ragged tails (lengths 1, 37, 130, 200 at chunk 64),
+    half of the sequences resuming from a saved state."""
+    d = D16.with_(out_dtype=out_dtype, state_dtype=state_dtype)
+    print(f"[prefill parity] out={out_dtype} state={state_dtype}", flush=True)
+    w = synth.prefill_batch(d, seed=7, seqlens=[1, 37, 130, 200], num_slots=9, initial_state=True)
+    has_init = np.array([1, 0, 1, 0], np.uint8)
+    check_prefill(d, w, has_init=has_init)
+
+
+def test_prefill_with_z_gate_and_tiny_dims():
+    d = TINY
+    w = synth.prefill_batch(d, seed=8, seqlens=[5, 16, 17, 40], num_slots=6, initial_state=True)
+    check_prefill(d, w, has_init=np.array([0, 1, 1, 0], np.uint8))
+
+
+def test_packed_equals_separate_runs_bitwise():
+    """Packing sequences with cu_seqlens changes nothing: each sequence's outputs are bit-identical."""
+    d = D16
+    w = synth.prefill_batch(d, seed=9, seqlens=[70, 3, 129], num_slots=3, initial_state=False)
+    y_all, _, ssm_all, _ = run_prefill(d, w)
+    cu = w["cu_seqlens"]
+    for i in range(3):
+        s, e = int(cu[i]), int(cu[i + 1])
+        wi = {**w, "xbc": w["xbc"][s:e], "dt_raw": w["dt_raw"][s:e], "z": w["z"][s:e],
+              "cu_seqlens": np.array([0, e - s], np.int32), "slots": w["slots"][i:i + 1],
+              "has_initial_state": w["has_initial_state"][i:i + 1]}
+        yi, _, ssmi, _ = run_prefill(d, wi)
+        assert torch.equal(yi, y_all[s:e])
+        sl = int(w["slots"][i])
+        assert torch.equal(ssmi[sl], ssm_all[sl])
+
+
+@pytest.mark.parametrize("dims,qs", [(D16, (64, 128)), (TINY, (16, 32))])
+def test_chunk_size_invariance(dims, qs):
+    w = synth.prefill_batch(dims, seed=10, seqlens=[150, 77], num_slots=2, initial_state=True)
+    outs = [run_prefill(dims.with_(chunk_size=q), w, has_init=np.array([1, 1], np.uint8)) for q in qs]
+    assert_close(host(outs[1][0]), host(outs[0][0]), dims.out_dtype, "y across chunk sizes")
+    assert_close(host(outs[1][2]), host(outs[0][2]), dims.state_dtype, "state across chunk sizes")
+
+
+def test_equivalence_contract_scan_equals_repeated_steps():
+    """A T-token chunk scan equals T single-token state updates (GPU vs GPU)."""
+    d = D16
+    T = 150
+    w = synth.prefill_batch(d, seed=11, seqlens=[T], num_slots=1, initial_state=True)
+    hi = np.array([1], np.uint8)
+    y_scan, _, ssm_scan, conv_scan = run_prefill(d, w, has_init=hi)
+    pd = params_dev(w["params"])
+    ssm = dev(w["ssm_pool"], d.state_dtype)
+    conv = dev(w["conv_pool"], d.state_dtype)
+    idx = dev_i32(w["slots"])
+    xbc, dt, z = dev(w["xbc"], d.act_dtype), dev(w["dt_raw"], d.act_dtype), dev(w["z"], d.act_dtype)
+    ys = torch.empty(T, d.d_inner, device="cuda")
+    post = torch.empty(1, d.conv_dim, dtype=B._TORCH_DT[d.post_dtype], device="cuda")
+    for t in range(T):
+        B.mamba2_conv1d_update(d, xbc[t:t + 1], pd["conv_w"], None, post, conv, idx)
+        B.mamba2_state_update(d, post, dt[t:t + 1], pd["A_log"], pd["dt_bias"], pd["D"], z[t:t + 1], ys[t:t + 1],
+                              ssm, idx)
+    torch.cuda.synchronize()
+    assert_close(host(y_scan), host(ys), F32, "y: scan vs steps")
+    assert_close(host(ssm_scan), host(ssm), F32, "state: scan vs steps")
+    assert torch.equal(conv_scan, conv)
+
+
+def test_padding_and_empty_sequences():
+    d = D16
+    w = synth.prefill_batch(d, seed=12, seqlens=[40, 0, 33, 0], num_slots=6, initial_state=True)
+    slots = w["slots"].copy()
+    slots[2] = -1  # padding sequence
+    has_init = np.array([1, 1, 0, 0], np.uint8)
+    y, post, ssm, conv = run_prefill(d, w, has_init=has_init, slots=slots)
+    cu = w["cu_seqlens"]
+    assert torch.all(y[int(cu[2]):int(cu[3])] == 0).item()
+    pad_slot = int(w["slots"][2])
+    assert np.array_equal(host(ssm[pad_slot]), w["ssm_pool"][pad_slot].astype(np.float64))
+    # empty sequence with a saved state keeps it; empty sequence without one ends at zero
+    assert np.array_equal(host(ssm[int(slots[1])]), w["ssm_pool"][slots[1]].astype(np.float64))
+    assert torch.all(ssm[int(slots[3])] == 0).item()
+    check_prefill(d, w, has_init=has_init, slots=slots)
+
+
+def test_full_size_prefill_sampled():
+    """The timed prefill workload (4 x 8192 tokens, 128 heads, chunk 128, bf16 y, fp32 state)
+    in the benchmark's launch configuration, checked on sampled (sequence, head) pairs."""
+    d = NEMOTRON_H_8B.with_(state_dtype=F32)
+    print("[prefill parity] full size 4x8192", flush=True)
+    w = synth.prefill_batch(d, seed=2, seqlens=[8192] * 4, num_slots=8, with_z=False)
+    y, _, ssm, _ = run_prefill(d, w)
+    yh = y.float().cpu().numpy()
+    cu = w["cu_seqlens"]
+    for seq, head in [(0, 0), (1, 37), (2, 77), (3, 127), (0, 64), (3, 15)]:
+        s, e = int(cu[seq]), int(cu[seq + 1])
+        yr, hr = oracle_head_seq(d, w["params"], w["xbc"][s:e], w["dt_raw"][s:e], head)
+        assert_close(yh[s:e, head * 64:(head + 1) * 64], yr, BF16, f"y seq {seq} head {head}")
+        assert_close(host(ssm[int(w["slots"][seq]), head]), hr, F32, f"state seq {seq} head {head}")
+
+
+def test_mixed_batch_matches_oracle():
+    """Varlen prefill sequences and decode rows in one call (fp32 pool)."""
+    d = D16
+    w = synth.mixed_batch(d, seed=3, num_prefill=3, len_lo=20, len_hi=150, decode_rows=5, num_slots=16,
+                          with_z=True)
+    pd = params_dev(w["params"])
+    T = int(w["cu_seqlens"][-1])
+    rows = T + 5
+    xbc = dev(np.concatenate([w["prefill"]["xbc"], w["decode"]["xbc"]]), d.act_dtype)
+    dt = dev(np.concatenate([w["prefill"]["dt_raw"], w["decode"]["dt_raw"]]), d.act_dtype)
+    z = dev(np.concatenate([w["prefill"]["z"], w["decode"]["z"]]), d.act_dtype)
+    ssm, conv = dev(w["ssm_pool"], d.state_dtype), dev(w["conv_pool"], d.state_dtype)
+    post = torch.empty(rows, d.conv_dim, dtype=B._TORCH_DT[d.post_dtype], device="cuda")
+    y = torch.empty(rows, d.d_inner, dtype=B._TORCH_DT[d.out_dtype], device="cuda")
+    B.mamba2_mixed_fwd(d, xbc, dt, z, pd["conv_w"], None, pd["A_log"], pd["dt_bias"], pd["D"], post, y, ssm, conv,
+                       dev_i32(w["cu_seqlens"]), dev_i32(w["prefill_slots"]), dev_u8(w["has_initial_state"]),
+                       dev_i32(w["decode_slots"]))
+    torch.cuda.synchronize()
+    allslots = np.concatenate([w["prefill_slots"], w["decode_slots"]])
+    cp, sp = compact_pools(w, allslots)
+    kw = oracle_kw(d)
+    yp, _ = oracle.prefill(w["prefill"]["xbc"], w["prefill"]["dt_raw"], w["params"], w["cu_seqlens"],
+                           np.arange(3), w["has_initial_state"], cp, sp, z=w["prefill"]["z"], **kw)
+    yd, _ = oracle.decode(w["decode"]["xbc"], w["decode"]["dt_raw"], w["params"], np.arange(3, 8), cp, sp,
+                          z=w["decode"]["z"], **kw)
+    assert_close(host(y), np.concatenate([yp, yd]), d.out_dtype, "mixed y")
+    u = torch.from_numpy(allslots.astype(np.int64)).cuda()
+    assert_close(host(ssm[u]), sp, d.state_dtype, "mixed states")
+    assert np.array_equal(host(conv[u]), cp)
