@@ -73,6 +73,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device-to-device copy (known bytes) for counter calibration")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build's hot path runs on a single MI355X "
@@ -180,7 +182,7 @@ def main():
         hi2 = torch.zeros(4, dtype=torch.uint8, device="cuda")
         post2 = torch.empty(T, d2.conv_dim, dtype=torch.float32, device="cuda")
         y2 = torch.empty(T, d2.d_inner, dtype=bf, device="cuda")
-        host_pre = {"xbc": w2["xbc"][:256].copy(), "dt_raw": w2["dt_raw"][:256].copy(), "params": w2["params"]}
+        host_pre = {"xbc": w2["xbc"][:8192].copy(), "dt_raw": w2["dt_raw"][:8192].copy(), "params": w2["params"]}
         del w2
 
         def conv_fwd():
@@ -230,30 +232,44 @@ def main():
         os.environ.setdefault("OMP_NUM_THREADS", str(cores))
         ssm_h = host_slots[0].astype(np.float64)
         conv_h = host_slots[1].astype(np.float64)
+        nrow = ssm_h.shape[0]
         t0 = time.perf_counter()
         done = 0
-        while done < 64 and time.perf_counter() - t0 < args.cpu_seconds:
-            oracle.decode(host_tok["xbc"][done:done + 1], host_tok["dt_raw"][done:done + 1], host_params, [0],
-                          conv_h[done:done + 1], ssm_h[done:done + 1], **kw)
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            i = done % nrow  # cycle over the sampled rows; each call is one full layer step of one row
+            oracle.decode(host_tok["xbc"][i:i + 1], host_tok["dt_raw"][i:i + 1], host_params, [0],
+                          conv_h[i:i + 1], ssm_h[i:i + 1], **kw)
             done += 1
         el = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": round(done / el, 2), "unit": "tok/s", "cores": cores, "kind": "oracle",
-                                  "sample": f"{done} of the 256 decode rows (one layer step each) through the fp64 "
-                                            f"C oracle, {el:.1f} s"}
+                                  "sample": f"{done} decode row-steps (cycling over {nrow} of the 256 rows, all 128 "
+                                            f"heads each) through the fp64 C oracle in {el:.1f} s"}
         log(f"cpu baseline: {done} rows in {el:.1f} s on {cores} threads")
         if not args.no_prefill:
             t0 = time.perf_counter()
             n = 0
+            T1 = host_pre["xbc"].shape[0]
             cs = np.zeros((d.conv_width - 1, d.conv_dim))
             hs = np.zeros((d.nheads, d.headdim, d.dstate))
-            while n < 256 and time.perf_counter() - t0 < args.cpu_seconds:
-                _, _, cs, hs = oracle.layer_seq(host_pre["xbc"][n:n + 32], host_pre["dt_raw"][n:n + 32],
+            while n < T1 and time.perf_counter() - t0 < args.cpu_seconds:
+                _, _, cs, hs = oracle.layer_seq(host_pre["xbc"][n:n + 64], host_pre["dt_raw"][n:n + 64],
                                                 host_pre["params"], cs, hs, **kw)
-                n += 32
+                n += 64
             el = time.perf_counter() - t0
             result["prefill"]["cpu_baseline"] = {
                 "value": round(n / el, 2), "unit": "tok/s", "cores": cores, "kind": "oracle",
-                "sample": f"first {n} tokens of one 8192-token sequence through the fp64 C oracle, {el:.1f} s"}
+                "sample": f"first {n} tokens of one 8192-token sequence (all 128 heads) through the fp64 C oracle "
+                          f"in {el:.1f} s"}
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        torch.cuda.synchronize()
+        ms_copy = time_region(lambda: dst.copy_(src), 5, torch)
+        result["copy_calibration"] = {"bytes_read": 1 << 30, "bytes_written": 1 << 30, "launches": 5,
+                                      "gbs": round(2 * (1 << 30) / (ms_copy * 1e-3) / 1e9, 1)}
+        del src, dst
 
     print(json.dumps(result), flush=True)
 

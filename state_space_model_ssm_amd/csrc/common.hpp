@@ -9,6 +9,7 @@ namespace m2 {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 enum Dt : int { DT_F32 = 0, DT_BF16 = 1 };
 
@@ -86,6 +87,33 @@ template <typename T, int K> __device__ __forceinline__ void store_k(T *p, const
     } else {
 #pragma unroll
         for (int i = 0; i < K; ++i) p[i] = f32_to_bf16(in[i]);
+    }
+}
+
+// 16-byte streaming (nontemporal) access: data touched once per launch should
+// not displace reusable lines from L2 / the memory-side cache.
+template <typename T> __device__ __forceinline__ void nt_load16(const T *p, float *out) {
+    if constexpr (sizeof(T) == 4) {
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+        out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+    } else {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(v[i] << 16);
+            out[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+        }
+    }
+}
+template <typename T> __device__ __forceinline__ void nt_store16(T *p, const float *in) {
+    if constexpr (sizeof(T) == 4) {
+        const f32x4 v = {in[0], in[1], in[2], in[3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
+    } else {
+        bf16x8 b;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) b[i] = f32_to_bf16(in[i]);
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(&b), reinterpret_cast<u32x4 *>(p));
     }
 }
 
