@@ -51,6 +51,26 @@ def scan_algorithmic(d, tokens, nseq, xbc_bytes, y_bytes, state_bytes):
     return nbytes, flops_per_tok * tokens
 
 
+def profiled_traffic(kernel):
+    """HBM bytes per launch of `kernel` as measured by the rocprofv3 FETCH_SIZE/WRITE_SIZE runs
+    recorded under profiles/ (calibrated against a plain copy). None when no record exists or
+    when the kernel's sources changed since the counters were taken."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            if not line.startswith("traffic-json:"):
+                continue
+            rec = json.loads(line.split(":", 1)[1])
+            if rec.get("kernel") != kernel:
+                continue
+            h = hashlib.sha256()
+            for f in rec["sources"]:
+                h.update(open(os.path.join(ROOT, "state_space_model_ssm_amd", "csrc", f), "rb").read())
+            return rec["bytes_per_launch"] if h.hexdigest()[:16] == rec["src_sha"] else None
+    return None
+
+
 def time_region(fn, iters, torch):
     """Average ms of fn() over iters, HIP events on the current stream."""
     s = torch.cuda.Event(enable_timing=True)
@@ -64,6 +84,81 @@ def time_region(fn, iters, torch):
     return s.elapsed_time(e) / iters
 
 
+def bench_stack(args, torch, np, B, synth, d, dev, bf, time_region):
+    """48 Mamba-2 layers x 32 decode steps at several concurrencies, eager and as one
+    captured HIP graph per run. Layer l has its own seeded parameters and an input
+    buffer of c + 31 rows (step s reads rows [s, s + c)); each layer has its own
+    bf16 state and conv pools of c slots, read and written in place every step."""
+    from state_space_model_ssm_amd.configs import NEMOTRON_H_8B_MAMBA_LAYERS as NL
+    conc = [int(c) for c in args.stack_concurrency.split(",") if c]
+    steps = 32
+    cmax = max(conc)
+    log(f"stack workload: {NL} layers x {steps} steps, concurrency {conc}; generating per-layer inputs")
+    layers = []
+    for l in range(NL):
+        w = synth.stack_layer(d, seed=4, layer=l, concurrency=cmax, steps=steps)
+        layers.append({"xbc": dev(w["xbc"], bf), "dt": dev(w["dt_raw"], bf),
+                       "conv_w": dev(w["params"]["conv_w"], torch.float32),
+                       "A_log": dev(w["params"]["A_log"], torch.float32),
+                       "dt_bias": dev(w["params"]["dt_bias"], torch.float32),
+                       "D": dev(w["params"]["D"], torch.float32)})
+    gen = torch.Generator(device="cuda")
+    row_b = decode_bytes_per_row(d, 2)[2]
+    out = {"workload": f"{NL}-layer Mamba-2 decode stack at Nemotron-H-8B dims, bf16 state (96 MiB per sequence), "
+                       f"{steps} steps of one token; per-layer seeded parameters and inputs; state pools filled "
+                       "on the device from a seeded normal generator (std sqrt(0.1))",
+           "layers": NL, "steps": steps, "points": []}
+    for c in conc:
+        gen.manual_seed(1000 + c)
+        pools = []
+        for l in range(NL):
+            ssm = torch.empty(c, d.nheads, d.headdim, d.dstate, dtype=bf, device="cuda")
+            ssm.normal_(0.0, 0.1 ** 0.5, generator=gen)
+            conv = torch.empty(c, d.conv_width - 1, d.conv_dim, dtype=bf, device="cuda")
+            conv.normal_(0.0, 1.0, generator=gen)
+            pools.append((ssm, conv))
+        idx = torch.arange(c, dtype=torch.int32, device="cuda")
+        post = torch.empty(c, d.conv_dim, dtype=bf, device="cuda")
+        y = torch.empty(c, d.d_inner, dtype=bf, device="cuda")
+
+        def run(steps_=steps):
+            for s_ in range(steps_):
+                for L, (ssm, conv) in zip(layers, pools):
+                    xb = L["xbc"][s_:s_ + c]
+                    B.mamba2_conv1d_update(d, xb, L["conv_w"], None, post, conv, idx)
+                    B.mamba2_state_update(d, post, L["dt"][s_:s_ + c], L["A_log"], L["dt_bias"], L["D"], None, y,
+                                          ssm, idx)
+
+        run(1)
+        torch.cuda.synchronize()
+        ms_eager = time_region(run, 1, torch)
+        graph = torch.cuda.CUDAGraph()
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            graph.capture_begin()
+            run()
+            graph.capture_end()
+        torch.cuda.current_stream().wait_stream(stream)
+        graph.replay()
+        torch.cuda.synchronize()
+        ms_graph = time_region(graph.replay, 1, torch)
+        tok = c * steps
+        bytes_ = row_b * c * NL * steps
+        pt = {"concurrency": c,
+              "eager": {"tok_s": round(tok / (ms_eager * 1e-3), 1), "ms_per_step": round(ms_eager / steps, 4),
+                        "hbm_frac": round(bytes_ / (ms_eager * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+              "graph": {"tok_s": round(tok / (ms_graph * 1e-3), 1), "ms_per_step": round(ms_graph / steps, 4),
+                        "hbm_frac": round(bytes_ / (ms_graph * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+        if c <= 16:
+            pt["note"] = "per-layer working set fits the 256 MB memory-side cache: launch-bound, not HBM-bound"
+        out["points"].append(pt)
+        log(f"stack c={c}: eager {ms_eager / steps * 1e3:.0f} us/step, graph {ms_graph / steps * 1e3:.0f} us/step")
+        del graph, pools, post, y
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -73,6 +168,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill+decode batch")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 48-layer decode stack sweep")
+    ap.add_argument("--stack-concurrency", default="1,16,64,256,1024")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device-to-device copy (known bytes) for counter calibration")
     args = ap.parse_args()
@@ -156,7 +254,7 @@ def main():
                    "rows": rows, "pool_slots": nslots, "state_dtype": "bf16", "act_dtype": "bf16"},
         "roofline": {"bound": "hbm", "kernel": "state_update_kernel", "achieved": round(su_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(su_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": su_b * rows,
+                     "traffic": profiled_traffic("state_update_kernel"), "algorithmic_bytes_per_launch": su_b * rows,
                      "avg_launch_us": round(ms_su * 1e3, 2)},
         "decode_detail": {"us_per_step": round(ms_step * 1e3, 2), "state_update_us": round(ms_su * 1e3, 2),
                           "conv_update_us": round(ms_conv * 1e3, 2),
@@ -217,12 +315,58 @@ def main():
             "chunk_scan_us": round(ms_scan * 1e3, 2), "conv1d_fwd_us": round(ms_cf * 1e3, 2),
             "roofline": {"bound": "mfma", "kernel": "chunk_scan_kernel", "achieved": round(scan_tfs, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(scan_tfs / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "frac": round(scan_tfs / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": profiled_traffic("chunk_scan_fast_kernel"),
                          "algorithmic_flops_per_launch": sf, "algorithmic_bytes_per_launch": sb,
                          "hbm_achieved_gbs": round(scan_gbs, 1), "hbm_frac": round(scan_gbs / HBM_PEAK_GBS, 4)},
         }
         del xbc2, dt2, pool2, convp2, post2, y2
         torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ mixed prefill + decode batch
+    if not args.no_mixed:
+        d3 = NEMOTRON_H_8B.with_(state_dtype=F32)
+        log("mixed workload: 8 prefill sequences U[256,4096] + 384 decode rows, 1024-slot fp32 pool")
+        w3 = synth.mixed_batch(d3, seed=3, num_prefill=8, len_lo=256, len_hi=4096, decode_rows=384, num_slots=1024)
+        T3 = int(w3["cu_seqlens"][-1])
+        rows3 = T3 + 384
+        xbc3 = dev(np.concatenate([w3["prefill"]["xbc"], w3["decode"]["xbc"]]), bf)
+        dt3 = dev(np.concatenate([w3["prefill"]["dt_raw"], w3["decode"]["dt_raw"]]), bf)
+        ssm3 = dev(w3["ssm_pool"], torch.float32)
+        conv3 = dev(w3["conv_pool"], torch.float32)
+        cw3 = dev(w3["params"]["conv_w"], torch.float32)
+        A3, dtb3, D3 = (dev(w3["params"][k], torch.float32) for k in ("A_log", "dt_bias", "D"))
+        cu3 = torch.from_numpy(w3["cu_seqlens"]).cuda()
+        pidx3 = torch.from_numpy(w3["prefill_slots"]).cuda()
+        didx3 = torch.from_numpy(w3["decode_slots"]).cuda()
+        hi3 = torch.from_numpy(w3["has_initial_state"]).cuda()
+        post3 = torch.empty(rows3, d3.conv_dim, dtype=torch.float32, device="cuda")
+        y3 = torch.empty(rows3, d3.d_inner, dtype=bf, device="cuda")
+        del w3
+
+        def mixed_step():
+            B.mamba2_mixed_fwd(d3, xbc3, dt3, None, cw3, None, A3, dtb3, D3, post3, y3, ssm3, conv3, cu3, pidx3, hi3,
+                               didx3)
+
+        for _ in range(2):
+            mixed_step()
+        ms_mix = time_region(mixed_step, max(3, args.prefill_steps), torch)
+        dec_b = 384 * decode_bytes_per_row(d3, 4)[2]
+        pre_b, _ = scan_algorithmic(d3, T3, 8, 2, 2, 4)
+        result["mixed"] = {
+            "workload": f"one Nemotron-H-8B layer: 8 prefill sequences ({T3} tokens, lengths U[256,4096], "
+                        "cu_seqlens) + 384 decode rows, 1024-slot fp32 state pool; step = mamba2_mixed_fwd",
+            "value": round(rows3 / (ms_mix * 1e-3), 1), "unit": "tok/s", "ms_per_step": round(ms_mix, 4),
+            "prefill_tokens": T3, "decode_rows": 384,
+            "algorithmic_bytes": int(dec_b + pre_b),
+            "hbm_frac": round((dec_b + pre_b) / (ms_mix * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"mixed: {ms_mix * 1e3:.1f} us/step ({rows3} rows)")
+        del xbc3, dt3, ssm3, conv3, post3, y3
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ 48-layer decode stack
+    if not args.no_stack:
+        result["stack"] = bench_stack(args, torch, np, B, synth, NEMOTRON_H_8B, dev, bf, time_region)
 
     # ------------------------------------------------------------ CPU baseline (oracle)
     if not args.no_cpu_baseline:

@@ -46,6 +46,28 @@ def counter_stats(db: str):
                   key=lambda r: -r["avg"])
 
 
+def traffic(fetch_db: str, write_db: str, calib_kernel: str = "__amd_rocclr_copyBuffer",
+            calib_bytes: int = 1 << 30):
+    """Calibrated HBM bytes per dispatch from a FETCH_SIZE run and a WRITE_SIZE run.
+
+    Both counters are in KiB per dispatch. Each is scaled by (known bytes / counted
+    bytes) of the largest dispatch of a plain copy kernel in the same run, which
+    read and wrote `calib_bytes`. Returns ({kernel: {"fetch": B, "write": B}},
+    {"fetch_factor": f, "write_factor": w})."""
+    out, factors = {}, {}
+    for db, ctr, key in ((fetch_db, "FETCH_SIZE", "fetch"), (write_db, "WRITE_SIZE", "write")):
+        rows = [r for r in counter_stats(db) if r["counter"] == ctr]
+        con = sqlite3.connect(db)
+        calib = con.execute("select max(value) from counters_collection where kernel_name = ? and counter_name = ?",
+                            (calib_kernel, ctr)).fetchone()[0]
+        factor = calib_bytes / (calib * 1024.0) if calib else None
+        factors[key + "_factor"] = factor
+        for r in rows:
+            if factor:
+                out.setdefault(r["name"], {})[key] = r["avg"] * 1024.0 * factor
+    return out, factors
+
+
 def render(db: str, title: str = "", cmd: str = "") -> str:
     lines = [f"# {title or 'rocprofv3 summary'}", ""]
     if cmd:
@@ -71,7 +93,14 @@ def main():
     ap.add_argument("db")
     ap.add_argument("--title", default="")
     ap.add_argument("--cmd", default="")
+    ap.add_argument("--write-db", default="", help="with a FETCH_SIZE db as DB: print calibrated traffic")
     a = ap.parse_args()
+    if a.write_db:
+        t, f = traffic(a.db, a.write_db)
+        print(f"calibration: {f}")
+        for k, v in sorted(t.items(), key=lambda kv: -sum(kv[1].values())):
+            print(f"{_short(k)}: fetch {v.get('fetch', 0) / 1e6:.1f} MB, write {v.get('write', 0) / 1e6:.1f} MB")
+        return
     print(render(a.db, a.title, a.cmd))
 
 
