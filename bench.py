@@ -4,8 +4,9 @@
 Primary line (the metric's decode half): decode tokens/s of one layer step
 (conv1d_update + state_update) for 256 sequences drawn from a 512-slot bf16
 state pool (128 heads x headdim 64 x d_state 128, 8 groups). The prefill half
-(conv1d_fwd + chunk_scan_fwd over 4 x 8192 tokens, chunk 128, bf16 inputs,
-fp32 state) is reported in the same JSON line under "prefill".
+(mamba2_prefill_fwd over 4 x 8192 tokens, chunk 128, bf16 inputs, fp32 state;
+the unfused conv1d_fwd + chunk_scan_fwd pair alongside) is reported in the
+same JSON line under "prefill".
 
 Inputs are seeded synthetic tensors already resident in HBM when timing
 starts. Per-kernel durations come from HIP events on the stream the kernels
@@ -283,44 +284,68 @@ def main():
         host_pre = {"xbc": w2["xbc"][:8192].copy(), "dt_raw": w2["dt_raw"][:8192].copy(), "params": w2["params"]}
         del w2
 
+        ws2 = B.prefill_workspace(d2, T)
+
         def conv_fwd():
             B.mamba2_conv1d_fwd(d2, xbc2, cw2, None, post2, convp2, cu2, idx2, hi2)
 
         def scan():
             B.mamba2_chunk_scan_fwd(d2, post2, dt2, A2, dtb2, D2, None, y2, pool2, cu2, idx2, hi2)
 
-        def prefill_step():
+        def unfused_step():
             conv_fwd()
             scan()
 
+        def prefill_step():  # conv of B/C to operand planes, fused conv(x) + scan, conv cache update
+            B.mamba2_prefill_fwd(d2, xbc2, dt2, None, cw2, None, A2, dtb2, D2, y2, pool2, convp2, cu2, idx2, hi2,
+                                 ws2)
+
         for _ in range(2):
             prefill_step()
+            unfused_step()
         torch.cuda.synchronize()
         log(f"timing {args.prefill_steps} prefill steps")
         ms_pre = time_region(prefill_step, args.prefill_steps, torch)
+        ms_unf = time_region(unfused_step, args.prefill_steps, torch)
         ms_scan = time_region(scan, args.prefill_steps, torch)
         ms_cf = time_region(conv_fwd, args.prefill_steps, torch)
+        # algorithmic minimum of the whole prefill: raw bf16 xBC + dt in, bf16 y out, final fp32 states
+        pb, pf = scan_algorithmic(d2, T, 4, 2, 2, 4)
+        pre_gbs = pb / (ms_pre * 1e-3) / 1e9
+        pre_tfs = pf / (ms_pre * 1e-3) / 1e12
         sb, sf = scan_algorithmic(d2, T, 4, 4, 2, 4)
         scan_gbs = sb / (ms_scan * 1e-3) / 1e9
         scan_tfs = sf / (ms_scan * 1e-3) / 1e12
         pre_tok_s = T / (ms_pre * 1e-3)
-        log(f"prefill: {ms_pre * 1e3:.1f} us/step ({pre_tok_s / 1e6:.2f} M tok/s); chunk_scan {ms_scan * 1e3:.1f} us "
-            f"({scan_gbs:.0f} GB/s, {scan_tfs:.1f} TFLOP/s); conv1d_fwd {ms_cf * 1e3:.1f} us")
+        log(f"prefill (fused): {ms_pre * 1e3:.1f} us/step ({pre_tok_s / 1e6:.2f} M tok/s, {pre_gbs:.0f} GB/s, "
+            f"{pre_tfs:.1f} TFLOP/s); unfused {ms_unf * 1e3:.1f} us = conv1d_fwd {ms_cf * 1e3:.1f} + chunk_scan "
+            f"{ms_scan * 1e3:.1f}")
         result["prefill"] = {
             "value": round(pre_tok_s, 1), "unit": "tok/s", "ms_per_step": round(ms_pre, 4),
             "steps": args.prefill_steps,
             "workload": "Nemotron-H-8B layer prefill: 4 x 8192 tokens (cu_seqlens), chunk 128, bf16 inputs, "
-                        "fp32 post-conv xBC, fp32 state, bf16 y, zero initial state, final states to pool slots; "
-                        "step = conv1d_fwd + chunk_scan_fwd",
-            "chunk_scan_us": round(ms_scan * 1e3, 2), "conv1d_fwd_us": round(ms_cf * 1e3, 2),
-            "roofline": {"bound": "mfma", "kernel": "chunk_scan_kernel", "achieved": round(scan_tfs, 2),
-                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(scan_tfs / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": profiled_traffic("chunk_scan_fast_kernel"),
-                         "algorithmic_flops_per_launch": sf, "algorithmic_bytes_per_launch": sb,
-                         "hbm_achieved_gbs": round(scan_gbs, 1), "hbm_frac": round(scan_gbs / HBM_PEAK_GBS, 4)},
+                        "fp32 state, bf16 y, zero initial state, final conv/SSM states to pool slots; "
+                        "step = mamba2_prefill_fwd (B/C conv pass + fused conv/scan kernel + conv cache update)",
+            "roofline": {"bound": "hbm", "kernel": "mamba2_prefill_fwd (whole call)", "achieved": round(pre_gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(pre_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": profiled_traffic("prefill_scan_kernel"),
+                         "algorithmic_bytes_per_launch": pb, "algorithmic_flops_per_launch": pf,
+                         "mfma_achieved_tflops": round(pre_tfs, 2),
+                         "mfma_frac": round(pre_tfs / MFMA_BF16_PEAK_TFLOPS, 4)},
+            "unfused": {
+                "ms_per_step": round(ms_unf, 4), "tok_s": round(T / (ms_unf * 1e-3), 1),
+                "step": "conv1d_fwd (fp32 post-conv xBC) + chunk_scan_fwd",
+                "chunk_scan_us": round(ms_scan * 1e3, 2), "conv1d_fwd_us": round(ms_cf * 1e3, 2),
+                "chunk_scan_roofline": {"bound": "mfma", "kernel": "chunk_scan_fast_kernel",
+                                        "achieved": round(scan_tfs, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                                        "unit": "TFLOP/s", "frac": round(scan_tfs / MFMA_BF16_PEAK_TFLOPS, 4),
+                                        "traffic": profiled_traffic("chunk_scan_fast_kernel"),
+                                        "algorithmic_flops_per_launch": sf, "algorithmic_bytes_per_launch": sb,
+                                        "hbm_achieved_gbs": round(scan_gbs, 1),
+                                        "hbm_frac": round(scan_gbs / HBM_PEAK_GBS, 4)},
+            },
         }
-        del xbc2, dt2, pool2, convp2, post2, y2
+        del xbc2, dt2, pool2, convp2, post2, y2, ws2
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ mixed prefill + decode batch

@@ -176,6 +176,45 @@ int mamba2_mixed_fwd(const mamba2_dims *dims, const void *xbc, const void *dt_ra
                      int32_t decode_batch, void *workspace, size_t workspace_bytes,
                      void *stream);
 
+/* Workspace that mamba2_prefill_fwd needs for `total_tokens` packed tokens.
+ * For the fused shape (headdim 64, dstate 128, chunk 64|128, out_dtype bf16)
+ * it holds the post-conv B/C operand planes, 3*G*N bf16 per token; otherwise
+ * the post-conv xBC, Cdim elements of xbc_dtype per token. */
+int mamba2_prefill_workspace_bytes(const mamba2_dims *dims, int64_t total_tokens, size_t *bytes);
+
+/* Whole prefill of the mixer's SSM core over packed sequences: conv1d + SiLU,
+ * chunked SSD scan, optional gate and optional gated RMSNorm ([record]: mixer
+ * tensors conv1d, A_log, D, dt_bias, norm; "REQUIRED KERNEL CLASS").
+ * Same results as mamba2_conv1d_fwd followed by mamba2_chunk_scan_fwd (and
+ * mamba2_gated_rmsnorm when norm_w is given), but for the fused shape the x
+ * channels are convolved inside the scan and never stored: only the B/C
+ * channels pass through the workspace, once per group rather than per head.
+ *   xbc [total_tokens][Cdim] act_dtype, raw (pre-conv); dt_raw, z as for
+ *   chunk_scan_fwd; y [total_tokens][H*P] out_dtype.
+ *   norm_w [H*P] fp32 or NULL (no norm): y = norm_w * g / rms_group(g) with
+ *   g = y_ssm * SiLU(z) (g = y_ssm when z is NULL), groups of norm_group
+ *   consecutive channels (0 = H*P/G), rms over the group plus norm_eps.
+ *   conv_pool / ssm_pool: read at state_indices[i] when has_initial_state[i]
+ *   is 1, then overwritten with the sequence's final conv and SSM state.
+ *   workspace: device memory of at least mamba2_prefill_workspace_bytes
+ *   (MAMBA2_ERR_WORKSPACE otherwise); its contents are scratch. */
+int mamba2_prefill_fwd(const mamba2_dims *dims, const void *xbc, const void *dt_raw, const void *z,
+                       const float *conv_w, const float *conv_b, const float *A_log,
+                       const float *dt_bias, const float *D, const float *norm_w, float norm_eps,
+                       int32_t norm_group, void *y, void *ssm_pool, void *conv_pool,
+                       const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens,
+                       const int32_t *state_indices, const uint8_t *has_initial_state,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Gated RMSNorm of mixer outputs ([record], the mixer's "norm" tensor):
+ * out = norm_w * g / sqrt(mean_group(g^2) + eps), g = y * SiLU(z) (g = y when z
+ * is NULL), over groups of group_size consecutive channels (0 = H*P/G).
+ *   y, out [rows][H*P] out_dtype (out may equal y); z [rows][H*P] act_dtype or
+ *   NULL; norm_w [H*P] fp32. group_size must divide H*P, be a multiple of 4
+ *   and at most 4096 (MAMBA2_ERR_UNSUPPORTED otherwise). */
+int mamba2_gated_rmsnorm(const mamba2_dims *dims, const void *y, const void *z, const float *norm_w,
+                         float eps, int32_t group_size, void *out, int64_t rows, void *stream);
+
 /* Fixed-size recurrent-state slot allocator ([record], "REQUIRED KERNEL
  * CLASS": a fixed-size recurrent state allocator; "Recurrent state": the
  * cost scales with concurrency, not context). Host-only: it hands out slot

@@ -13,7 +13,9 @@ Sources of what it computes (see ``ssm_oracle.c`` for the step list):
   * the per-head tensors A_log, D, dt_bias and the n_groups=8 grouping: the
     "Nemotron-H-8B-Base-8K" record (mixer tensors, "Recurrent state");
   * the equivalence contract (a T-token chunk scan equals T single steps):
-    the vllm.cpp issue, section "Confirm or refute".
+    the vllm.cpp issue, section "Confirm or refute";
+  * the gated RMSNorm of the mixer output (``norm.py``): the record's "norm"
+    mixer tensor.
 
 Every function here loops over sequences and tokens in order and calls the C
 routines, which hold the arithmetic. ``dual`` (the quadratic matrix form) is a
@@ -195,3 +197,4 @@ def decode(xbc_raw, dt_raw, params, state_indices, conv_pool, ssm_pool, *, H, P,
 
 
 from . import dual  # noqa: E402,F401  (independent quadratic form)
+from .norm import gated_rmsnorm  # noqa: E402,F401  (the mixer's gated RMSNorm)

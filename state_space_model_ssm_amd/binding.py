@@ -67,6 +67,13 @@ _SIGS = {
     "mamba2_mixed_fwd": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                         _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P, ctypes.c_int32, _P,
                                         ctypes.c_size_t, _P]),
+    "mamba2_prefill_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(CDims), ctypes.c_int64,
+                                                       ctypes.POINTER(ctypes.c_size_t)]),
+    "mamba2_prefill_fwd": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                          ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P,
+                                          ctypes.c_size_t, _P]),
+    "mamba2_gated_rmsnorm": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, ctypes.c_float, ctypes.c_int32, _P,
+                                            ctypes.c_int64, _P]),
     "mamba2_slots_create": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(_P)]),
     "mamba2_slot_alloc": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32)]),
     "mamba2_slot_free": (ctypes.c_int, [_P, ctypes.c_int32]),
@@ -238,6 +245,61 @@ def mamba2_state_update(d: Dims, xbc, dt_raw, A_log, dt_bias, D, z, y, ssm_pool,
     _check(lib().mamba2_state_update(ctypes.byref(c), _ptr(xbc), _ptr(dt_raw), _ptr(A_log), _ptr(dt_bias), _ptr(D),
                                      _ptr(z), _ptr(y), _ptr(ssm_pool), _ptr(state_indices), Bd, _stream(stream)),
            "mamba2_state_update")
+
+
+def mamba2_prefill_workspace_bytes(d: Dims, total_tokens: int, *, xbc_dtype=None) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().mamba2_prefill_workspace_bytes(ctypes.byref(cdims(d, xbc_dtype)), total_tokens, ctypes.byref(out)),
+           "mamba2_prefill_workspace_bytes")
+    return int(out.value)
+
+
+def prefill_workspace(d: Dims, total_tokens: int, *, xbc_dtype=None, device="cuda") -> torch.Tensor:
+    """A device byte buffer of the size mamba2_prefill_fwd needs (allocate once, reuse)."""
+    n = mamba2_prefill_workspace_bytes(d, total_tokens, xbc_dtype=xbc_dtype)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def mamba2_prefill_fwd(d: Dims, xbc, dt_raw, z, conv_w, conv_b, A_log, dt_bias, D, y, ssm_pool, conv_pool,
+                       cu_seqlens, state_indices, has_initial_state=None, workspace=None, norm_w=None,
+                       norm_eps: float = 1e-5, norm_group: int = 0, *, xbc_dtype=None, stream=None):
+    T = xbc.shape[0]
+    nseq = state_indices.shape[0]
+    H = d.nheads
+    _want(xbc, "xbc", _TORCH_DT[d.act_dtype], (T, d.conv_dim))
+    _want(dt_raw, "dt_raw", _TORCH_DT[d.act_dtype], (T, H))
+    _want(z, "z", _TORCH_DT[d.act_dtype], (T, d.d_inner), optional=True)
+    _want(conv_w, "conv_w", torch.float32, (d.conv_dim, d.conv_width))
+    _want(conv_b, "conv_b", torch.float32, (d.conv_dim,), optional=True)
+    for n, t in (("A_log", A_log), ("dt_bias", dt_bias), ("D", D)):
+        _want(t, n, torch.float32, (H,))
+    _want(norm_w, "norm_w", torch.float32, (d.d_inner,), optional=True)
+    _want(y, "y", _TORCH_DT[d.out_dtype], (T, d.d_inner))
+    _want(ssm_pool, "ssm_pool", _TORCH_DT[d.state_dtype])
+    if ssm_pool.dim() != 4 or tuple(ssm_pool.shape[1:]) != (H, d.headdim, d.dstate):
+        raise ValueError("ssm_pool must be [slots, H, P, N]")
+    _want(conv_pool, "conv_pool", _TORCH_DT[d.state_dtype])
+    _want(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,))
+    _want(state_indices, "state_indices", torch.int32, (nseq,))
+    _want(has_initial_state, "has_initial_state", torch.uint8, (nseq,), optional=True)
+    _want(workspace, "workspace", optional=True)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = cdims(d, xbc_dtype)
+    _check(lib().mamba2_prefill_fwd(ctypes.byref(c), _ptr(xbc), _ptr(dt_raw), _ptr(z), _ptr(conv_w), _ptr(conv_b),
+                                    _ptr(A_log), _ptr(dt_bias), _ptr(D), _ptr(norm_w), float(norm_eps),
+                                    int(norm_group), _ptr(y), _ptr(ssm_pool), _ptr(conv_pool), _ptr(cu_seqlens),
+                                    nseq, T, _ptr(state_indices), _ptr(has_initial_state), _ptr(workspace), ws_bytes,
+                                    _stream(stream)), "mamba2_prefill_fwd")
+
+
+def mamba2_gated_rmsnorm(d: Dims, y, z, norm_w, out, eps: float = 1e-5, group_size: int = 0, *, stream=None):
+    rows = y.shape[0]
+    _want(y, "y", _TORCH_DT[d.out_dtype], (rows, d.d_inner))
+    _want(z, "z", _TORCH_DT[d.act_dtype], (rows, d.d_inner), optional=True)
+    _want(norm_w, "norm_w", torch.float32, (d.d_inner,))
+    _want(out, "out", _TORCH_DT[d.out_dtype], (rows, d.d_inner))
+    _check(lib().mamba2_gated_rmsnorm(ctypes.byref(cdims(d)), _ptr(y), _ptr(z), _ptr(norm_w), float(eps),
+                                      int(group_size), _ptr(out), rows, _stream(stream)), "mamba2_gated_rmsnorm")
 
 
 def mamba2_mixed_fwd(d: Dims, xbc, dt_raw, z, conv_w, conv_b, A_log, dt_bias, D, xbc_post, y, ssm_pool, conv_pool,

@@ -235,6 +235,117 @@ int mamba2_mixed_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw, 
     return ok();
 }
 
+// ------------------------------------------------------------ fused prefill + gated norm
+namespace {
+
+bool fused_path(const mamba2_dims *d) { return m2::prefill_fused_supported(shape_of(d)); }
+
+int norm_group_of(const mamba2_dims *d, int32_t group) {
+    return group > 0 ? group : (d->nheads * d->headdim) / d->ngroups;
+}
+
+int check_norm(const mamba2_dims *d, int32_t group) {
+    const int64_t width = (int64_t)d->nheads * d->headdim;
+    const int gs = norm_group_of(d, group);
+    if (group < 0) return fail(MAMBA2_ERR_INVALID_ARG, "norm group size must be >= 0 (0 = H*P/G)");
+    if (!m2::gated_norm_supported(width, gs))
+        return fail(MAMBA2_ERR_UNSUPPORTED, "gated norm needs a group size dividing H*P, a multiple of 4, <= 4096 (%d)",
+                    gs);
+    return MAMBA2_OK;
+}
+
+}  // namespace
+
+int mamba2_prefill_workspace_bytes(const mamba2_dims *d, int64_t total_tokens, size_t *bytes) {
+    int st = check_conv(d);
+    if (st) return st;
+    st = check_scan(d);
+    if (st) return st;
+    if (!bytes) return fail(MAMBA2_ERR_INVALID_ARG, "bytes is NULL");
+    if (total_tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative total_tokens");
+    const m2::LayerShape s = shape_of(d);
+    const size_t per_token = fused_path(d) ? (size_t)3 * s.G * s.N * 2 : (size_t)s.cdim() * dtype_bytes(d->xbc_dtype);
+    *bytes = per_token * (size_t)total_tokens;
+    return ok();
+}
+
+int mamba2_gated_rmsnorm(const mamba2_dims *d, const void *y, const void *z, const float *norm_w, float eps,
+                         int32_t group_size, void *out, int64_t rows, void *stream) {
+    int st = check_dims_basic(d);
+    if (st) return st;
+    st = check_norm(d, group_size);
+    if (st) return st;
+    if (rows < 0) return fail(MAMBA2_ERR_INVALID_ARG, "rows < 0");
+    if (!(eps >= 0.0f)) return fail(MAMBA2_ERR_INVALID_ARG, "eps must be >= 0");
+    if (rows == 0) return ok();
+    REQUIRE_PTR(y); OPT_PTR(z); REQUIRE_PTR(norm_w); REQUIRE_PTR(out);
+    if (z && z == out) return fail(MAMBA2_ERR_INVALID_ARG, "out must not alias z");
+    m2::NormArgs a{y, z, norm_w, out, eps, rows};
+    return hip_status(m2::launch_gated_norm(a, d->out_dtype, d->act_dtype, (int64_t)d->nheads * d->headdim,
+                                            norm_group_of(d, group_size), static_cast<hipStream_t>(stream)),
+                      "gated_rmsnorm launch");
+}
+
+int mamba2_prefill_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw, const void *z, const float *conv_w,
+                       const float *conv_b, const float *A_log, const float *dt_bias, const float *D,
+                       const float *norm_w, float norm_eps, int32_t norm_group, void *y, void *ssm_pool,
+                       void *conv_pool, const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens,
+                       const int32_t *state_indices, const uint8_t *has_initial_state, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    int st = check_conv(d);
+    if (st) return st;
+    st = check_scan(d);
+    if (st) return st;
+    if (norm_w) {
+        st = check_norm(d, norm_group);
+        if (st) return st;
+        if (!(norm_eps >= 0.0f)) return fail(MAMBA2_ERR_INVALID_ARG, "norm_eps must be >= 0");
+    }
+    if (nseq < 0 || total_tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative nseq or total_tokens");
+    if (nseq == 0) {
+        if (total_tokens != 0) return fail(MAMBA2_ERR_INVALID_ARG, "tokens without sequences");
+        return ok();
+    }
+    size_t need = 0;
+    st = mamba2_prefill_workspace_bytes(d, total_tokens, &need);
+    if (st) return st;
+    if (workspace_bytes < need)
+        return fail(MAMBA2_ERR_WORKSPACE, "prefill needs %zu workspace bytes, got %zu", need, workspace_bytes);
+    REQUIRE_PTR(conv_w); OPT_PTR(conv_b); REQUIRE_PTR(A_log); REQUIRE_PTR(dt_bias); REQUIRE_PTR(D);
+    REQUIRE_PTR(ssm_pool); REQUIRE_PTR(conv_pool); REQUIRE_IDX(cu_seqlens); REQUIRE_IDX(state_indices);
+    if (total_tokens > 0) {
+        REQUIRE_PTR(xbc); REQUIRE_PTR(dt_raw); REQUIRE_PTR(y); OPT_PTR(z); REQUIRE_PTR(workspace);
+        if (xbc == y || workspace == xbc || workspace == y)
+            return fail(MAMBA2_ERR_INVALID_ARG, "xbc, y and workspace must not alias");
+    }
+    hipStream_t strm = static_cast<hipStream_t>(stream);
+    const m2::LayerShape s = shape_of(d);
+    // with a norm, the gate is applied by the norm pass (the scan writes ungated y)
+    const void *scan_z = norm_w ? nullptr : z;
+    m2::ConvFwdArgs ca{xbc, conv_w, conv_b, workspace, conv_pool, cu_seqlens, state_indices, has_initial_state, nseq,
+                       total_tokens};
+    if (fused_path(d)) {
+        st = hip_status(m2::launch_bc_planes(s, ca, strm), "prefill B/C conv launch");
+        if (st) return st;
+        m2::PrefillArgs pa{xbc, workspace, conv_w, conv_b, conv_pool, dt_raw, A_log, dt_bias, D, scan_z, y,
+                           ssm_pool, cu_seqlens, state_indices, has_initial_state, nseq, total_tokens};
+        st = hip_status(m2::launch_prefill_scan(s, pa, strm), "prefill scan launch");
+        if (st) return st;
+        st = hip_status(m2::launch_conv_state(s, ca, strm), "prefill conv state launch");
+        if (st) return st;
+    } else {
+        st = mamba2_conv1d_fwd(d, xbc, conv_w, conv_b, workspace, conv_pool, cu_seqlens, nseq, total_tokens,
+                               state_indices, has_initial_state, stream);
+        if (st) return st;
+        st = mamba2_chunk_scan_fwd(d, workspace, dt_raw, A_log, dt_bias, D, scan_z, y, ssm_pool, cu_seqlens, nseq,
+                                   total_tokens, state_indices, has_initial_state, nullptr, 0, stream);
+        if (st) return st;
+    }
+    if (norm_w && total_tokens > 0)
+        return mamba2_gated_rmsnorm(d, y, z, norm_w, norm_eps, norm_group, y, total_tokens, stream);
+    return ok();
+}
+
 // ------------------------------------------------------------ slot allocator
 struct mamba2_slots {
     std::vector<int32_t> free_list;  // stack of free slot ids

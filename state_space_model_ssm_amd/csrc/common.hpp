@@ -90,6 +90,34 @@ template <typename T, int K> __device__ __forceinline__ void store_k(T *p, const
     }
 }
 
+// K elements of T held as their raw bits after one vector load and widened to
+// float only where used: converting right at the load would make the compiler
+// wait for that load (and, loads completing in order, for every earlier one).
+template <typename T, int K> struct Raw {
+    static_assert((K * sizeof(T)) % 8 == 0, "Raw: 8-byte multiple");
+    static constexpr int kW = (int)(K * sizeof(T) / 4);
+    uint32_t w[kW];
+    __device__ __forceinline__ void load(const T *p) {
+        if constexpr (kW % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < kW / 4; ++i) {
+                const uint4 v = reinterpret_cast<const uint4 *>(p)[i];
+                w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kW / 2; ++i) {
+                const uint2 v = reinterpret_cast<const uint2 *>(p)[i];
+                w[2 * i] = v.x; w[2 * i + 1] = v.y;
+            }
+        }
+    }
+    __device__ __forceinline__ float operator[](int i) const {
+        if constexpr (sizeof(T) == 4) return __uint_as_float(w[i]);
+        else return __uint_as_float((i & 1) ? (w[i >> 1] & 0xffff0000u) : (w[i >> 1] << 16));
+    }
+};
+
 // 16-byte streaming (nontemporal) access: data touched once per launch should
 // not displace reusable lines from L2 / the memory-side cache.
 template <typename T> __device__ __forceinline__ void nt_load16(const T *p, float *out) {

@@ -56,6 +56,31 @@ struct ScanArgs {
     int64_t T;
 };
 
+struct PrefillArgs {
+    const void *xbc;      // [T][Cdim] raw (pre-conv), activation dtype
+    const void *bc;       // [T][3*G*N] bf16 planes B hi | B lo | C (post-conv), from launch_bc_planes
+    const float *conv_w, *conv_b;  // [Cdim][W], [Cdim] or null
+    const void *conv_pool;  // [slots][W-1][Cdim], read for the context before each sequence
+    const void *dt_raw;   // [T][H]
+    const float *A_log, *dt_bias, *D;
+    const void *z;        // [T][H*P] or null
+    void *y;              // [T][H*P] bf16
+    void *pool;           // [slots][H][P][N]
+    const int32_t *cu, *idx;
+    const uint8_t *has_init;
+    int nseq;
+    int64_t T;
+};
+
+struct NormArgs {
+    const void *y;        // [rows][width]
+    const void *z;        // [rows][width] or null
+    const float *w;       // [width]
+    void *out;            // [rows][width] (may equal y)
+    float eps;
+    int64_t rows;
+};
+
 // Each returns hipSuccess or the launch error. `supported` queries return
 // false for shapes outside the compiled set (no launch happens).
 bool state_update_supported(const LayerShape &s);
@@ -64,6 +89,16 @@ hipError_t launch_state_update(const LayerShape &s, const StateUpdateArgs &a, hi
 bool conv_supported(const LayerShape &s);
 hipError_t launch_conv_update(const LayerShape &s, const ConvUpdateArgs &a, hipStream_t st);
 hipError_t launch_conv_fwd(const LayerShape &s, const ConvFwdArgs &a, hipStream_t st);
+// B/C channels only, as bf16 planes [B hi | B lo | C] per token (a.out); no cache update
+hipError_t launch_bc_planes(const LayerShape &s, const ConvFwdArgs &a, hipStream_t st);
+// the conv cache update of launch_conv_fwd alone
+hipError_t launch_conv_state(const LayerShape &s, const ConvFwdArgs &a, hipStream_t st);
+
+bool prefill_fused_supported(const LayerShape &s);
+hipError_t launch_prefill_scan(const LayerShape &s, const PrefillArgs &a, hipStream_t st);
+
+bool gated_norm_supported(int64_t width, int gs);
+hipError_t launch_gated_norm(const NormArgs &a, int y_dt, int z_dt, int64_t width, int gs, hipStream_t st);
 
 bool scan_supported(const LayerShape &s);
 hipError_t launch_chunk_scan(const LayerShape &s, const ScanArgs &a, hipStream_t st);

@@ -64,6 +64,14 @@ def layer_params(dims: Dims, rng) -> dict:
     return {"conv_w": conv_w, "conv_b": None, "A_log": A_log, "dt_bias": dt_bias, "D": D}
 
 
+def norm_weight(dims: Dims, seed: int) -> np.ndarray:
+    """Gated-RMSNorm weight [H*P], fp32: 1 + N(0, 0.1^2), from a stream of its own
+    (SeedSequence(seed) spawned child 1) so the other seeded inputs are unchanged."""
+    ss = np.random.SeedSequence(seed).spawn(2)[1]
+    rng = np.random.Generator(np.random.PCG64(ss))
+    return (1.0 + _normal(rng, (dims.d_inner,), std=0.1)).astype(np.float32)
+
+
 def xbc_values(dims: Dims, rng, rows: int) -> np.ndarray:
     """Raw xBC rows [rows, Cdim]: x ~ N(0,1), B and C ~ N(0,1)/sqrt(d_state)."""
     v = _normal(rng, (rows, dims.conv_dim))

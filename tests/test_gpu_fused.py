@@ -1,0 +1,196 @@
+"""GPU parity of the whole-prefill entry point (mamba2_prefill_fwd: conv1d + chunk scan, fused
+for the Nemotron-H head shape with bf16 y, composed otherwise) and of the gated RMSNorm,
+against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _helpers import (assert_close, compact_pools, dev, dev_i32, dev_u8, host, oracle_head_seq, oracle_kw,
+                      params_dev)
+from state_space_model_ssm_amd import binding as B
+from state_space_model_ssm_amd import synth
+from state_space_model_ssm_amd.configs import BF16, F32, NEMOTRON_H_8B, TINY
+
+pytestmark = pytest.mark.gpu
+
+# Nemotron-H-8B head shape (P=64, N=128) with 16 heads / 2 groups; bf16 y selects the fused kernel.
+D16B = NEMOTRON_H_8B.with_(nheads=16, ngroups=2, chunk_size=64, state_dtype=F32, out_dtype=BF16)
+
+
+def run_fused(d, w, has_init=None, slots=None, norm_w=None, eps=1e-5, group=0, use_z=True):
+    pd = params_dev(w["params"])
+    T = w["xbc"].shape[0]
+    slots = w["slots"] if slots is None else slots
+    has_init = w["has_initial_state"] if has_init is None else has_init
+    ssm = dev(w["ssm_pool"], d.state_dtype)
+    conv = dev(w["conv_pool"], d.state_dtype)
+    xbc, dt = dev(w["xbc"], d.act_dtype), dev(w["dt_raw"], d.act_dtype)
+    z = dev(w["z"], d.act_dtype) if (use_z and w["z"] is not None) else None
+    y = torch.empty(T, d.d_inner, dtype=B._TORCH_DT[d.out_dtype], device="cuda")
+    ws = B.prefill_workspace(d, T)
+    nw = None if norm_w is None else dev(norm_w, F32)
+    B.mamba2_prefill_fwd(d, xbc, dt, z, pd["conv_w"], pd["conv_b"], pd["A_log"], pd["dt_bias"], pd["D"], y, ssm,
+                         conv, dev_i32(w["cu_seqlens"]), dev_i32(slots), dev_u8(has_init), ws, nw, eps, group)
+    torch.cuda.synchronize()
+    return y, ssm, conv
+
+
+def oracle_fused(d, w, has_init=None, slots=None, norm_w=None, eps=1e-5, group=0, use_z=True):
+    slots = w["slots"] if slots is None else slots
+    has_init = w["has_initial_state"] if has_init is None else has_init
+    used = [s for s in slots if s >= 0]
+    cp, sp = compact_pools(w, used)
+    pos = {int(s): i for i, s in enumerate(used)}
+    cidx = np.array([pos[int(s)] if s >= 0 else -1 for s in slots])
+    z = w["z"] if use_z else None
+    # with a norm the gate belongs to the norm: g = y * SiLU(z)
+    y, _ = oracle.prefill(w["xbc"], w["dt_raw"], w["params"], w["cu_seqlens"], cidx, has_init, cp, sp,
+                          z=None if norm_w is not None else z, **oracle_kw(d))
+    if norm_w is not None:
+        gs = group if group > 0 else d.d_inner // d.ngroups
+        y = oracle.gated_rmsnorm(y, z, norm_w, eps, gs)
+        cu = w["cu_seqlens"]
+        for i, s in enumerate(slots):  # padding sequences keep y = 0 (the norm of 0 is 0)
+            if s < 0:
+                y[int(cu[i]):int(cu[i + 1])] = 0.0
+    return y, cp, sp, used
+
+
+def check_fused(d, w, **kw):
+    y, ssm, conv = run_fused(d, w, **kw)
+    y_ref, cp, sp, used = oracle_fused(d, w, **kw)
+    e_y = assert_close(host(y), y_ref, d.out_dtype, "y")
+    u = torch.tensor(used, dtype=torch.long, device="cuda")
+    e_h = assert_close(host(ssm[u]), sp, d.state_dtype, "final ssm state")
+    assert np.array_equal(host(conv[u]), cp), "conv cache must hold the exact raw inputs"
+    print(f"  y err {e_y:.2e}  state err {e_h:.2e}", flush=True)
+    return y, ssm, conv
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("state_dtype", [F32, BF16])
+@pytest.mark.parametrize("use_z", [False, True])
+def test_fused_prefill_matches_oracle(chunk, state_dtype, use_z):
+    """Ragged varlen batch (lengths 1, 37, 130, 200), half of the sequences resuming from
+    saved conv and SSM state, so the conv context of a sequence comes from its slot."""
+    d = D16B.with_(chunk_size=chunk, state_dtype=state_dtype)
+    print(f"[fused prefill] chunk={chunk} state={state_dtype} z={use_z}", flush=True)
+    w = synth.prefill_batch(d, seed=21, seqlens=[1, 37, 130, 200], num_slots=9, initial_state=True)
+    check_fused(d, w, has_init=np.array([1, 0, 1, 0], np.uint8), use_z=use_z)
+
+
+@pytest.mark.parametrize("group", [0, 64])
+def test_fused_prefill_with_gated_norm(group):
+    d = D16B
+    print(f"[fused prefill + gated norm] group={group}", flush=True)
+    w = synth.prefill_batch(d, seed=22, seqlens=[70, 129], num_slots=4, initial_state=True)
+    check_fused(d, w, has_init=np.array([1, 0], np.uint8), norm_w=synth.norm_weight(d, 22), eps=1e-5, group=group)
+
+
+@pytest.mark.parametrize("dims", [D16B.with_(out_dtype=F32), TINY], ids=["p64n128-f32y", "tiny"])
+def test_prefill_fwd_composed_path_with_norm(dims):
+    """Shapes outside the fused kernel (fp32 y, small heads) run conv1d_fwd + chunk_scan_fwd
+    through the workspace, then the norm."""
+    print(f"[composed prefill] {dims}", flush=True)
+    w = synth.prefill_batch(dims, seed=23, seqlens=[5, 40, 17], num_slots=5, initial_state=True)
+    check_fused(dims, w, has_init=np.array([0, 1, 1], np.uint8), norm_w=synth.norm_weight(dims, 23), eps=1e-5)
+
+
+@pytest.mark.parametrize("out_dtype", [F32, BF16])
+def test_gated_rmsnorm_standalone(out_dtype):
+    d = D16B.with_(out_dtype=out_dtype)
+    rng = np.random.default_rng(24)
+    rows = 37
+    yv = synth.round_to_dtype(rng.standard_normal((rows, d.d_inner)).astype(np.float32), out_dtype)
+    zv = synth.round_to_dtype(rng.standard_normal((rows, d.d_inner)).astype(np.float32), d.act_dtype)
+    nw = synth.norm_weight(d, 24)
+    y, z = dev(yv, out_dtype), dev(zv, d.act_dtype)
+    for group, gate in ((0, True), (256, False), (1024, True)):
+        out = torch.empty_like(y)
+        B.mamba2_gated_rmsnorm(d, y, z if gate else None, dev(nw, F32), out, 1e-5, group)
+        torch.cuda.synchronize()
+        ref = oracle.gated_rmsnorm(yv, zv if gate else None, nw, 1e-5, group or d.d_inner // d.ngroups)
+        assert_close(host(out), ref, out_dtype, f"norm group={group} gate={gate}")
+    # in place
+    ref = oracle.gated_rmsnorm(yv, zv, nw, 1e-5, 512)
+    B.mamba2_gated_rmsnorm(d, y, z, dev(nw, F32), y, 1e-5, 0)
+    torch.cuda.synchronize()
+    assert_close(host(y), ref, out_dtype, "norm in place")
+
+
+def test_fused_packed_equals_separate_runs_bitwise():
+    d = D16B
+    w = synth.prefill_batch(d, seed=25, seqlens=[70, 3, 129], num_slots=3, initial_state=False)
+    y_all, ssm_all, conv_all = run_fused(d, w)
+    cu = w["cu_seqlens"]
+    for i in range(3):
+        s, e = int(cu[i]), int(cu[i + 1])
+        wi = {**w, "xbc": w["xbc"][s:e], "dt_raw": w["dt_raw"][s:e], "z": w["z"][s:e],
+              "cu_seqlens": np.array([0, e - s], np.int32), "slots": w["slots"][i:i + 1],
+              "has_initial_state": w["has_initial_state"][i:i + 1]}
+        yi, ssmi, convi = run_fused(d, wi)
+        assert torch.equal(yi, y_all[s:e])
+        sl = int(w["slots"][i])
+        assert torch.equal(ssmi[sl], ssm_all[sl]) and torch.equal(convi[sl], conv_all[sl])
+
+
+def test_fused_padding_and_empty_sequences():
+    d = D16B
+    w = synth.prefill_batch(d, seed=26, seqlens=[40, 0, 33, 0, 2], num_slots=7, initial_state=True)
+    slots = w["slots"].copy()
+    slots[2] = -1
+    has_init = np.array([1, 1, 0, 0, 1], np.uint8)
+    y, ssm, conv = run_fused(d, w, has_init=has_init, slots=slots)
+    cu = w["cu_seqlens"]
+    assert torch.all(y[int(cu[2]):int(cu[3])] == 0).item()
+    pad = int(w["slots"][2])
+    assert np.array_equal(host(ssm[pad]), w["ssm_pool"][pad].astype(np.float64))
+    assert np.array_equal(host(conv[pad]), w["conv_pool"][pad].astype(np.float64))
+    assert np.array_equal(host(ssm[int(slots[1])]), w["ssm_pool"][slots[1]].astype(np.float64))
+    assert torch.all(ssm[int(slots[3])] == 0).item()
+    check_fused(d, w, has_init=has_init, slots=slots)
+
+
+def test_fused_prefill_equals_repeated_steps():
+    """Equivalence contract on the fused path: the prefill of T tokens equals T one-token
+    conv updates + state updates (bf16 y on both sides, fp32 state)."""
+    d = D16B
+    T = 150
+    w = synth.prefill_batch(d, seed=27, seqlens=[T], num_slots=1, initial_state=True)
+    hi = np.array([1], np.uint8)
+    y_scan, ssm_scan, conv_scan = run_fused(d, w, has_init=hi)
+    pd = params_dev(w["params"])
+    ssm, conv = dev(w["ssm_pool"], d.state_dtype), dev(w["conv_pool"], d.state_dtype)
+    idx = dev_i32(w["slots"])
+    xbc, dt, z = dev(w["xbc"], d.act_dtype), dev(w["dt_raw"], d.act_dtype), dev(w["z"], d.act_dtype)
+    ys = torch.empty(T, d.d_inner, dtype=torch.bfloat16, device="cuda")
+    post = torch.empty(1, d.conv_dim, dtype=B._TORCH_DT[d.post_dtype], device="cuda")
+    for t in range(T):
+        B.mamba2_conv1d_update(d, xbc[t:t + 1], pd["conv_w"], None, post, conv, idx)
+        B.mamba2_state_update(d, post, dt[t:t + 1], pd["A_log"], pd["dt_bias"], pd["D"], z[t:t + 1], ys[t:t + 1],
+                              ssm, idx)
+    torch.cuda.synchronize()
+    assert_close(host(y_scan), host(ys), BF16, "y: fused prefill vs steps")
+    assert_close(host(ssm_scan), host(ssm), F32, "state: fused prefill vs steps")
+    assert torch.equal(conv_scan, conv)
+
+
+def test_fused_full_size_sampled():
+    """The timed prefill workload (4 x 8192 tokens, 128 heads, chunk 128, bf16 inputs and y,
+    fp32 state) through mamba2_prefill_fwd in the benchmark's launch configuration, checked
+    on sampled (sequence, head) pairs, plus the whole conv cache."""
+    d = NEMOTRON_H_8B.with_(state_dtype=F32)
+    print("[fused prefill] full size 4x8192", flush=True)
+    w = synth.prefill_batch(d, seed=2, seqlens=[8192] * 4, num_slots=8, with_z=False)
+    y, ssm, conv = run_fused(d, w)
+    yh = y.float().cpu().numpy()
+    cu = w["cu_seqlens"]
+    for seq, head in [(0, 0), (1, 37), (2, 77), (3, 127), (0, 64), (3, 15)]:
+        s, e = int(cu[seq]), int(cu[seq + 1])
+        yr, hr = oracle_head_seq(d, w["params"], w["xbc"][s:e], w["dt_raw"][s:e], head)
+        assert_close(yh[s:e, head * 64:(head + 1) * 64], yr, BF16, f"y seq {seq} head {head}")
+        assert_close(host(ssm[int(w["slots"][seq]), head]), hr, F32, f"state seq {seq} head {head}")
+    for seq in range(4):
+        e = int(cu[seq + 1])
+        assert np.array_equal(host(conv[int(w["slots"][seq])]), w["xbc"][e - 3:e].astype(np.float64))

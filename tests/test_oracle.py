@@ -332,3 +332,69 @@ def test_bf16_state_emulation_rounds_every_step():
         h = np.vectorize(oracle.round_bf16)(h)
     _, hb = oracle.ssm_seq(xbc, dt_raw, A_log, dt_bias, D, h0, H=H, P=P, N=N, G=G, round_state_bf16=True)
     assert np.array_equal(h, hb)
+
+
+# ---------------------------------------------------------------- gated RMSNorm
+# The "norm" mixer tensor of the record page; the formula is this build's reading
+# (see oracle/norm.py). Pins: hand example, unit RMS per group, per-group scale
+# and sign behaviour, group independence, the two limits of the SiLU gate.
+
+def _norm_inputs(rows=3, width=64, seed=0):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((rows, width)), rng.standard_normal((rows, width))
+
+
+def test_norm_hand_example():
+    # group of 4: y = (3, 4, 0, 0) -> rms = sqrt(25/4) = 2.5 -> (1.2, 1.6, 0, 0)
+    y = np.array([[3.0, 4.0, 0.0, 0.0, 1.0, 1.0, 1.0, 1.0]])
+    out = oracle.gated_rmsnorm(y, None, np.ones(8), 0.0, 4)
+    assert np.allclose(out, [[1.2, 1.6, 0.0, 0.0, 1.0, 1.0, 1.0, 1.0]], rtol=0, atol=1e-15)
+
+
+def test_norm_unit_rms_per_group_and_group_independence():
+    y, z = _norm_inputs()
+    out = oracle.gated_rmsnorm(y, z, np.ones(64), 0.0, 16)
+    ms = (out.reshape(3, 4, 16) ** 2).mean(axis=2)
+    assert np.allclose(ms, 1.0, rtol=0, atol=1e-12)
+    y2 = y.copy()
+    y2[:, :16] *= 7.0
+    y2[:, 3] = -2.0
+    out2 = oracle.gated_rmsnorm(y2, z, np.ones(64), 0.0, 16)
+    assert np.array_equal(out2[:, 16:], out[:, 16:])
+
+
+def test_norm_scale_and_sign_per_group():
+    y, _ = _norm_inputs(seed=1)
+    base = oracle.gated_rmsnorm(y, None, np.ones(64), 0.0, 32)
+    c = np.repeat(np.array([[0.25, 3.0]]), 32, axis=1)
+    assert np.allclose(oracle.gated_rmsnorm(y * c, None, np.ones(64), 0.0, 32), base, rtol=0, atol=1e-12)
+    assert np.allclose(oracle.gated_rmsnorm(-y, None, np.ones(64), 0.0, 32), -base, rtol=0, atol=1e-15)
+
+
+def test_norm_weight_is_per_channel():
+    y, z = _norm_inputs(seed=2)
+    w = np.linspace(-2.0, 2.0, 64)
+    assert np.allclose(oracle.gated_rmsnorm(y, z, w, 1e-5, 16), w * oracle.gated_rmsnorm(y, z, np.ones(64), 1e-5, 16),
+                       rtol=0, atol=1e-14)
+
+
+def test_norm_gate_limits():
+    """SiLU(z) -> z for large z and -> 0 from below for very negative z: a gate of
+    +40 * s acts as the multiplier s, a gate of -40 flips the sign."""
+    y, _ = _norm_inputs(seed=3)
+    plain = oracle.gated_rmsnorm(y, None, np.ones(64), 0.0, 16)
+    s = np.random.default_rng(4).uniform(1.0, 2.0, size=y.shape)  # z >= 40: SiLU(z) = z in fp64
+    assert np.allclose(oracle.gated_rmsnorm(y, np.full(y.shape, 40.0), np.ones(64), 0.0, 16), plain, rtol=0,
+                       atol=1e-12)
+    assert np.allclose(oracle.gated_rmsnorm(y, 40.0 * s, np.ones(64), 0.0, 16),
+                       oracle.gated_rmsnorm(y * s, None, np.ones(64), 0.0, 16), rtol=0, atol=1e-12)
+    assert np.allclose(oracle.gated_rmsnorm(y, np.full(y.shape, -40.0), np.ones(64), 0.0, 16), -plain, rtol=0,
+                       atol=1e-12)
+
+
+def test_norm_zero_group_with_eps_is_zero():
+    y = np.zeros((2, 8))
+    y[1, 4:] = 1.0
+    out = oracle.gated_rmsnorm(y, None, np.ones(8), 1e-5, 4)
+    assert np.all(out[0] == 0.0) and np.all(out[1, :4] == 0.0)
+    assert np.allclose(out[1, 4:], 1.0 / math.sqrt(1.0 + 1e-5), rtol=0, atol=1e-15)
