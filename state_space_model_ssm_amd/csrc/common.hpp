@@ -156,5 +156,12 @@ __device__ __forceinline__ void st(void *p, int dt, int64_t i, float v) {
 
 __device__ __forceinline__ float softplus_f(float v) { return fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v))); }
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + expf(-v)); }
+// SiLU from the hardware exp2 and reciprocal (each about 1 ulp): a few
+// instructions instead of the accurate exp and IEEE divide, for the per-element
+// conv outputs of prefill. Relative error of a few fp32 ulp; the limits hold
+// (large negative v: exp2 -> inf, rcp -> 0, result -> 0; large positive: v).
+__device__ __forceinline__ float silu_fast(float v) {
+    return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.4426950408889634f));
+}
 
 }  // namespace m2

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(ConvFwdArgs a, int64_t cd
 #pragma unroll
                 for (int k = 0; k < W - 1; ++k) v += w[j * W + k] * win[k][j];
                 v += w[j * W + W - 1] * u[j];
-                o[j] = silu_f(v);
+                o[j] = silu_fast(v);
             }
         }
         if constexpr (BC) {

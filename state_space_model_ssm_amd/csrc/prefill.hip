@@ -131,32 +131,38 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     u32x4 br[BI];
     u32x4 cr[TW][KN];
     float dtr[LB];
+    // Addresses are a 64-bit chunk base plus 32-bit row offsets (rows of one
+    // chunk span far less than 2^31 elements).
+    const int xrow0 = R * xs - (W - 1);  // first raw row of the strip, relative to the chunk
     auto prefetch = [&](int64_t c0, int cl) {
-        const int64_t last = c0 + cl - 1;
+        const AT *xc = xin + c0 * cdim + offX + 4 * xg;
+        const bf16 *bcc = bc + c0 * bcs;
+        const int lo = (int)(start - c0);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
-            int64_t r = c0 + R * xs - (W - 1) + i;
-            r = r < start ? start : (r > last ? last : r);
-            xr[i].load(xin + r * cdim + offX + 4 * xg);
+            int r = xrow0 + i;
+            r = r < lo ? lo : (r > cl - 1 ? cl - 1 : r);
+            xr[i].load(xc + r * (int)cdim);
         }
 #pragma unroll
         for (int i = 0; i < BI; ++i) {
-            const int id = tid + i * NT, s = min(id / BPR, cl - 1), pc = id % BPR;
-            const int64_t off = (pc < N / 8 ? offBh : offBl - N) + 8 * pc;
-            br[i] = *reinterpret_cast<const u32x4 *>(bc + (c0 + s) * bcs + off);
+            const int id = tid + i * NT, sr = min(id / BPR, cl - 1), pc = id % BPR;
+            const int off = (pc < N / 8 ? (int)offBh : (int)offBl - N) + 8 * pc;
+            br[i] = *reinterpret_cast<const u32x4 *>(bcc + sr * (int)bcs + off);
         }
 #pragma unroll
         for (int w = 0; w < TW; ++w) {
             const int t = min(16 * ttile_of<TL, NW>(wave, w) + col, cl - 1);
 #pragma unroll
             for (int kn = 0; kn < KN; ++kn)
-                cr[w][kn] = *reinterpret_cast<const u32x4 *>(bc + (c0 + t) * bcs + offC + kn * 32 + q * 8);
+                cr[w][kn] = *reinterpret_cast<const u32x4 *>(bcc + t * (int)bcs + (int)offC + kn * 32 + q * 8);
         }
         if (wave == 0) {
+            const AT *dtc = static_cast<const AT *>(a.dt_raw) + c0 * H + head;
 #pragma unroll
             for (int b = 0; b < LB; ++b) {
                 const int t = min(b * 64 + lane, cl - 1);
-                dtr[b] = (float)static_cast<const AT *>(a.dt_raw)[(c0 + t) * H + head];
+                dtr[b] = (float)dtc[t * H];
             }
         }
     };
@@ -207,14 +213,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         {
             float u[NR][4];
 #pragma unroll
-            for (int i = 0; i < NR; ++i) {
-                const int64_t r = c0 + R * xs - (W - 1) + i;
+            for (int i = 0; i < NR; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) u[i][j] = xr[i][j];
-                if (r < start) {  // before the sequence: cached context (first chunk, first strip only)
+            if (c0 == start && xs == 0) {  // rows before the sequence: its cached context
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) u[i][j] = sCtx[(int)(r - start) + (W - 1)][4 * xg + j];
-                }
+                for (int i = 0; i < W - 1; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) u[i][j] = sCtx[i][4 * xg + j];
             }
 #pragma unroll
             for (int tp = 0; tp < R; tp += 2) {
@@ -228,7 +234,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                         float v = cb[j];
 #pragma unroll
                         for (int k = 0; k < W; ++k) v += cw[j * W + k] * u[tp + h2 + k][j];
-                        xv[h2][j] = ok ? silu_f(v) : 0.0f;
+                        xv[h2][j] = ok ? silu_fast(v) : 0.0f;
                     }
                     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
                     bf16x4 xb;
@@ -328,20 +334,41 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                     acc[pt] = mma(*reinterpret_cast<const bf16x8 *>(&sXD[(16 * pt + col) * XSb + 32 * m + q * 8]), mh,
                                   acc[pt]);
             }
-            if (valid) {
-                const int64_t tok = c0 + t;
+            // Epilogue: y = acc + D x (times SiLU(z)). The tile goes through this
+            // wave's own rows of sX (the rows it just read x from), so the global
+            // store writes whole 128-byte rows (2 x 8 rows of 64 bf16) instead of
+            // 32 bytes into each of 16 rows per instruction.
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            const int64_t tokc = c0 + (valid ? t : cl - 1);
+            bf16 *yc = y + c0 * HP + offX;
 #pragma unroll
-                for (int pt = 0; pt < TP; ++pt) {
-                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                    const bf16x4 xb = *reinterpret_cast<const bf16x4 *>(&sX[t * XRb + 16 * pt + 4 * q]);
-                    float o[4];
+            for (int pt = 0; pt < TP; ++pt) {
+                bf16x4 *px = reinterpret_cast<bf16x4 *>(&sX[t * XRb + 16 * pt + 4 * q]);
+                const bf16x4 xb = *px;
+                float o[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float v = acc[pt][r] + Dh * (float)xb[r];
-                        if (a.z) v *= silu_f((float)static_cast<const AT *>(a.z)[tok * HP + offX + 16 * pt + 4 * q + r]);
-                        o[r] = v;
-                    }
-                    store_k<bf16, 4>(y + tok * HP + offX + 16 * pt + 4 * q, o);
+                for (int r = 0; r < 4; ++r) o[r] = acc[pt][r] + Dh * (float)xb[r];
+                if (a.z) {
+                    float zf[4];
+                    load_k<AT, 4>(static_cast<const AT *>(a.z) + tokc * HP + offX + 16 * pt + 4 * q, zf);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] *= silu_fast(zf[r]);
+                }
+                bf16x4 ob;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ob[r] = f32_to_bf16(o[r]);
+                *px = ob;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int tr = 16 * tt + 8 * it + (lane >> 3), seg = lane & 7;
+                if (tr < cl) {
+                    const uint2 lo = *reinterpret_cast<const uint2 *>(&sX[tr * XRb + seg * 8]);
+                    const uint2 hi = *reinterpret_cast<const uint2 *>(&sX[tr * XRb + seg * 8 + 4]);
+                    *reinterpret_cast<uint4 *>(yc + tr * (int)HP + seg * 8) = uint4{lo.x, lo.y, hi.x, hi.y};
                 }
             }
         }
