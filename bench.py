@@ -167,6 +167,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-multi", action="store_true", help="skip the multi-token decode section")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill+decode batch")
@@ -264,6 +265,63 @@ def main():
     }
     del ssm, conv, xbc, dt, post, y
     torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ multi-token decode (drafted tokens)
+    if not args.no_multi:
+        Tm, rows_m = 4, 256
+        nsl = rows_m * (Tm + 1)
+        log(f"multi-token decode workload: {rows_m} rows x {Tm} tokens, bf16 pool of {nsl} slots")
+        rng = np.random.Generator(np.random.PCG64(5))
+        pm = synth.layer_params(d, rng)
+        tm = synth.tokens(d, rng, rows_m * Tm, with_z=False)
+        ssm_m = torch.empty(nsl, d.nheads, d.headdim, d.dstate, dtype=bf, device="cuda").normal_(0.0, 0.1 ** 0.5)
+        conv_m = torch.empty(nsl, d.conv_width - 1, d.conv_dim, dtype=bf, device="cuda").normal_()
+        xm = dev(tm["xbc"].reshape(rows_m, Tm, d.conv_dim), bf)
+        dtm = dev(tm["dt_raw"].reshape(rows_m, Tm, d.nheads), bf)
+        cwm = dev(pm["conv_w"], torch.float32)
+        Am, dtbm, Dm = (dev(pm[k], torch.float32) for k in ("A_log", "dt_bias", "D"))
+        srcm = torch.from_numpy(rng.permutation(nsl)[:rows_m].astype(np.int32)).cuda()
+        rest = np.setdiff1d(np.arange(nsl), srcm.cpu().numpy())
+        dstm = torch.from_numpy(rng.permutation(rest)[:rows_m * Tm].reshape(rows_m, Tm).astype(np.int32)).cuda()
+        postm = torch.empty(rows_m, Tm, d.conv_dim, dtype=bf, device="cuda")
+        ym = torch.empty(rows_m, Tm, d.d_inner, dtype=bf, device="cuda")
+        del tm
+
+        def multi_step(dst):
+            B.mamba2_conv1d_update_multi(d, xm, cwm, None, postm, conv_m, srcm, dst)
+            B.mamba2_state_update_multi(d, postm, dtm, Am, dtbm, Dm, None, ym, ssm_m, srcm, dst)
+
+        for _ in range(2):
+            multi_step(dstm)
+            multi_step(None)
+        ms_snap = time_region(lambda: multi_step(dstm), args.steps, torch)
+        ms_fin = time_region(lambda: multi_step(None), args.steps, torch)
+        H, P, N, G, W = d.nheads, d.headdim, d.dstate, d.ngroups, d.conv_width
+        cdim = d.conv_dim
+        tok_in = cdim * 2 + H * 2 + H * P * 2 + cdim * 2          # raw xBC, dt, y out, post-conv round trip
+        state, cstate = H * P * N * 2, (W - 1) * cdim * 2
+        b_snap = rows_m * (state + cstate + Tm * (state + cstate) + Tm * tok_in)
+        b_fin = rows_m * (2 * (state + cstate) + Tm * tok_in)
+        g_snap = b_snap / (ms_snap * 1e-3) / 1e9
+        g_fin = b_fin / (ms_fin * 1e-3) / 1e9
+        log(f"multi-token decode: every step snapshotted {ms_snap * 1e3:.1f} us ({g_snap:.0f} GB/s), final state "
+            f"only {ms_fin * 1e3:.1f} us ({rows_m * Tm / (ms_fin * 1e-3) / 1e6:.2f} M tok/s, {g_fin:.0f} GB/s)")
+        result["decode_multi"] = {
+            "workload": f"Nemotron-H-8B layer, {rows_m} rows x {Tm} tokens per row (a step verifying drafted "
+                        f"tokens), bf16 pools of {nsl} slots; step = conv1d_update_multi + state_update_multi",
+            "tokens_per_step": rows_m * Tm,
+            "snapshots_every_step": {"ms_per_step": round(ms_snap, 4),
+                                     "tok_s": round(rows_m * Tm / (ms_snap * 1e-3), 1),
+                                     "roofline": {"bound": "hbm", "achieved": round(g_snap, 1), "peak": HBM_PEAK_GBS,
+                                                  "unit": "GB/s", "frac": round(g_snap / HBM_PEAK_GBS, 4),
+                                                  "algorithmic_bytes": b_snap}},
+            "final_state_only": {"ms_per_step": round(ms_fin, 4), "tok_s": round(rows_m * Tm / (ms_fin * 1e-3), 1),
+                                 "roofline": {"bound": "hbm", "achieved": round(g_fin, 1), "peak": HBM_PEAK_GBS,
+                                              "unit": "GB/s", "frac": round(g_fin / HBM_PEAK_GBS, 4),
+                                              "algorithmic_bytes": b_fin}},
+        }
+        del ssm_m, conv_m, xm, dtm, postm, ym
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ prefill workload
     if not args.no_prefill:

@@ -159,6 +159,32 @@ int mamba2_state_update(const mamba2_dims *dims, const void *xbc, const void *dt
                         void *y, void *ssm_pool, const int32_t *state_indices, int32_t batch,
                         void *stream);
 
+/* Multi-token decode: `tokens` (T) consecutive tokens per row, as when a step
+ * verifies drafted tokens ([TRT-LLM]: one-model MTP in the hybrid serving
+ * configurations; the equivalence of one multi-token pass and T single steps is
+ * the [vllm.cpp] "Confirm or refute" contract). Row i starts from the state in
+ * slot src_indices[i] and takes its T tokens in order; after token t the state
+ * (conv window, SSM state) is written to slot dst_indices[i*T + t] when that is
+ * >= 0, a per-step snapshot the caller can resume from once it knows how many
+ * tokens were accepted. dst_indices NULL: only the final state is written, back
+ * to src_indices[i]. The state stays in registers between tokens, so it is
+ * rounded to the pool dtype only where it is written.
+ *   xbc [batch][T][Cdim] (raw for conv1d, post-conv xbc_dtype for the state
+ *   update); dt_raw [batch][T][H]; z [batch][T][H*P] or NULL; y [batch][T][H*P];
+ *   xbc_out [batch][T][Cdim] xbc_dtype.
+ * Every source slot is read before any destination is written only within a
+ * row: a destination that is another row's source (or two rows writing one
+ * slot) races. src_indices[i] < 0 marks a padding row (y = 0, no slot access). */
+int mamba2_conv1d_update_multi(const mamba2_dims *dims, const void *xbc, const float *conv_w,
+                               const float *conv_b, void *xbc_out, void *conv_pool,
+                               const int32_t *src_indices, const int32_t *dst_indices,
+                               int32_t batch, int32_t tokens, void *stream);
+int mamba2_state_update_multi(const mamba2_dims *dims, const void *xbc, const void *dt_raw,
+                              const float *A_log, const float *dt_bias, const float *D,
+                              const void *z, void *y, void *ssm_pool, const int32_t *src_indices,
+                              const int32_t *dst_indices, int32_t batch, int32_t tokens,
+                              void *stream);
+
 /* Mixed batch ([TRT-LLM] mixed prefill+decode iterations): the prefill
  * segment (packed by cu_seqlens) runs conv1d_fwd + chunk_scan_fwd, the
  * decode segment (`decode_batch` rows, one token each) runs conv1d_update +

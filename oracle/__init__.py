@@ -196,5 +196,42 @@ def decode(xbc_raw, dt_raw, params, state_indices, conv_pool, ssm_pool, *, H, P,
     return y, post
 
 
+def decode_multi(xbc_raw, dt_raw, params, src_indices, dst_indices, conv_pool, ssm_pool, *, H, P, N, G, z=None):
+    """T tokens per row (multi-token decode, e.g. verifying drafted tokens).
+
+    xbc_raw [B, T, Cdim]; dt_raw [B, T, H]; z [B, T, H*P] or None. Row i starts from
+    slot src_indices[i] and takes its T tokens in order, one step each. After step t
+    the conv and SSM state are written to slot dst_indices[i][t] when that is >= 0;
+    with dst_indices None only the final state is written, to src_indices[i]. Slots
+    are read before any is written. Rows with a negative source slot are padding:
+    y stays zero and no slot is touched. Returns (y [B, T, H*P], xbc_post [B, T, Cdim]).
+    """
+    Bd, T, Cdim = xbc_raw.shape
+    y = np.zeros((Bd, T, H * P), dtype=np.float64)
+    post = np.zeros((Bd, T, Cdim), dtype=np.float64)
+    start_conv = {int(s): conv_pool[int(s)].copy() for s in src_indices if s >= 0}
+    start_ssm = {int(s): ssm_pool[int(s)].copy() for s in src_indices if s >= 0}
+    writes = []
+    for i in range(Bd):
+        src = int(src_indices[i])
+        if src < 0:
+            continue
+        cs, hs = start_conv[src], start_ssm[src]
+        for t in range(T):
+            zz = None if z is None else z[i, t:t + 1]
+            yy, pp, cs, hs = layer_seq(xbc_raw[i, t:t + 1], dt_raw[i, t:t + 1], params, cs, hs, H=H, P=P, N=N, G=G,
+                                       z=zz)
+            y[i, t] = yy[0]
+            post[i, t] = pp[0]
+            if dst_indices is not None and int(dst_indices[i][t]) >= 0:
+                writes.append((int(dst_indices[i][t]), cs.copy(), hs.copy()))
+        if dst_indices is None:
+            writes.append((src, cs.copy(), hs.copy()))
+    for slot, cs, hs in writes:
+        conv_pool[slot] = cs
+        ssm_pool[slot] = hs
+    return y, post
+
+
 from . import dual  # noqa: E402,F401  (independent quadratic form)
 from .norm import gated_rmsnorm  # noqa: E402,F401  (the mixer's gated RMSNorm)

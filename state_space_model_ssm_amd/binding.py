@@ -67,6 +67,10 @@ _SIGS = {
     "mamba2_mixed_fwd": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                         _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P, ctypes.c_int32, _P,
                                         ctypes.c_size_t, _P]),
+    "mamba2_conv1d_update_multi": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P,
+                                                   ctypes.c_int32, ctypes.c_int32, _P]),
+    "mamba2_state_update_multi": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                  ctypes.c_int32, ctypes.c_int32, _P]),
     "mamba2_prefill_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(CDims), ctypes.c_int64,
                                                        ctypes.POINTER(ctypes.c_size_t)]),
     "mamba2_prefill_fwd": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
@@ -245,6 +249,43 @@ def mamba2_state_update(d: Dims, xbc, dt_raw, A_log, dt_bias, D, z, y, ssm_pool,
     _check(lib().mamba2_state_update(ctypes.byref(c), _ptr(xbc), _ptr(dt_raw), _ptr(A_log), _ptr(dt_bias), _ptr(D),
                                      _ptr(z), _ptr(y), _ptr(ssm_pool), _ptr(state_indices), Bd, _stream(stream)),
            "mamba2_state_update")
+
+
+def mamba2_conv1d_update_multi(d: Dims, xbc, conv_w, conv_b, xbc_out, conv_pool, src_indices, dst_indices=None, *,
+                               xbc_dtype=None, stream=None):
+    """xbc [batch, T, Cdim] raw; xbc_out [batch, T, Cdim]; dst_indices [batch, T] int32 or None."""
+    Bd, T = xbc.shape[0], xbc.shape[1]
+    _want(xbc, "xbc", _TORCH_DT[d.act_dtype], (Bd, T, d.conv_dim))
+    _want(conv_w, "conv_w", torch.float32, (d.conv_dim, d.conv_width))
+    _want(conv_b, "conv_b", torch.float32, (d.conv_dim,), optional=True)
+    _want(xbc_out, "xbc_out", _xdt(d, xbc_dtype), (Bd, T, d.conv_dim))
+    _want(conv_pool, "conv_pool", _TORCH_DT[d.state_dtype])
+    _want(src_indices, "src_indices", torch.int32, (Bd,))
+    _want(dst_indices, "dst_indices", torch.int32, (Bd, T), optional=True)
+    _check(lib().mamba2_conv1d_update_multi(ctypes.byref(cdims(d, xbc_dtype)), _ptr(xbc), _ptr(conv_w), _ptr(conv_b),
+                                            _ptr(xbc_out), _ptr(conv_pool), _ptr(src_indices), _ptr(dst_indices), Bd, T,
+                                            _stream(stream)), "mamba2_conv1d_update_multi")
+
+
+def mamba2_state_update_multi(d: Dims, xbc, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, src_indices, dst_indices=None,
+                              *, xbc_dtype=None, stream=None):
+    """xbc [batch, T, Cdim] post-conv; dt_raw [batch, T, H]; z/y [batch, T, H*P]; dst_indices [batch, T] or None."""
+    Bd, T = xbc.shape[0], xbc.shape[1]
+    H = d.nheads
+    _want(xbc, "xbc", _xdt(d, xbc_dtype), (Bd, T, d.conv_dim))
+    _want(dt_raw, "dt_raw", _TORCH_DT[d.act_dtype], (Bd, T, H))
+    for n, t in (("A_log", A_log), ("dt_bias", dt_bias), ("D", D)):
+        _want(t, n, torch.float32, (H,))
+    _want(z, "z", _TORCH_DT[d.act_dtype], (Bd, T, d.d_inner), optional=True)
+    _want(y, "y", _TORCH_DT[d.out_dtype], (Bd, T, d.d_inner))
+    _want(ssm_pool, "ssm_pool", _TORCH_DT[d.state_dtype])
+    if ssm_pool.dim() != 4 or tuple(ssm_pool.shape[1:]) != (H, d.headdim, d.dstate):
+        raise ValueError("ssm_pool must be [slots, H, P, N]")
+    _want(src_indices, "src_indices", torch.int32, (Bd,))
+    _want(dst_indices, "dst_indices", torch.int32, (Bd, T), optional=True)
+    _check(lib().mamba2_state_update_multi(ctypes.byref(cdims(d, xbc_dtype)), _ptr(xbc), _ptr(dt_raw), _ptr(A_log),
+                                           _ptr(dt_bias), _ptr(D), _ptr(z), _ptr(y), _ptr(ssm_pool), _ptr(src_indices),
+                                           _ptr(dst_indices), Bd, T, _stream(stream)), "mamba2_state_update_multi")
 
 
 def mamba2_prefill_workspace_bytes(d: Dims, total_tokens: int, *, xbc_dtype=None) -> int:

@@ -198,6 +198,40 @@ int mamba2_state_update(const mamba2_dims *d, const void *xbc, const void *dt_ra
     return hip_status(m2::launch_state_update(shape_of(d), a, static_cast<hipStream_t>(stream)), "state_update launch");
 }
 
+int mamba2_conv1d_update_multi(const mamba2_dims *d, const void *xbc, const float *conv_w, const float *conv_b,
+                               void *xbc_out, void *conv_pool, const int32_t *src_indices,
+                               const int32_t *dst_indices, int32_t batch, int32_t tokens, void *stream) {
+    int st = check_conv(d);
+    if (st) return st;
+    if (batch < 0 || tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative batch or tokens");
+    if (batch == 0 || tokens == 0) return ok();
+    REQUIRE_PTR(xbc); REQUIRE_PTR(conv_w); OPT_PTR(conv_b); REQUIRE_PTR(xbc_out); REQUIRE_PTR(conv_pool);
+    REQUIRE_IDX(src_indices);
+    if (dst_indices && (reinterpret_cast<uintptr_t>(dst_indices) & 3u))
+        return fail(MAMBA2_ERR_INVALID_ARG, "dst_indices is not 4-byte aligned");
+    if (xbc == xbc_out) return fail(MAMBA2_ERR_INVALID_ARG, "xbc_out must not alias xbc");
+    m2::ConvMultiArgs a{xbc, conv_w, conv_b, xbc_out, conv_pool, src_indices, dst_indices, batch, tokens};
+    return hip_status(m2::launch_conv_update_multi(shape_of(d), a, static_cast<hipStream_t>(stream)),
+                      "conv1d_update_multi launch");
+}
+
+int mamba2_state_update_multi(const mamba2_dims *d, const void *xbc, const void *dt_raw, const float *A_log,
+                              const float *dt_bias, const float *D, const void *z, void *y, void *ssm_pool,
+                              const int32_t *src_indices, const int32_t *dst_indices, int32_t batch, int32_t tokens,
+                              void *stream) {
+    int st = check_state_update(d);
+    if (st) return st;
+    if (batch < 0 || tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative batch or tokens");
+    if (batch == 0 || tokens == 0) return ok();
+    REQUIRE_PTR(xbc); REQUIRE_PTR(dt_raw); REQUIRE_PTR(A_log); REQUIRE_PTR(dt_bias); REQUIRE_PTR(D);
+    OPT_PTR(z); REQUIRE_PTR(y); REQUIRE_PTR(ssm_pool); REQUIRE_IDX(src_indices);
+    if (dst_indices && (reinterpret_cast<uintptr_t>(dst_indices) & 3u))
+        return fail(MAMBA2_ERR_INVALID_ARG, "dst_indices is not 4-byte aligned");
+    m2::MultiStepArgs a{xbc, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, src_indices, dst_indices, batch, tokens};
+    return hip_status(m2::launch_state_update_multi(shape_of(d), a, static_cast<hipStream_t>(stream)),
+                      "state_update_multi launch");
+}
+
 int mamba2_mixed_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw, const void *z, const float *conv_w,
                      const float *conv_b, const float *A_log, const float *dt_bias, const float *D, void *xbc_post,
                      void *y, void *ssm_pool, void *conv_pool, const int32_t *cu_seqlens, int32_t nseq,

@@ -153,6 +153,171 @@ hipError_t launch_state_update(const LayerShape &s, const StateUpdateArgs &a, hi
     return s.xbc_dt == DT_BF16 ? dispatch_su_n<float, bf16>(s, a, stream) : dispatch_su_n<float, float>(s, a, stream);
 }
 
+// ------------------------------------------------------- multi-token state update
+// T tokens per row (drafted tokens being verified, or any short run of decode
+// tokens): the row's state is read once from its source slot, kept in registers
+// through the T steps (so it is rounded to the pool dtype only where written),
+// and after step t written to dst[row][t] when that slot is >= 0 (a per-step
+// snapshot the caller can roll back to); with no dst table only the final state
+// is written, in place. Per step and lane the inputs are the same handful of
+// values as the one-token update.
+template <typename ST, typename XT, typename AT, int N, int ITERS>
+__global__ __launch_bounds__(256) void state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt,
+                                                                 int psplit) {
+    constexpr int kVec = Io<ST>::kVec;
+    constexpr int kLpr = N / kVec;
+    constexpr int kRpi = 256 / kLpr;  // p-rows per pass; each thread holds ITERS rows
+    const int tid = threadIdx.x;
+    const int head = blockIdx.x / psplit;
+    const int pblk = blockIdx.x - head * psplit;
+    const int row = blockIdx.y;
+    const int lr = tid & (kLpr - 1);
+    const int n0 = lr * kVec;
+    const int p_first = pblk * kRpi * ITERS + tid / kLpr;
+    const int64_t HP = (int64_t)H * P;
+    const int64_t cdim = HP + 2LL * G * N;
+    const int T = a.T;
+    const int src = a.src[row];
+    if (src < 0) {
+        if (lr == 0)
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) {
+                const int p = p_first + it * kRpi;
+                if (p < P)
+                    for (int t = 0; t < T; ++t) st(a.y, out_dt, ((int64_t)row * T + t) * HP + (int64_t)head * P + p, 0.0f);
+            }
+        return;
+    }
+    const int g = head / (H / G);
+    ST *pool = static_cast<ST *>(a.pool);
+    const int64_t tile0 = (int64_t)head * P * N + n0;
+    float h[ITERS][kVec];
+    int pr[ITERS];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        pr[it] = min(p_first + it * kRpi, P - 1);  // loads clamped; stores guarded
+        nt_load16<ST>(pool + (int64_t)src * H * P * N + tile0 + (int64_t)pr[it] * N, h[it]);
+    }
+    const float A = -expf(a.A_log[head]);
+    const float dtb = a.dt_bias[head];
+    const float Dh = a.D[head];
+    const AT *zsrc = a.z ? static_cast<const AT *>(a.z) : static_cast<const AT *>(a.dt_raw);
+
+    // B and C of a block of TB tokens are loaded once per workgroup into LDS
+    // (every p-row of the head uses the same vectors: re-reading them per row
+    // would move TB * 2 * N values per row through L1/L2 against N state
+    // values); x, dt and z of the block are loaded together, so a block of TB
+    // steps waits on memory once. Tokens past T are clamped and unused.
+    constexpr int TB = 4;
+    constexpr int NT4 = TB * 2 * N / 4;  // 4-element pieces of the block's B|C
+    __shared__ __attribute__((aligned(16))) float sBC[TB][2][N];
+    for (int t0 = 0; t0 < T; t0 += TB) {
+        if (t0 > 0) __syncthreads();  // previous block's B/C fully read
+        for (int k = tid; k < NT4; k += 256) {
+            const int u = k / (N / 2), rem = k % (N / 2), which = rem / (N / 4), n4 = rem % (N / 4);
+            const int64_t r = (int64_t)row * T + min(t0 + u, T - 1);
+            float v[4];
+            load_k<XT, 4>(static_cast<const XT *>(a.xbc) + r * cdim + HP + (int64_t)which * G * N + (int64_t)g * N + 4 * n4,
+                          v);
+            *reinterpret_cast<f32x4 *>(&sBC[u][which][4 * n4]) = f32x4{v[0], v[1], v[2], v[3]};
+        }
+        float xv[TB][ITERS], zv[TB][ITERS], dtr[TB];
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            const int64_t r = (int64_t)row * T + min(t0 + u, T - 1);
+            dtr[u] = (float)static_cast<const AT *>(a.dt_raw)[r * H + head];
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) {
+                xv[u][it] = (float)static_cast<const XT *>(a.xbc)[r * cdim + (int64_t)head * P + pr[it]];
+                zv[u][it] = (float)zsrc[a.z ? r * HP + (int64_t)head * P + pr[it] : 0];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            const int t = t0 + u;
+            if (t >= T) break;
+            float Bv[kVec], Cv[kVec];
+#pragma unroll
+            for (int j = 0; j < kVec; j += 4) {
+                const f32x4 bq = *reinterpret_cast<const f32x4 *>(&sBC[u][0][n0 + j]);
+                const f32x4 cq = *reinterpret_cast<const f32x4 *>(&sBC[u][1][n0 + j]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { Bv[j + e] = bq[e]; Cv[j + e] = cq[e]; }
+            }
+            const float dt = softplus_f(dtr[u] + dtb);
+            const float decay = expf(dt * A);
+            const int d = a.dst ? a.dst[(int64_t)row * T + t] : -1;
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) {
+                const int p = p_first + it * kRpi;
+                const float dx = dt * xv[u][it];
+                float acc = 0.0f;
+#pragma unroll
+                for (int j = 0; j < kVec; ++j) {
+                    h[it][j] = decay * h[it][j] + dx * Bv[j];
+                    acc += Cv[j] * h[it][j];
+                }
+                if (d >= 0 && p < P) nt_store16<ST>(pool + (int64_t)d * H * P * N + tile0 + (int64_t)p * N, h[it]);
+#pragma unroll
+                for (int m = kLpr / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+                if (lr == 0 && p < P) {
+                    float yv = acc + Dh * xv[u][it];
+                    if (a.z) yv *= silu_f(zv[u][it]);
+                    st(a.y, out_dt, ((int64_t)row * T + t) * HP + (int64_t)head * P + p, yv);
+                }
+            }
+        }
+    }
+    if (!a.dst)
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+            const int p = p_first + it * kRpi;
+            if (p < P) nt_store16<ST>(pool + (int64_t)src * H * P * N + tile0 + (int64_t)p * N, h[it]);
+        }
+}
+
+template <typename ST, typename XT, int N, int ITERS>
+static hipError_t launch_sum(const LayerShape &s, const MultiStepArgs &a, hipStream_t stream, int rows_needed) {
+    const int psplit = (rows_needed + ITERS - 1) / ITERS;
+    dim3 grid(s.H * psplit, a.batch);
+    if (s.act_dt == DT_BF16)
+        hipLaunchKernelGGL((state_update_multi_kernel<ST, XT, bf16, N, ITERS>), grid, dim3(256), 0, stream, a, s.H,
+                           s.P, s.G, s.out_dt, psplit);
+    else
+        hipLaunchKernelGGL((state_update_multi_kernel<ST, XT, float, N, ITERS>), grid, dim3(256), 0, stream, a, s.H,
+                           s.P, s.G, s.out_dt, psplit);
+    return hipGetLastError();
+}
+
+template <typename ST, typename XT, int N>
+static hipError_t launch_sum_i(const LayerShape &s, const MultiStepArgs &a, hipStream_t stream) {
+    constexpr int kRpi = 256 / (N / Io<ST>::kVec);
+    const int rows_needed = (s.P + kRpi - 1) / kRpi;  // passes that cover one head tile
+    // as many state rows per thread as keeps >= 2048 workgroups (8 per CU)
+    const int64_t wg1 = (int64_t)a.batch * s.H * rows_needed;
+    if (rows_needed >= 4 && wg1 / 4 >= 2048) return launch_sum<ST, XT, N, 4>(s, a, stream, rows_needed);
+    if (rows_needed >= 2 && wg1 / 2 >= 2048) return launch_sum<ST, XT, N, 2>(s, a, stream, rows_needed);
+    return launch_sum<ST, XT, N, 1>(s, a, stream, rows_needed);
+}
+
+template <typename ST, typename XT>
+static hipError_t launch_sum_n(const LayerShape &s, const MultiStepArgs &a, hipStream_t stream) {
+    switch (s.N) {
+        case 16: return launch_sum_i<ST, XT, 16>(s, a, stream);
+        case 64: return launch_sum_i<ST, XT, 64>(s, a, stream);
+        case 128: return launch_sum_i<ST, XT, 128>(s, a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_state_update_multi(const LayerShape &s, const MultiStepArgs &a, hipStream_t stream) {
+    if (a.batch == 0 || a.T == 0) return hipSuccess;
+    if (s.state_dt == DT_BF16)
+        return s.xbc_dt == DT_BF16 ? launch_sum_n<bf16, bf16>(s, a, stream) : launch_sum_n<bf16, float>(s, a, stream);
+    return s.xbc_dt == DT_BF16 ? launch_sum_n<float, bf16>(s, a, stream) : launch_sum_n<float, float>(s, a, stream);
+}
+
 // ----------------------------------------------------------------- conv update
 // One thread per 8 channels of one row: window = [cached W-1 inputs || u],
 // out = SiLU(bias + sum_k w[k] * window[k]); the cache shifts by one.
@@ -216,6 +381,86 @@ static hipError_t launch_cu_s(const LayerShape &s, const ConvUpdateArgs &a, hipS
 hipError_t launch_conv_update(const LayerShape &s, const ConvUpdateArgs &a, hipStream_t stream) {
     if (a.batch == 0) return hipSuccess;
     return s.act_dt == DT_BF16 ? launch_cu_s<bf16>(s, a, stream) : launch_cu_s<float>(s, a, stream);
+}
+
+// T tokens per row: window = [cached W-1 inputs || token], shifted per token;
+// after token t the window goes to dst[row][t] when that slot is >= 0 (no dst
+// table: the final window to the source slot).
+template <typename AT, typename ST, typename XT, int W>
+__global__ __launch_bounds__(256) void conv_update_multi_kernel(ConvMultiArgs a, int64_t cdim) {
+    const int row = blockIdx.y;
+    const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (c0 >= cdim) return;
+    const int T = a.T;
+    const int src = a.src[row];
+    float o[8];
+    if (src < 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = 0.0f;
+        for (int t = 0; t < T; ++t) store_k<XT, 8>(static_cast<XT *>(a.out) + ((int64_t)row * T + t) * cdim + c0, o);
+        return;
+    }
+    ST *pool = static_cast<ST *>(a.pool);
+    float win[W - 1][8], w[8 * W];
+#pragma unroll
+    for (int k = 0; k < W - 1; ++k) load_k<ST, 8>(pool + ((int64_t)src * (W - 1) + k) * cdim + c0, win[k]);
+    load_k<float, 8 * W>(a.w + c0 * W, w);
+    for (int t = 0; t < T; ++t) {
+        float u[8];
+        load_k<AT, 8>(static_cast<const AT *>(a.xbc) + ((int64_t)row * T + t) * cdim + c0, u);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float v = a.b ? a.b[c0 + j] : 0.0f;
+#pragma unroll
+            for (int k = 0; k < W - 1; ++k) v += w[j * W + k] * win[k][j];
+            v += w[j * W + W - 1] * u[j];
+            o[j] = silu_f(v);
+        }
+        store_k<XT, 8>(static_cast<XT *>(a.out) + ((int64_t)row * T + t) * cdim + c0, o);
+#pragma unroll
+        for (int k = 0; k < W - 2; ++k)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) win[k][j] = win[k + 1][j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) win[W - 2][j] = u[j];
+        if (a.dst) {
+            const int d = a.dst[(int64_t)row * T + t];
+            if (d >= 0)
+#pragma unroll
+                for (int k = 0; k < W - 1; ++k) store_k<ST, 8>(pool + ((int64_t)d * (W - 1) + k) * cdim + c0, win[k]);
+        }
+    }
+    if (!a.dst)
+#pragma unroll
+        for (int k = 0; k < W - 1; ++k) store_k<ST, 8>(pool + ((int64_t)src * (W - 1) + k) * cdim + c0, win[k]);
+}
+
+template <typename AT, typename ST, typename XT>
+static hipError_t launch_cum_w(const LayerShape &s, const ConvMultiArgs &a, hipStream_t stream) {
+    const int64_t cdim = s.cdim();
+    dim3 grid((unsigned)((cdim / 8 + 255) / 256), a.batch);
+    switch (s.W) {
+        case 2: hipLaunchKernelGGL((conv_update_multi_kernel<AT, ST, XT, 2>), grid, dim3(256), 0, stream, a, cdim); break;
+        case 3: hipLaunchKernelGGL((conv_update_multi_kernel<AT, ST, XT, 3>), grid, dim3(256), 0, stream, a, cdim); break;
+        case 4: hipLaunchKernelGGL((conv_update_multi_kernel<AT, ST, XT, 4>), grid, dim3(256), 0, stream, a, cdim); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename AT, typename ST>
+static hipError_t launch_cum_x(const LayerShape &s, const ConvMultiArgs &a, hipStream_t stream) {
+    return s.xbc_dt == DT_BF16 ? launch_cum_w<AT, ST, bf16>(s, a, stream) : launch_cum_w<AT, ST, float>(s, a, stream);
+}
+
+template <typename AT>
+static hipError_t launch_cum_s(const LayerShape &s, const ConvMultiArgs &a, hipStream_t stream) {
+    return s.state_dt == DT_BF16 ? launch_cum_x<AT, bf16>(s, a, stream) : launch_cum_x<AT, float>(s, a, stream);
+}
+
+hipError_t launch_conv_update_multi(const LayerShape &s, const ConvMultiArgs &a, hipStream_t stream) {
+    if (a.batch == 0 || a.T == 0) return hipSuccess;
+    return s.act_dt == DT_BF16 ? launch_cum_s<bf16>(s, a, stream) : launch_cum_s<float>(s, a, stream);
 }
 
 }  // namespace m2

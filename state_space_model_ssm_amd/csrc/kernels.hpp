@@ -56,6 +56,29 @@ struct ScanArgs {
     int64_t T;
 };
 
+// T tokens per row: activations [batch][T][...]; src [batch] (slot read before the
+// first token), dst [batch][T] (slot written after each token, < 0 = skip) or
+// null (final state written back to src).
+struct MultiStepArgs {
+    const void *xbc;      // [batch][T][Cdim] post-conv
+    const void *dt_raw;   // [batch][T][H]
+    const float *A_log, *dt_bias, *D;
+    const void *z;        // [batch][T][H*P] or null
+    void *y;              // [batch][T][H*P]
+    void *pool;           // [slots][H][P][N]
+    const int32_t *src, *dst;
+    int batch, T;
+};
+
+struct ConvMultiArgs {
+    const void *xbc;      // [batch][T][Cdim] raw
+    const float *w, *b;
+    void *out;            // [batch][T][Cdim]
+    void *pool;           // [slots][W-1][Cdim]
+    const int32_t *src, *dst;
+    int batch, T;
+};
+
 struct PrefillArgs {
     const void *xbc;      // [T][Cdim] raw (pre-conv), activation dtype
     const void *bc;       // [T][3*G*N] bf16 planes B hi | B lo | C (post-conv), from launch_bc_planes
@@ -85,6 +108,9 @@ struct NormArgs {
 // false for shapes outside the compiled set (no launch happens).
 bool state_update_supported(const LayerShape &s);
 hipError_t launch_state_update(const LayerShape &s, const StateUpdateArgs &a, hipStream_t st);
+
+hipError_t launch_state_update_multi(const LayerShape &s, const MultiStepArgs &a, hipStream_t st);
+hipError_t launch_conv_update_multi(const LayerShape &s, const ConvMultiArgs &a, hipStream_t st);
 
 bool conv_supported(const LayerShape &s);
 hipError_t launch_conv_update(const LayerShape &s, const ConvUpdateArgs &a, hipStream_t st);

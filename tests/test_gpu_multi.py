@@ -1,0 +1,115 @@
+"""GPU parity of multi-token decode (T tokens per row with per-step state snapshots, as
+when a step verifies drafted tokens) against the fp64 oracle, and its equivalence with
+T one-token steps."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _helpers import assert_close, dev, dev_i32, host, oracle_kw, params_dev
+from state_space_model_ssm_amd import binding as B
+from state_space_model_ssm_amd import synth
+from state_space_model_ssm_amd.configs import BF16, F32, NEMOTRON_H_8B
+
+pytestmark = pytest.mark.gpu
+
+D16 = NEMOTRON_H_8B.with_(nheads=16, ngroups=2, state_dtype=F32, out_dtype=F32)
+
+
+def make_inputs(d, seed, rows, T, num_slots, with_z, init_slots=None):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    params = synth.layer_params(d, rng)
+    tok = synth.tokens(d, rng, rows * T, with_z=with_z)
+    pl = synth.pools(d, rng, num_slots, list(range(num_slots)) if init_slots is None else init_slots)
+    x = tok["xbc"].reshape(rows, T, d.conv_dim)
+    dt = tok["dt_raw"].reshape(rows, T, d.nheads)
+    z = None if tok["z"] is None else tok["z"].reshape(rows, T, d.d_inner)
+    return params, x, dt, z, pl
+
+
+def run_multi(d, params, x, dt, z, pl, src, dst):
+    rows, T = x.shape[:2]
+    pd = params_dev(params)
+    conv, ssm = dev(pl["conv_pool"], d.state_dtype), dev(pl["ssm_pool"], d.state_dtype)
+    xb, dtb = dev(x, d.act_dtype), dev(dt, d.act_dtype)
+    zb = None if z is None else dev(z, d.act_dtype)
+    post = torch.empty(rows, T, d.conv_dim, dtype=B._TORCH_DT[d.post_dtype], device="cuda")
+    y = torch.empty(rows, T, d.d_inner, dtype=B._TORCH_DT[d.out_dtype], device="cuda")
+    si = dev_i32(src)
+    di = None if dst is None else dev_i32(dst)
+    B.mamba2_conv1d_update_multi(d, xb, pd["conv_w"], None, post, conv, si, di)
+    B.mamba2_state_update_multi(d, post, dtb, pd["A_log"], pd["dt_bias"], pd["D"], zb, y, ssm, si, di)
+    torch.cuda.synchronize()
+    return y, conv, ssm
+
+
+@pytest.mark.parametrize("state_dtype,out_dtype", [(F32, F32), (BF16, BF16), (BF16, F32)])
+@pytest.mark.parametrize("with_z", [False, True])
+def test_multi_token_decode_matches_oracle(state_dtype, out_dtype, with_z):
+    d = D16.with_(state_dtype=state_dtype, out_dtype=out_dtype)
+    print(f"[multi decode] state={state_dtype} out={out_dtype} z={with_z}", flush=True)
+    rows, T, slots = 5, 4, 24
+    params, x, dt, z, pl = make_inputs(d, 41, rows, T, slots, with_z)
+    src = np.array([3, 7, -1, 11, 0], np.int32)
+    dst = np.array([[12, 13, 14, 3],      # snapshots, final state back in place
+                    [15, -1, 16, -1],     # some steps not kept
+                    [17, 18, 19, 20],     # padding row: nothing written
+                    [21, 22, 23, 11],
+                    [-1, -1, -1, 0]], np.int32)
+    y, conv, ssm = run_multi(d, params, x, dt, z, pl, src, dst)
+    cp = pl["conv_pool"].astype(np.float64)
+    sp = pl["ssm_pool"].astype(np.float64)
+    y_ref, _ = oracle.decode_multi(x, dt, params, src, dst, cp, sp, z=z, **oracle_kw(d))
+    assert_close(host(y), y_ref, out_dtype, "y")
+    assert torch.all(y[2] == 0).item()
+    written = sorted({int(v) for r in (0, 1, 3, 4) for v in dst[r] if v >= 0})
+    u = torch.tensor(written, dtype=torch.long, device="cuda")
+    assert_close(host(ssm[u]), sp[written], state_dtype, "state snapshots")
+    assert np.array_equal(host(conv[u]), cp[written]), "conv snapshots hold the exact raw inputs"
+    untouched = [17, 18, 19, 20, 1, 2]
+    assert np.array_equal(host(ssm[untouched]), pl["ssm_pool"][untouched].astype(np.float64))
+
+
+def test_multi_token_equals_single_steps_bitwise_fp32():
+    """Without snapshots the final state goes back to the source slot; with an fp32 pool the
+    T-token pass performs exactly the arithmetic of T one-token calls."""
+    d = D16
+    rows, T, slots = 6, 5, 8
+    params, x, dt, z, pl = make_inputs(d, 42, rows, T, slots, True)
+    src = np.array([5, 0, 7, 2, -1, 3], np.int32)
+    y_m, conv_m, ssm_m = run_multi(d, params, x, dt, z, pl, src, None)
+    pd = params_dev(params)
+    conv, ssm = dev(pl["conv_pool"], F32), dev(pl["ssm_pool"], F32)
+    si = dev_i32(src)
+    post = torch.empty(rows, d.conv_dim, device="cuda")
+    for t in range(T):
+        yt = torch.empty(rows, d.d_inner, device="cuda")
+        A = d.act_dtype
+        B.mamba2_conv1d_update(d, dev(x[:, t], A), pd["conv_w"], None, post, conv, si)
+        B.mamba2_state_update(d, post, dev(dt[:, t], A), pd["A_log"], pd["dt_bias"], pd["D"], dev(z[:, t], A), yt,
+                              ssm, si)
+        torch.cuda.synchronize()
+        assert torch.equal(yt, y_m[:, t]), f"y differs at token {t}"
+    assert torch.equal(ssm, ssm_m) and torch.equal(conv, conv_m)
+
+
+def test_multi_token_full_dims_sampled():
+    """Nemotron-H-8B dims (128 heads, bf16 pool), 64 rows x 4 tokens, every step snapshotted."""
+    d = NEMOTRON_H_8B
+    print("[multi decode] 8B dims, 64 rows x 4 tokens", flush=True)
+    rows, T = 64, 4
+    slots = rows * (T + 1)
+    params, x, dt, z, pl = make_inputs(d, 43, rows, T, slots, False, init_slots=list(range(rows)))
+    src = np.arange(rows, dtype=np.int32)
+    dst = (rows + np.arange(rows * T, dtype=np.int32)).reshape(rows, T)
+    y, conv, ssm = run_multi(d, params, x, dt, z, pl, src, dst)
+    for r in (0, 17, 63):
+        used = [int(src[r])] + [int(v) for v in dst[r]]  # compact fp64 pools for the oracle
+        cp = pl["conv_pool"][used].astype(np.float64)
+        sp = pl["ssm_pool"][used].astype(np.float64)
+        y_ref, _ = oracle.decode_multi(x[r:r + 1], dt[r:r + 1], params, np.array([0]),
+                                       np.arange(1, T + 1).reshape(1, T), cp, sp, **oracle_kw(d))
+        assert_close(host(y[r:r + 1]), y_ref, BF16, f"y row {r}")
+        u = used[1:]
+        assert_close(host(ssm[u]), sp[1:], BF16, f"snapshots row {r}")
+        assert np.array_equal(host(conv[u]), cp[1:])

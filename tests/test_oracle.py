@@ -398,3 +398,35 @@ def test_norm_zero_group_with_eps_is_zero():
     out = oracle.gated_rmsnorm(y, None, np.ones(8), 1e-5, 4)
     assert np.all(out[0] == 0.0) and np.all(out[1, :4] == 0.0)
     assert np.allclose(out[1, 4:], 1.0 / math.sqrt(1.0 + 1e-5), rtol=0, atol=1e-15)
+
+
+def test_multi_token_decode_equals_single_steps_and_snapshots():
+    """T tokens per row through decode_multi equal T one-token decode calls (the same C
+    loop, so bit-identical), and each per-step snapshot is the state after that step."""
+    d = TINY
+    rng = np.random.default_rng(31)
+    w = synth.prefill_batch(d, seed=31, seqlens=[1], num_slots=8, initial_state=False)
+    params = w["params"]
+    kw = dict(H=d.nheads, P=d.headdim, N=d.dstate, G=d.ngroups)
+    Bd, T = 3, 4
+    x = rng.standard_normal((Bd, T, d.conv_dim))
+    dt = rng.standard_normal((Bd, T, d.nheads)) * 0.7
+    z = rng.standard_normal((Bd, T, d.d_inner))
+    cp = rng.standard_normal((8, d.conv_width - 1, d.conv_dim))
+    sp = rng.standard_normal((8, d.nheads, d.headdim, d.dstate)) * 0.3
+    src = np.array([5, -1, 2])
+    dst = np.array([[0, 1, -1, 5], [3, 3, 3, 3], [4, -1, 6, 7]])
+    cp1, sp1 = cp.copy(), sp.copy()
+    y, _ = oracle.decode_multi(x, dt, params, src, dst, cp1, sp1, z=z, **kw)
+    cp2, sp2 = cp.copy(), sp.copy()
+    for t in range(T):
+        yt, _ = oracle.decode(x[:, t], dt[:, t], params, src, cp2, sp2, z=z[:, t], **kw)
+        assert np.array_equal(yt, y[:, t])
+        for i in (0, 2):
+            if dst[i][t] >= 0:
+                assert np.array_equal(sp1[dst[i][t]], sp2[src[i]]) and np.array_equal(cp1[dst[i][t]], cp2[src[i]])
+    assert np.all(y[1] == 0) and np.array_equal(sp1[3], sp[3]) and np.array_equal(cp1[3], cp[3])
+    # without destinations the final state lands in the source slot
+    cp3, sp3 = cp.copy(), sp.copy()
+    oracle.decode_multi(x, dt, params, src, None, cp3, sp3, z=z, **kw)
+    assert np.array_equal(sp3[5], sp2[5]) and np.array_equal(sp3[2], sp2[2]) and np.array_equal(cp3[2], cp2[2])
