@@ -15,7 +15,10 @@ Sources of what it computes (see ``ssm_oracle.c`` for the step list):
   * the equivalence contract (a T-token chunk scan equals T single steps):
     the vllm.cpp issue, section "Confirm or refute";
   * the gated RMSNorm of the mixer output (``norm.py``): the record's "norm"
-    mixer tensor.
+    mixer tensor;
+  * the Mamba-1 selective scan (diagonal A per channel and state): the
+    "selective_scan_fwd" kernel the trace page names for Mamba layers, with the
+    recurrence of the Mamba paper that page cites.
 
 Every function here loops over sequences and tokens in order and calls the C
 routines, which hold the arithmetic. ``dual`` (the quadratic matrix form) is a
@@ -62,6 +65,10 @@ def _load():
                                            ctypes.c_int32, ctypes.c_int32, dp, dp, dp, dp, dp, dp,
                                            dp, dp, ctypes.c_int32]
             lib.oracle_ssm_seq.restype = None
+            lib.oracle_selective_scan_seq.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                      ctypes.c_int32, dp, dp, dp, dp, dp, dp, dp, dp,
+                                                      ctypes.c_int32, dp, dp]
+            lib.oracle_selective_scan_seq.restype = None
             for name in ("oracle_softplus", "oracle_silu", "oracle_round_bf16"):
                 getattr(lib, name).argtypes = [ctypes.c_double]
                 getattr(lib, name).restype = ctypes.c_double
@@ -194,6 +201,49 @@ def decode(xbc_raw, dt_raw, params, state_indices, conv_pool, ssm_pool, *, H, P,
         conv_pool[slot] = cs
         ssm_pool[slot] = hs
     return y, post
+
+
+def selective_scan_seq(u, delta_raw, A, B, C, h0, *, D=None, z=None, delta_bias=None, delta_softplus=True):
+    """One sequence of the Mamba-1 selective scan (diagonal A per channel and state).
+
+    u, delta_raw [T, Dc]; A [Dc, N]; B, C [T, G, N]; h0 [Dc, N]; D, delta_bias [Dc] or
+    None; z [T, Dc] or None. Returns (y [T, Dc], h_final [Dc, N]).
+    """
+    u = _f64(u)
+    T, Dc = u.shape
+    A = _f64(A)
+    N = A.shape[1]
+    B = _f64(B).reshape(T, -1, N)
+    G = B.shape[1]
+    assert Dc % G == 0
+    h = np.array(h0, dtype=np.float64, copy=True).reshape(Dc, N)
+    y = np.empty((T, Dc), dtype=np.float64)
+    _load().oracle_selective_scan_seq(T, Dc, N, G, _ptr(u), _ptr(_f64(delta_raw).reshape(T, Dc)), _ptr(A), _ptr(B),
+                                      _ptr(_f64(C).reshape(T, G, N)), _ptr(_f64(D)),
+                                      _ptr(None if z is None else _f64(z).reshape(T, Dc)), _ptr(_f64(delta_bias)),
+                                      1 if delta_softplus else 0, _ptr(h), _ptr(y))
+    return y, h
+
+
+def selective_scan(u, delta_raw, A, B, C, cu_seqlens, state_indices, has_initial_state, ssm_pool, *, D=None, z=None,
+                   delta_bias=None, delta_softplus=True):
+    """Packed sequences of the selective scan; ssm_pool [slots, Dc, N] fp64, updated in place
+    (final state of each sequence to its slot; negative slot = padding, y stays zero)."""
+    T, Dc = u.shape
+    y = np.zeros((T, Dc), dtype=np.float64)
+    for i in range(len(cu_seqlens) - 1):
+        s, e = int(cu_seqlens[i]), int(cu_seqlens[i + 1])
+        slot = int(state_indices[i])
+        if slot < 0:
+            continue
+        init = bool(has_initial_state[i]) if has_initial_state is not None else False
+        h0 = ssm_pool[slot] if init else np.zeros_like(ssm_pool[slot])
+        yy, hh = selective_scan_seq(u[s:e], delta_raw[s:e], A, B[s:e], C[s:e], h0, D=D,
+                                    z=None if z is None else z[s:e], delta_bias=delta_bias,
+                                    delta_softplus=delta_softplus)
+        y[s:e] = yy
+        ssm_pool[slot] = hh
+    return y
 
 
 def decode_multi(xbc_raw, dt_raw, params, src_indices, dst_indices, conv_pool, ssm_pool, *, H, P, N, G, z=None):

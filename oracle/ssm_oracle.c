@@ -28,8 +28,19 @@
  *     ("NemotronH runs the PREFILL mamba kernels at decode", section "Confirm
  *     or refute") gives hpg = H/G. Reading: head h belongs to group h / hpg.
  *
- * Everything is fp64, no fast-math; OpenMP runs only across heads, which are
- * independent, never across time.
+ *  3. The selective scan of the Mamba paper (S6, the "selective_scan_fwd"
+ *     kernel the trace page names for Mamba layers): a diagonal state per
+ *     (channel d, state n) with its own decay A[d][n],
+ *        delta = softplus(delta_raw + delta_bias)   (or delta_raw + bias)
+ *        h_t[d][n] = exp(delta_t[d] * A[d][n]) * h_{t-1}[d][n]
+ *                    + delta_t[d] * B_t[g][n] * u_t[d]
+ *        y_t[d]    = sum_n C_t[g][n] * h_t[d][n] + D[d] * u_t[d]  (* SiLU(z))
+ *     with B and C shared by the D/G channels of a group g = d / (D/G).
+ *     Reading: the input matrix is discretised as delta * B (the form the
+ *     paper's implementation uses), A as exp(delta * A).
+ *
+ * Everything is fp64, no fast-math; OpenMP runs only across heads or
+ * channels, which are independent, never across time.
  */
 #include <math.h>
 #include <stddef.h>
@@ -135,6 +146,37 @@ void oracle_ssm_seq(int64_t T, int32_t H, int32_t P, int32_t N, int32_t G, const
 }
 
 /* Scalar helpers exposed so tests can pin them against closed forms. */
+/* One sequence of the selective scan (item 3). u, delta_raw [T][Dc]; A [Dc][N];
+ * B, C [T][G][N]; Dv, delta_bias [Dc] or NULL; z [T][Dc] or NULL; h [Dc][N]
+ * in/out; y [T][Dc]. */
+void oracle_selective_scan_seq(int64_t T, int32_t Dc, int32_t N, int32_t G, const double *u,
+                               const double *delta_raw, const double *A, const double *B,
+                               const double *C, const double *Dv, const double *z,
+                               const double *delta_bias, int32_t delta_softplus, double *h,
+                               double *y) {
+    const int32_t cpg = Dc / G;
+#pragma omp parallel for schedule(static)
+    for (int32_t d = 0; d < Dc; ++d) {
+        const int32_t g = d / cpg;
+        double *hd = h + (int64_t)d * N;
+        for (int64_t t = 0; t < T; ++t) {
+            double dl = delta_raw[t * Dc + d] + (delta_bias ? delta_bias[d] : 0.0);
+            if (delta_softplus) dl = softplus(dl);
+            const double ut = u[t * Dc + d];
+            const double *Bt = B + (t * G + g) * N;
+            const double *Ct = C + (t * G + g) * N;
+            double acc = 0.0;
+            for (int32_t n = 0; n < N; ++n) {
+                hd[n] = exp(dl * A[(int64_t)d * N + n]) * hd[n] + dl * Bt[n] * ut;
+                acc += Ct[n] * hd[n];
+            }
+            if (Dv) acc += Dv[d] * ut;
+            if (z) acc *= silu(z[t * Dc + d]);
+            y[t * Dc + d] = acc;
+        }
+    }
+}
+
 double oracle_softplus(double v) { return softplus(v); }
 double oracle_silu(double v) { return silu(v); }
 double oracle_round_bf16(double v) { return round_bf16(v); }

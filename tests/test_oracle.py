@@ -430,3 +430,104 @@ def test_multi_token_decode_equals_single_steps_and_snapshots():
     cp3, sp3 = cp.copy(), sp.copy()
     oracle.decode_multi(x, dt, params, src, None, cp3, sp3, z=z, **kw)
     assert np.array_equal(sp3[5], sp2[5]) and np.array_equal(sp3[2], sp2[2]) and np.array_equal(cp3[2], cp2[2])
+
+
+# ---------------------------------------------------------------- Mamba-1 selective scan
+# The "selective_scan_fwd" kernel named on the trace page; the recurrence of the Mamba
+# paper (diagonal A per channel and state). Pins: reduction to the (separately pinned)
+# scalar-A recurrence, a closed form, A = 0, and the unrolled quadratic form.
+
+def _sel_inputs(T, Dc, N, G, seed):
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal((T, Dc))
+    dr = rng.standard_normal((T, Dc)) * 0.7
+    A = -np.exp(rng.uniform(-1.0, 1.5, size=(Dc, N)))
+    Bm = rng.standard_normal((T, G, N)) / math.sqrt(N)
+    Cm = rng.standard_normal((T, G, N)) / math.sqrt(N)
+    return rng, u, dr, A, Bm, Cm
+
+
+def test_selective_scan_reduces_to_scalar_decay_recurrence():
+    """With A constant over a head's channels and states and delta shared by the head, the
+    selective scan is the scalar-A recurrence (x = u)."""
+    H, P, N, G, T = 4, 3, 5, 2, 9
+    rng = np.random.default_rng(40)
+    A_log = rng.uniform(-1.0, 1.0, H)
+    dt_bias = rng.standard_normal(H) * 0.3
+    D = rng.standard_normal(H)
+    x = rng.standard_normal((T, H * P))
+    Bm = rng.standard_normal((T, G, N))
+    Cm = rng.standard_normal((T, G, N))
+    dt_raw = rng.standard_normal((T, H))
+    h0 = rng.standard_normal((H, P, N)) * 0.3
+    z = rng.standard_normal((T, H * P))
+    xbc = np.concatenate([x, Bm.reshape(T, G * N), Cm.reshape(T, G * N)], axis=1)
+    y2, h2 = oracle.ssm_seq(xbc, dt_raw, A_log, dt_bias, D, h0, H=H, P=P, N=N, G=G, z=z)
+    rep = lambda v: np.repeat(v, P, axis=-1)
+    A1 = np.repeat(-np.exp(A_log), P)[:, None] * np.ones((1, N))
+    y1, h1 = oracle.selective_scan_seq(x, rep(dt_raw), A1, Bm, Cm, h0.reshape(H * P, N), D=rep(D), z=z,
+                                       delta_bias=rep(dt_bias))
+    assert np.allclose(y1, y2, rtol=1e-12, atol=1e-12)
+    assert np.allclose(h1.reshape(H, P, N), h2, rtol=1e-12, atol=1e-13)
+
+
+def test_selective_scan_scalar_closed_form():
+    """Dc = N = 1, constant delta, u, B: h_t = a^t h0 + delta u B (1 - a^t) / (1 - a)."""
+    T, dl, uu, bb, cc, A, h0 = 12, 0.3, 1.7, -0.6, 1.3, -0.8, 0.45
+    a = math.exp(dl * A)
+    y, h = oracle.selective_scan_seq(np.full((T, 1), uu), np.full((T, 1), dl), np.array([[A]]),
+                                     np.full((T, 1, 1), bb), np.full((T, 1, 1), cc), np.array([[h0]]),
+                                     delta_softplus=False)
+    ht = [a ** (t + 1) * h0 + dl * uu * bb * (1 - a ** (t + 1)) / (1 - a) for t in range(T)]
+    assert np.allclose(y[:, 0], cc * np.array(ht), rtol=1e-13, atol=1e-14)
+    assert math.isclose(h[0, 0], ht[-1], rel_tol=1e-13)
+
+
+def test_selective_scan_zero_decay_is_cumsum():
+    T, Dc, N, G = 7, 4, 3, 1
+    rng, u, dr, A, Bm, Cm = _sel_inputs(T, Dc, N, G, 41)
+    dl = np.abs(dr) + 0.1
+    h0 = rng.standard_normal((Dc, N))
+    y, h = oracle.selective_scan_seq(u, dl, np.zeros((Dc, N)), Bm, Cm, h0, delta_softplus=False)
+    hs = h0[None] + np.cumsum(dl[:, :, None] * Bm[:, 0][:, None, :] * u[:, :, None], axis=0)
+    assert np.allclose(h, hs[-1], rtol=1e-13, atol=1e-13)
+    assert np.allclose(y, np.einsum("tn,tdn->td", Cm[:, 0], hs), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_selective_scan_equals_unrolled_quadratic_form(G):
+    """y_t[d] = sum_{s<=t} sum_n C_t[n] exp(A[d,n] sum_{s<r<=t} delta_r) delta_s B_s[n] u_s
+    + sum_n C_t[n] exp(A[d,n] sum_{r<=t} delta_r) h0[d,n] + D u_t, computed term by term."""
+    T, Dc, N = 6, 4, 3
+    rng, u, dr, A, Bm, Cm = _sel_inputs(T, Dc, N, G, 42 + G)
+    Dv = rng.standard_normal(Dc)
+    bias = rng.standard_normal(Dc) * 0.2
+    h0 = rng.standard_normal((Dc, N))
+    y, _ = oracle.selective_scan_seq(u, dr, A, Bm, Cm, h0, D=Dv, delta_bias=bias)
+    dl = np.log1p(np.exp(dr + bias))  # softplus
+    ref = np.zeros((T, Dc))
+    for t in range(T):
+        for d in range(Dc):
+            g = d // (Dc // G)
+            acc = Dv[d] * u[t, d]
+            for n in range(N):
+                acc += Cm[t, g, n] * math.exp(A[d, n] * dl[:t + 1, d].sum()) * h0[d, n]
+                for s in range(t + 1):
+                    acc += Cm[t, g, n] * math.exp(A[d, n] * dl[s + 1:t + 1, d].sum()) * dl[s, d] * Bm[s, g, n] * u[s, d]
+            ref[t, d] = acc
+    assert np.allclose(y, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_selective_scan_channels_are_independent():
+    T, Dc, N, G = 5, 6, 4, 1
+    rng, u, dr, A, Bm, Cm = _sel_inputs(T, Dc, N, G, 44)
+    h0 = np.zeros((Dc, N))
+    y, h = oracle.selective_scan_seq(u, dr, A, Bm, Cm, h0)
+    A2 = A.copy()
+    A2[2, 1] *= 3.0
+    u2 = u.copy()
+    u2[:, 4] += 1.0
+    y2, h2 = oracle.selective_scan_seq(u2, dr, A2, Bm, Cm, h0)
+    keep = [0, 1, 3, 5]
+    assert np.array_equal(y2[:, keep], y[:, keep]) and np.array_equal(h2[keep], h[keep])
+    assert not np.allclose(y2[:, 2], y[:, 2]) and not np.allclose(y2[:, 4], y[:, 4])
