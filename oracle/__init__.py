@@ -213,7 +213,8 @@ def selective_scan_seq(u, delta_raw, A, B, C, h0, *, D=None, z=None, delta_bias=
     T, Dc = u.shape
     A = _f64(A)
     N = A.shape[1]
-    B = _f64(B).reshape(T, -1, N)
+    B = _f64(B)
+    assert B.ndim == 3 and B.shape[0] == T and B.shape[2] == N, "B must be [T, G, N]"
     G = B.shape[1]
     assert Dc % G == 0
     h = np.array(h0, dtype=np.float64, copy=True).reshape(Dc, N)

@@ -20,6 +20,7 @@ from .configs import BF16, F32, Dims
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmamba2.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "mamba2.h")
+HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(_HERE), "include", "mamba1.h")]
 
 _DT_CODE = {F32: 0, BF16: 1}
 _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
@@ -37,6 +38,14 @@ class CDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "nheads", "headdim", "dstate", "ngroups", "conv_width", "chunk_size",
         "act_dtype", "xbc_dtype", "state_dtype", "out_dtype")]
+
+
+class CDims1(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("dim", "dstate", "ngroups", "act_dtype", "state_dtype", "out_dtype")]
+
+
+def cdims1(d) -> CDims1:
+    return CDims1(d.dim, d.dstate, d.ngroups, _DT_CODE[d.act_dtype], _DT_CODE[d.state_dtype], _DT_CODE[d.out_dtype])
 
 
 def cdims(d: Dims, xbc_dtype: Optional[str] = None) -> CDims:
@@ -78,6 +87,10 @@ _SIGS = {
                                           ctypes.c_size_t, _P]),
     "mamba2_gated_rmsnorm": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, ctypes.c_float, ctypes.c_int32, _P,
                                             ctypes.c_int64, _P]),
+    "mamba1_ssm_slot_bytes": (ctypes.c_size_t, [ctypes.POINTER(CDims1)]),
+    "mamba1_selective_scan_fwd": (ctypes.c_int, [ctypes.POINTER(CDims1), _P, _P, _P, _P, _P, _P, _P, _P,
+                                                  ctypes.c_int32, _P, _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P,
+                                                  _P]),
     "mamba2_slots_create": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(_P)]),
     "mamba2_slot_alloc": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32)]),
     "mamba2_slot_free": (ctypes.c_int, [_P, ctypes.c_int32]),
@@ -108,9 +121,9 @@ def lib():
 
 def header_functions() -> list:
     """Names of the functions declared in include/mamba2.h."""
-    text = open(HEADER_PATH).read()
+    text = "".join(open(p).read() for p in HEADER_PATHS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mamba2_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mamba[12]_[a-z0-9_]+)\s*\(", text)))
 
 
 def _check(status: int, fn: str):
@@ -341,6 +354,38 @@ def mamba2_gated_rmsnorm(d: Dims, y, z, norm_w, out, eps: float = 1e-5, group_si
     _want(out, "out", _TORCH_DT[d.out_dtype], (rows, d.d_inner))
     _check(lib().mamba2_gated_rmsnorm(ctypes.byref(cdims(d)), _ptr(y), _ptr(z), _ptr(norm_w), float(eps),
                                       int(group_size), _ptr(out), rows, _stream(stream)), "mamba2_gated_rmsnorm")
+
+
+def mamba1_ssm_slot_bytes(d) -> int:
+    return int(lib().mamba1_ssm_slot_bytes(ctypes.byref(cdims1(d))))
+
+
+def mamba1_selective_scan_fwd(d, u, delta_raw, A, B, C, D, z, delta_bias, y, ssm_pool, cu_seqlens, state_indices,
+                              has_initial_state=None, delta_softplus: bool = True, *, stream=None):
+    """Mamba-1 selective scan over packed sequences. ``d`` is a Mamba1Dims.
+    u, delta_raw, z, y [T, dim]; B, C [T, ngroups, dstate]; A [dim, dstate]; ssm_pool [slots, dim, dstate]."""
+    T = u.shape[0]
+    nseq = state_indices.shape[0]
+    act = _TORCH_DT[d.act_dtype]
+    _want(u, "u", act, (T, d.dim))
+    _want(delta_raw, "delta_raw", act, (T, d.dim))
+    _want(A, "A", torch.float32, (d.dim, d.dstate))
+    _want(B, "B", act, (T, d.ngroups, d.dstate))
+    _want(C, "C", act, (T, d.ngroups, d.dstate))
+    _want(D, "D", torch.float32, (d.dim,), optional=True)
+    _want(z, "z", act, (T, d.dim), optional=True)
+    _want(delta_bias, "delta_bias", torch.float32, (d.dim,), optional=True)
+    _want(y, "y", _TORCH_DT[d.out_dtype], (T, d.dim))
+    _want(ssm_pool, "ssm_pool", _TORCH_DT[d.state_dtype])
+    if ssm_pool.dim() != 3 or tuple(ssm_pool.shape[1:]) != (d.dim, d.dstate):
+        raise ValueError("ssm_pool must be [slots, dim, dstate]")
+    _want(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,))
+    _want(state_indices, "state_indices", torch.int32, (nseq,))
+    _want(has_initial_state, "has_initial_state", torch.uint8, (nseq,), optional=True)
+    _check(lib().mamba1_selective_scan_fwd(ctypes.byref(cdims1(d)), _ptr(u), _ptr(delta_raw), _ptr(A), _ptr(B), _ptr(C),
+                                           _ptr(D), _ptr(z), _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(y),
+                                           _ptr(ssm_pool), _ptr(cu_seqlens), nseq, T, _ptr(state_indices),
+                                           _ptr(has_initial_state), _stream(stream)), "mamba1_selective_scan_fwd")
 
 
 def mamba2_mixed_fwd(d: Dims, xbc, dt_raw, z, conv_w, conv_b, A_log, dt_bias, D, xbc_post, y, ssm_pool, conv_pool,

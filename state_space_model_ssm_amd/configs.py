@@ -66,6 +66,26 @@ NEMOTRON_H_8B_MAMBA_LAYERS = 48
 
 
 @dataclass(frozen=True)
+class Mamba1Dims:
+    """Mamba-1 selective scan: ``dim`` channels, ``dstate`` states per channel,
+    ``ngroups`` groups sharing B/C (1 in the Mamba paper's layer)."""
+    dim: int
+    dstate: int
+    ngroups: int = 1
+    act_dtype: str = BF16
+    state_dtype: str = F32
+    out_dtype: str = BF16
+
+    def with_(self, **kw) -> "Mamba1Dims":
+        return replace(self, **kw)
+
+
+#: Selective scan with d_inner equal to the Nemotron-H-8B x width (8192) and
+#: 16 states per channel, the Mamba paper's default state size.
+MAMBA1_8K = Mamba1Dims(dim=8192, dstate=16)
+
+
+@dataclass(frozen=True)
 class Workload:
     name: str
     dims: Dims

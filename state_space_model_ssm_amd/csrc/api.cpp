@@ -2,6 +2,7 @@
 // HIP kernels on the caller's stream, and the host-side slot allocator.
 // Nothing here allocates device memory, synchronises or memsets.
 #include "../../include/mamba2.h"
+#include "../../include/mamba1.h"
 
 #include <hip/hip_runtime.h>
 
@@ -378,6 +379,56 @@ int mamba2_prefill_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw
     if (norm_w && total_tokens > 0)
         return mamba2_gated_rmsnorm(d, y, z, norm_w, norm_eps, norm_group, y, total_tokens, stream);
     return ok();
+}
+
+// ------------------------------------------------------------ Mamba-1 selective scan
+namespace {
+
+int check_sel(const mamba1_dims *d) {
+    if (!d) return fail(MAMBA2_ERR_INVALID_ARG, "dims is NULL");
+    if (d->dim <= 0 || d->dstate <= 0 || d->ngroups <= 0)
+        return fail(MAMBA2_ERR_INVALID_ARG, "dims must be positive (Dc=%d N=%d G=%d)", d->dim, d->dstate, d->ngroups);
+    if (d->dim % d->ngroups != 0)
+        return fail(MAMBA2_ERR_INVALID_ARG, "dim (%d) must be a multiple of ngroups (%d)", d->dim, d->ngroups);
+    if (!valid_dtype(d->act_dtype) || !valid_dtype(d->state_dtype) || !valid_dtype(d->out_dtype))
+        return fail(MAMBA2_ERR_INVALID_ARG, "unknown dtype code");
+    m2::SelShape s{d->dim, d->dstate, d->ngroups, d->act_dtype, d->state_dtype, d->out_dtype};
+    if (!m2::selective_scan_supported(s))
+        return fail(MAMBA2_ERR_UNSUPPORTED,
+                    "selective scan supports dstate in {4, 8, 16} with dim/ngroups a multiple of 64/128/256 (Dc=%d "
+                    "N=%d G=%d)", d->dim, d->dstate, d->ngroups);
+    return MAMBA2_OK;
+}
+
+}  // namespace
+
+size_t mamba1_ssm_slot_bytes(const mamba1_dims *d) {
+    if (!d || d->dim <= 0 || d->dstate <= 0 || !valid_dtype(d->state_dtype)) return 0;
+    return (size_t)d->dim * d->dstate * dtype_bytes(d->state_dtype);
+}
+
+int mamba1_selective_scan_fwd(const mamba1_dims *d, const void *u, const void *delta_raw, const float *A,
+                              const void *B, const void *C, const float *D, const void *z, const float *delta_bias,
+                              int32_t delta_softplus, void *y, void *ssm_pool, const int32_t *cu_seqlens,
+                              int32_t nseq, int64_t total_tokens, const int32_t *state_indices,
+                              const uint8_t *has_initial_state, void *stream) {
+    int st = check_sel(d);
+    if (st) return st;
+    if (nseq < 0 || total_tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative nseq or total_tokens");
+    if (nseq == 0) {
+        if (total_tokens != 0) return fail(MAMBA2_ERR_INVALID_ARG, "tokens without sequences");
+        return ok();
+    }
+    REQUIRE_PTR(A); OPT_PTR(D); OPT_PTR(delta_bias); REQUIRE_PTR(ssm_pool);
+    REQUIRE_IDX(cu_seqlens); REQUIRE_IDX(state_indices);
+    if (total_tokens > 0) {
+        REQUIRE_PTR(u); REQUIRE_PTR(delta_raw); REQUIRE_PTR(B); REQUIRE_PTR(C); OPT_PTR(z); REQUIRE_PTR(y);
+        if (y == u || y == delta_raw || (z && y == z)) return fail(MAMBA2_ERR_INVALID_ARG, "y must not alias inputs");
+    }
+    m2::SelShape s{d->dim, d->dstate, d->ngroups, d->act_dtype, d->state_dtype, d->out_dtype};
+    m2::SelScanArgs a{u, delta_raw, A, B, C, D, z, delta_bias, delta_softplus ? 1 : 0, y, ssm_pool, cu_seqlens,
+                      state_indices, has_initial_state, nseq, total_tokens};
+    return hip_status(m2::launch_selective_scan(s, a, static_cast<hipStream_t>(stream)), "selective_scan launch");
 }
 
 // ------------------------------------------------------------ slot allocator

@@ -85,8 +85,14 @@ template <typename T, int K> __device__ __forceinline__ void store_k(T *p, const
 #pragma unroll
         for (int i = 0; i < K / 8; ++i) Io<bf16>::store(p + 8 * i, in + 8 * i);
     } else {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-        for (int i = 0; i < K; ++i) p[i] = f32_to_bf16(in[i]);
+        for (int i = 0; i < K / 4; ++i) {
+            bf16x4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = f32_to_bf16(in[4 * i + j]);
+            *reinterpret_cast<bf16x4 *>(p + 4 * i) = v;  // one 8-byte store
+        }
     }
 }
 
@@ -156,6 +162,18 @@ __device__ __forceinline__ void st(void *p, int dt, int64_t i, float v) {
 
 __device__ __forceinline__ float softplus_f(float v) { return fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v))); }
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + expf(-v)); }
+// softplus(v) = max(v, 0) + log1p(exp(-|v|)) from the hardware exp2/log2, with
+// log1p(e) evaluated as log(1 + e) * e / ((1 + e) - 1), which cancels the
+// rounding of 1 + e (the classic compensated form; e itself when 1 + e rounds to
+// 1). A few fp32 ulp; for per-element use where the library softplus (a long
+// polynomial with a float64 step) would dominate the instruction count.
+__device__ __forceinline__ float softplus_fast(float v) {
+    const float e = __builtin_amdgcn_exp2f(-fabsf(v) * 1.4426950408889634f);
+    const float u = 1.0f + e;
+    const float l = (u == 1.0f) ? e : __builtin_amdgcn_logf(u) * 0.6931471805599453f * e * __builtin_amdgcn_rcpf(u - 1.0f);
+    return fmaxf(v, 0.0f) + l;
+}
+
 // SiLU from the hardware exp2 and reciprocal (each about 1 ulp): a few
 // instructions instead of the accurate exp and IEEE divide, for the per-element
 // conv outputs of prefill. Relative error of a few fp32 ulp; the limits hold

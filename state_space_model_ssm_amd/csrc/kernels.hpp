@@ -104,6 +104,28 @@ struct NormArgs {
     int64_t rows;
 };
 
+// Mamba-1 selective scan: Dc channels, N states, G groups of B/C.
+struct SelShape {
+    int Dc, N, G;
+    int act_dt, state_dt, out_dt;
+};
+
+struct SelScanArgs {
+    const void *u, *delta;       // [T][Dc] activation dtype
+    const float *A;              // [Dc][N]
+    const void *B, *C;           // [T][G][N] activation dtype
+    const float *D;              // [Dc] or null
+    const void *z;               // [T][Dc] or null
+    const float *delta_bias;     // [Dc] or null
+    int delta_softplus;
+    void *y;                     // [T][Dc] out dtype
+    void *pool;                  // [slots][Dc][N] state dtype
+    const int32_t *cu, *idx;
+    const uint8_t *has_init;
+    int nseq;
+    int64_t T;
+};
+
 // Each returns hipSuccess or the launch error. `supported` queries return
 // false for shapes outside the compiled set (no launch happens).
 bool state_update_supported(const LayerShape &s);
@@ -125,6 +147,9 @@ hipError_t launch_prefill_scan(const LayerShape &s, const PrefillArgs &a, hipStr
 
 bool gated_norm_supported(int64_t width, int gs);
 hipError_t launch_gated_norm(const NormArgs &a, int y_dt, int z_dt, int64_t width, int gs, hipStream_t st);
+
+bool selective_scan_supported(const SelShape &s);
+hipError_t launch_selective_scan(const SelShape &s, const SelScanArgs &a, hipStream_t st);
 
 bool scan_supported(const LayerShape &s);
 hipError_t launch_chunk_scan(const LayerShape &s, const ScanArgs &a, hipStream_t st);

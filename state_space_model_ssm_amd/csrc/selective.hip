@@ -1,0 +1,215 @@
+// Mamba-1 selective scan (the "selective_scan_fwd" kernel the trace page
+// "Hybrid Mamba-Transformer MoEs hide their stalls..." names for Mamba layers;
+// the recurrence is that of the Mamba paper the page cites): a diagonal state
+// per (channel d, state n) with its own decay A[d][n],
+//   delta = softplus(delta_raw + bias)        (or delta_raw + bias)
+//   h_t[d][n] = exp(delta_t[d] A[d][n]) h_{t-1}[d][n] + delta_t[d] B_t[n] u_t[d]
+//   y_t[d]    = sum_n C_t[n] h_t[d][n] + D[d] u_t[d]        (times SiLU(z_t[d]))
+// with B, C shared by the channels of a group.
+//
+// There is no dense contraction here: per state element and token it is one
+// exp and a few multiply-adds, so the bound is VALU issue (the exp runs on the
+// transcendental unit), not MFMA and not HBM (u, delta, z, y are 8 bytes per
+// channel and token against N = 16 state updates).
+//
+// Design: one workgroup per (64 channels, sequence), looping over the
+// sequence's tokens in chunks (64 tokens at N = 16):
+//   * staging: the chunk's u, delta, z of the workgroup's channels and B, C of
+//     its group are loaded cooperatively (coalesced rows) and reduced once per
+//     (token, channel) to delta, delta*u, D*u and the gate, in LDS;
+//   * recurrence: each thread owns 4 states of one channel (N/4 lanes per
+//     channel) in registers, A pre-scaled by log2(e) so each step is one
+//     multiply, one exp2 and two fused multiply-adds per state; the partial
+//     C.h sums are combined across the channel's lanes with DPP quad moves;
+//   * the chunk's y tile is written to LDS and stored as coalesced rows.
+// The state stays in registers for the whole sequence; only the initial and
+// final states touch the pool.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace m2 {
+
+// Sum over aligned groups of G consecutive lanes (G = 1, 2, 4), every lane of the
+// group ending with the total. DPP quad permutations move values within quads of
+// lanes as ordinary VALU operations (no LDS crossbar, no wait): [1,0,3,2] swaps
+// neighbours, [2,3,0,1] swaps pairs.
+template <int G> __device__ __forceinline__ float lane_group_sum(float v) {
+    static_assert(G == 1 || G == 2 || G == 4, "lane groups of 1, 2 or 4");
+    if constexpr (G >= 2)
+        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    if constexpr (G >= 4)
+        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+    return v;
+}
+
+template <int N, typename AT, typename ST, typename OT>
+__global__ __launch_bounds__(256) void selective_scan_kernel(SelScanArgs a, int Dc, int G) {
+    constexpr int LPC = N / 4;          // lanes per channel (4 states each)
+    constexpr int CH = 256 / LPC;       // channels per workgroup
+    constexpr int TT = 16 * LPC;        // tokens per chunk (LDS stays ~70 KB for every N)
+    constexpr int CS = CH + 4;          // row stride of the per-token channel arrays (floats)
+    constexpr float LOG2E = 1.4426950408889634f;
+    static_assert(N % 4 == 0 && LPC >= 1 && LPC <= 16, "dstate must be a multiple of 4, at most 64");
+
+    __shared__ __attribute__((aligned(16))) float sDl[TT][CS];   // delta
+    __shared__ __attribute__((aligned(16))) float sDu[TT][CS];   // delta * u; then y of the chunk
+    __shared__ __attribute__((aligned(16))) float sSk[TT][CS];   // D * u
+    __shared__ __attribute__((aligned(16))) float sGt[TT][CS];   // SiLU(z) or 1
+    __shared__ __attribute__((aligned(16))) float sB[TT][N];
+    __shared__ __attribute__((aligned(16))) float sC[TT][N];
+
+    const int tid = threadIdx.x;
+    const int cblk = blockIdx.x, seq = blockIdx.y;
+    const int c0 = cblk * CH;                 // first channel of the workgroup
+    const int g = c0 / (Dc / G);              // its group (CH divides Dc / G)
+    const int64_t start = a.cu[seq], end = a.cu[seq + 1];
+    const int slot = a.idx[seq];
+    OT *y = static_cast<OT *>(a.y);
+
+    if (slot < 0) {
+        for (int64_t i = tid; i < (end - start) * CH; i += 256) {
+            const int64_t t = start + i / CH;
+            Io<OT>::put(y, t * Dc + c0 + (int)(i % CH), 0.0f);
+        }
+        return;
+    }
+
+    // recurrence role: channel cl of the workgroup, states [n0, n0 + 4)
+    const int cl = tid / LPC, sg = tid % LPC, n0 = 4 * sg;
+    const int ch = c0 + cl;
+    float A2[4], h[4];
+    load_k<float, 4>(a.A + (int64_t)ch * N + n0, A2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) A2[j] *= LOG2E;
+    ST *hp = static_cast<ST *>(a.pool) + ((int64_t)slot * Dc + ch) * N + n0;
+    const bool init = a.has_init && a.has_init[seq];
+    if (init) load_k<ST, 4>(hp, h);
+    else
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = 0.0f;
+
+    // staging role: token row sr, channels [4 * sc, 4 * sc + 4) of the workgroup
+    constexpr int SC = CH / 4;             // 4-channel pieces per token row
+    constexpr int SR = 256 / SC;           // token rows per staging pass
+    const int sc = tid % SC, sr0 = tid / SC;
+    float bias[4], Dv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        bias[j] = a.delta_bias ? a.delta_bias[c0 + 4 * sc + j] : 0.0f;
+        Dv[j] = a.D ? a.D[c0 + 4 * sc + j] : 0.0f;
+    }
+    const AT *uin = static_cast<const AT *>(a.u);
+    const AT *din = static_cast<const AT *>(a.delta);
+    const AT *zin = static_cast<const AT *>(a.z);
+    const AT *bin = static_cast<const AT *>(a.B);
+    const AT *cin = static_cast<const AT *>(a.C);
+
+    for (int64_t t0 = start; t0 < end; t0 += TT) {
+        const int cl_n = (int)((end - t0) < TT ? (end - t0) : TT);
+        // ---------------- stage the chunk
+        for (int r = sr0; r < TT; r += SR) {
+            float dl[4], du[4], sk[4], gt[4];
+            if (r < cl_n) {
+                const int64_t off = (t0 + r) * Dc + c0 + 4 * sc;
+                float uu[4], dd[4];
+                load_k<AT, 4>(uin + off, uu);
+                load_k<AT, 4>(din + off, dd);
+                if (zin) load_k<AT, 4>(zin + off, gt);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float v = dd[j] + bias[j];
+                    if (a.delta_softplus) v = softplus_fast(v);
+                    dl[j] = v;
+                    du[j] = v * uu[j];
+                    sk[j] = Dv[j] * uu[j];
+                    gt[j] = zin ? silu_fast(gt[j]) : 1.0f;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dl[j] = du[j] = sk[j] = gt[j] = 0.0f;
+            }
+            *reinterpret_cast<f32x4 *>(&sDl[r][4 * sc]) = f32x4{dl[0], dl[1], dl[2], dl[3]};
+            *reinterpret_cast<f32x4 *>(&sDu[r][4 * sc]) = f32x4{du[0], du[1], du[2], du[3]};
+            *reinterpret_cast<f32x4 *>(&sSk[r][4 * sc]) = f32x4{sk[0], sk[1], sk[2], sk[3]};
+            *reinterpret_cast<f32x4 *>(&sGt[r][4 * sc]) = f32x4{gt[0], gt[1], gt[2], gt[3]};
+        }
+        for (int k = tid; k < TT * (N / 4) * 2; k += 256) {
+            const int which = k / (TT * (N / 4)), rem = k % (TT * (N / 4)), r = rem / (N / 4), q4 = rem % (N / 4);
+            float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (r < cl_n) load_k<AT, 4>((which ? cin : bin) + ((t0 + r) * G + g) * N + 4 * q4, v);
+            *reinterpret_cast<f32x4 *>(which ? &sC[r][4 * q4] : &sB[r][4 * q4]) = f32x4{v[0], v[1], v[2], v[3]};
+        }
+        __syncthreads();
+
+        // ---------------- recurrence over the chunk
+#pragma unroll 4
+        for (int t = 0; t < cl_n; ++t) {
+            const float dl = sDl[t][cl], du = sDu[t][cl];
+            const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&sB[t][n0]);
+            const f32x4 c4 = *reinterpret_cast<const f32x4 *>(&sC[t][n0]);
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                h[j] = __builtin_amdgcn_exp2f(dl * A2[j]) * h[j] + du * b4[j];
+                acc += c4[j] * h[j];
+            }
+            acc = lane_group_sum<LPC>(acc);
+            if (sg == 0) sDu[t][cl] = (acc + sSk[t][cl]) * sGt[t][cl];
+        }
+        __syncthreads();
+
+        // ---------------- store the y tile (rows of CH channels)
+        for (int r = sr0; r < cl_n; r += SR) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(&sDu[r][4 * sc]);
+            const float o[4] = {v[0], v[1], v[2], v[3]};
+            store_k<OT, 4>(y + (t0 + r) * Dc + c0 + 4 * sc, o);
+        }
+        __syncthreads();
+    }
+    Io<ST>::put(hp, 0, h[0]);
+    Io<ST>::put(hp, 1, h[1]);
+    Io<ST>::put(hp, 2, h[2]);
+    Io<ST>::put(hp, 3, h[3]);
+}
+
+template <int N, typename AT, typename ST, typename OT>
+static hipError_t launch_sel_t(const SelShape &s, const SelScanArgs &a, hipStream_t stream) {
+    constexpr int CH = 256 / (N / 4);
+    dim3 grid(s.Dc / CH, a.nseq);
+    hipLaunchKernelGGL((selective_scan_kernel<N, AT, ST, OT>), grid, dim3(256), 0, stream, a, s.Dc, s.G);
+    return hipGetLastError();
+}
+
+template <int N, typename AT, typename ST>
+static hipError_t launch_sel_o(const SelShape &s, const SelScanArgs &a, hipStream_t stream) {
+    return s.out_dt == DT_BF16 ? launch_sel_t<N, AT, ST, bf16>(s, a, stream)
+                               : launch_sel_t<N, AT, ST, float>(s, a, stream);
+}
+
+template <int N, typename AT>
+static hipError_t launch_sel_s(const SelShape &s, const SelScanArgs &a, hipStream_t stream) {
+    return s.state_dt == DT_BF16 ? launch_sel_o<N, AT, bf16>(s, a, stream) : launch_sel_o<N, AT, float>(s, a, stream);
+}
+
+template <int N>
+static hipError_t launch_sel_a(const SelShape &s, const SelScanArgs &a, hipStream_t stream) {
+    return s.act_dt == DT_BF16 ? launch_sel_s<N, bf16>(s, a, stream) : launch_sel_s<N, float>(s, a, stream);
+}
+
+bool selective_scan_supported(const SelShape &s) {
+    if (!(s.N == 4 || s.N == 8 || s.N == 16)) return false;
+    const int ch = 256 / (s.N / 4);
+    return s.G > 0 && s.Dc % s.G == 0 && (s.Dc / s.G) % ch == 0;
+}
+
+hipError_t launch_selective_scan(const SelShape &s, const SelScanArgs &a, hipStream_t stream) {
+    if (a.nseq == 0) return hipSuccess;
+    switch (s.N) {
+        case 4: return launch_sel_a<4>(s, a, stream);
+        case 8: return launch_sel_a<8>(s, a, stream);
+        case 16: return launch_sel_a<16>(s, a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace m2

@@ -174,3 +174,35 @@ def stack_layer(dims: Dims, seed: int, layer: int, concurrency: int, steps: int)
     params = layer_params(dims, rng)
     tok = tokens(dims, rng, concurrency + steps - 1, with_z=False)
     return {"params": params, **tok}
+
+
+def mamba1_batch(d, seed: int, seqlens, num_slots: int, with_z: bool = True, initial_state: bool = False):
+    """Packed sequences for the Mamba-1 selective scan (``d`` a Mamba1Dims).
+
+    u, z ~ N(0, 1); delta_raw ~ N(0, 0.5); delta_bias = softplus^-1(logU[1e-3, 0.1]) per
+    channel; A[c][n] = -(n + 1) * exp(N(0, 0.1^2)) (the S4D-real initialisation of the Mamba
+    paper, perturbed per channel); B, C ~ N(0, 1) / sqrt(dstate) per token and group;
+    D = 1 + N(0, 0.1^2); initial states ~ N(0, 0.1). Activations are rounded to act_dtype.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    Dc, N, G = d.dim, d.dstate, d.ngroups
+    seqlens = np.asarray(seqlens, dtype=np.int64)
+    cu = np.zeros(len(seqlens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(seqlens)
+    T = int(cu[-1])
+    A = (-(np.arange(1, N + 1, dtype=np.float64))[None, :] * np.exp(0.1 * rng.standard_normal((Dc, N)))).astype(np.float32)
+    delta_bias = _softplus_inv(_log_uniform(rng, 1e-3, 0.1, Dc)).astype(np.float32)
+    Dv = (1.0 + _normal(rng, (Dc,), std=0.1)).astype(np.float32)
+    u = round_to_dtype(_normal(rng, (T, Dc)), d.act_dtype)
+    delta_raw = round_to_dtype(_normal(rng, (T, Dc), std=math.sqrt(0.5)), d.act_dtype)
+    Bm = round_to_dtype(_normal(rng, (T, G, N), std=1.0 / math.sqrt(N)), d.act_dtype)
+    Cm = round_to_dtype(_normal(rng, (T, G, N), std=1.0 / math.sqrt(N)), d.act_dtype)
+    z = round_to_dtype(_normal(rng, (T, Dc)), d.act_dtype) if with_z else None
+    slots = slot_ids(rng, num_slots, len(seqlens))
+    pool = np.full((num_slots, Dc, N), SENTINEL, dtype=np.float32)
+    if initial_state:
+        for sl in slots.tolist():
+            pool[sl] = round_to_dtype(_normal(rng, (Dc, N), std=math.sqrt(0.1)), d.state_dtype)
+    his = np.full(len(seqlens), 1 if initial_state else 0, dtype=np.uint8)
+    return {"u": u, "delta_raw": delta_raw, "A": A, "B": Bm, "C": Cm, "D": Dv, "z": z, "delta_bias": delta_bias,
+            "cu_seqlens": cu, "slots": slots, "has_initial_state": his, "ssm_pool": pool}
