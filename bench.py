@@ -388,7 +388,7 @@ def main():
                         "step = mamba2_prefill_fwd (B/C conv pass + fused conv/scan kernel + conv cache update)",
             "roofline": {"bound": "hbm", "kernel": "mamba2_prefill_fwd (whole call)", "achieved": round(pre_gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(pre_gbs / HBM_PEAK_GBS, 4),
-                         "traffic": profiled_traffic("prefill_scan_kernel"),
+                         "traffic": profiled_traffic("mamba2_prefill_fwd"),
                          "algorithmic_bytes_per_launch": pb, "algorithmic_flops_per_launch": pf,
                          "mfma_achieved_tflops": round(pre_tfs, 2),
                          "mfma_frac": round(pre_tfs / MFMA_BF16_PEAK_TFLOPS, 4)},
@@ -443,7 +443,8 @@ def main():
             "value": round(T1 / (ms_sel * 1e-3), 1), "unit": "tok/s", "ms_per_step": round(ms_sel, 4),
             "roofline": {"bound": "alu", "kernel": "selective_scan_kernel", "achieved": round(sel_tfs, 2),
                          "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(sel_tfs / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
+                         "frac": round(sel_tfs / FP32_VECTOR_PEAK_TFLOPS, 4),
+                         "traffic": profiled_traffic("selective_scan_kernel"),
                          "algorithmic_flops_per_launch": sel_flops, "exp_per_launch": elems,
                          "algorithmic_bytes_per_launch": sel_bytes,
                          "hbm_achieved_gbs": round(sel_bytes / (ms_sel * 1e-3) / 1e9, 1)},
