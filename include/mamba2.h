@@ -186,9 +186,12 @@ int mamba2_state_update_multi(const mamba2_dims *dims, const void *xbc, const vo
                               void *stream);
 
 /* Mixed batch ([TRT-LLM] mixed prefill+decode iterations): the prefill
- * segment (packed by cu_seqlens) runs conv1d_fwd + chunk_scan_fwd, the
- * decode segment (`decode_batch` rows, one token each) runs conv1d_update +
- * state_update, all on `stream` with no host synchronisation.
+ * segment (packed by cu_seqlens) runs conv1d_fwd + chunk_scan_fwd, or
+ * mamba2_prefill_fwd when `workspace` holds at least
+ * mamba2_prefill_workspace_bytes(total_tokens) (then xbc_post rows
+ * [0, total_tokens) are not written); the decode segment (`decode_batch`
+ * rows, one token each) runs conv1d_update + state_update, all on `stream`
+ * with no host synchronisation.
  *   xbc/dt_raw/z/y hold prefill tokens in rows [0, total_tokens) and decode
  *   rows in rows [total_tokens, total_tokens + decode_batch);
  *   xbc_post [total_tokens + decode_batch][Cdim] xbc_dtype receives the conv output.

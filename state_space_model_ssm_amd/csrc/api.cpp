@@ -246,13 +246,24 @@ int mamba2_mixed_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw, 
     const int64_t cdim = s.cdim(), hp = (int64_t)s.H * s.P;
     const size_t ab = dtype_bytes(d->act_dtype), xb = dtype_bytes(d->xbc_dtype), ob = dtype_bytes(d->out_dtype);
     if (nseq > 0) {
-        st = mamba2_conv1d_fwd(d, xbc, conv_w, conv_b, xbc_post, conv_pool, cu_seqlens, nseq, total_tokens,
-                               prefill_indices, has_initial_state, stream);
+        size_t need = 0;
+        st = mamba2_prefill_workspace_bytes(d, total_tokens, &need);
         if (st) return st;
-        st = mamba2_chunk_scan_fwd(d, xbc_post, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, cu_seqlens, nseq,
-                                   total_tokens, prefill_indices, has_initial_state, workspace, workspace_bytes,
-                                   stream);
-        if (st) return st;
+        if (workspace && workspace_bytes >= need && total_tokens > 0) {
+            // whole prefill in one call (fused for the Nemotron head shape); xbc_post rows of the
+            // prefill segment are not written
+            st = mamba2_prefill_fwd(d, xbc, dt_raw, z, conv_w, conv_b, A_log, dt_bias, D, nullptr, 0.0f, 0, y,
+                                    ssm_pool, conv_pool, cu_seqlens, nseq, total_tokens, prefill_indices,
+                                    has_initial_state, workspace, workspace_bytes, stream);
+            if (st) return st;
+        } else {
+            st = mamba2_conv1d_fwd(d, xbc, conv_w, conv_b, xbc_post, conv_pool, cu_seqlens, nseq, total_tokens,
+                                   prefill_indices, has_initial_state, stream);
+            if (st) return st;
+            st = mamba2_chunk_scan_fwd(d, xbc_post, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, cu_seqlens, nseq,
+                                       total_tokens, prefill_indices, has_initial_state, nullptr, 0, stream);
+            if (st) return st;
+        }
     }
     if (decode_batch > 0) {
         REQUIRE_PTR(xbc); REQUIRE_PTR(dt_raw); REQUIRE_PTR(xbc_post); REQUIRE_PTR(y);

@@ -194,3 +194,36 @@ def test_fused_full_size_sampled():
     for seq in range(4):
         e = int(cu[seq + 1])
         assert np.array_equal(host(conv[int(w["slots"][seq])]), w["xbc"][e - 3:e].astype(np.float64))
+
+
+def test_mixed_batch_through_fused_prefill():
+    """mamba2_mixed_fwd with a prefill workspace: the prefill segment runs mamba2_prefill_fwd
+    (fused for bf16 y), the decode rows conv1d_update + state_update, against the oracle."""
+    d = D16B
+    w = synth.mixed_batch(d, seed=28, num_prefill=3, len_lo=20, len_hi=150, decode_rows=5, num_slots=16,
+                          with_z=True)
+    pd = params_dev(w["params"])
+    T = int(w["cu_seqlens"][-1])
+    rows = T + 5
+    xbc = dev(np.concatenate([w["prefill"]["xbc"], w["decode"]["xbc"]]), d.act_dtype)
+    dt = dev(np.concatenate([w["prefill"]["dt_raw"], w["decode"]["dt_raw"]]), d.act_dtype)
+    z = dev(np.concatenate([w["prefill"]["z"], w["decode"]["z"]]), d.act_dtype)
+    ssm, conv = dev(w["ssm_pool"], d.state_dtype), dev(w["conv_pool"], d.state_dtype)
+    post = torch.empty(rows, d.conv_dim, dtype=B._TORCH_DT[d.post_dtype], device="cuda")
+    y = torch.empty(rows, d.d_inner, dtype=B._TORCH_DT[d.out_dtype], device="cuda")
+    ws = B.prefill_workspace(d, T)
+    B.mamba2_mixed_fwd(d, xbc, dt, z, pd["conv_w"], None, pd["A_log"], pd["dt_bias"], pd["D"], post, y, ssm, conv,
+                       dev_i32(w["cu_seqlens"]), dev_i32(w["prefill_slots"]), dev_u8(w["has_initial_state"]),
+                       dev_i32(w["decode_slots"]), ws)
+    torch.cuda.synchronize()
+    allslots = np.concatenate([w["prefill_slots"], w["decode_slots"]])
+    cp, sp = compact_pools(w, allslots)
+    kw = oracle_kw(d)
+    yp, _ = oracle.prefill(w["prefill"]["xbc"], w["prefill"]["dt_raw"], w["params"], w["cu_seqlens"],
+                           np.arange(3), w["has_initial_state"], cp, sp, z=w["prefill"]["z"], **kw)
+    yd, _ = oracle.decode(w["decode"]["xbc"], w["decode"]["dt_raw"], w["params"], np.arange(3, 8), cp, sp,
+                          z=w["decode"]["z"], **kw)
+    assert_close(host(y), np.concatenate([yp, yd]), d.out_dtype, "mixed y")
+    u = torch.from_numpy(allslots.astype(np.int64)).cuda()
+    assert_close(host(ssm[u]), sp, d.state_dtype, "mixed states")
+    assert np.array_equal(host(conv[u]), cp)
