@@ -450,6 +450,32 @@ def main():
                          "hbm_achieved_gbs": round(sel_bytes / (ms_sel * 1e-3) / 1e9, 1)},
         }
         del u1, dl1, B1, C1, y1, pool1
+        # one-token update: 256 rows from a 512-slot fp32 pool, in place
+        rows1, nsl1 = 256, 512
+        wd = synth.mamba1_batch(d1, seed=7, seqlens=[1] * rows1, num_slots=nsl1, with_z=False, initial_state=True)
+        ud, dld, Bd1, Cd1 = (dev(wd[k], bf) for k in ("u", "delta_raw", "B", "C"))
+        poold = dev(wd["ssm_pool"], torch.float32)
+        idxd = torch.from_numpy(wd["slots"]).cuda()
+        yd1 = torch.empty(rows1, d1.dim, dtype=bf, device="cuda")
+        del wd
+
+        def sel_dec():
+            B.mamba1_selective_state_update(d1, ud, dld, A1, Bd1, Cd1, D1, None, db1, yd1, poold, idxd)
+
+        for _ in range(3):
+            sel_dec()
+        ms_dec = time_region(sel_dec, args.steps, torch)
+        dec_bytes = rows1 * (2 * d1.dim * d1.dstate * 4 + 3 * d1.dim * 2 + 2 * d1.ngroups * d1.dstate * 2)
+        dec_gbs = dec_bytes / (ms_dec * 1e-3) / 1e9
+        log(f"mamba-1 decode: {ms_dec * 1e3:.1f} us for {rows1} rows ({rows1 / (ms_dec * 1e-3) / 1e6:.2f} M tok/s, "
+            f"{dec_gbs:.0f} GB/s)")
+        result["mamba1_scan"]["decode"] = {
+            "workload": f"one token for each of {rows1} rows from a {nsl1}-slot fp32 state pool (8192 x 16 per "
+                        "slot), in place; step = mamba1_selective_state_update",
+            "us_per_step": round(ms_dec * 1e3, 2), "tok_s": round(rows1 / (ms_dec * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": dec_bytes}}
+        del ud, dld, Bd1, Cd1, poold, yd1
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ mixed prefill + decode batch

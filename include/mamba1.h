@@ -55,6 +55,19 @@ int mamba1_selective_scan_fwd(const mamba1_dims *dims, const void *u, const void
                               int64_t total_tokens, const int32_t *state_indices,
                               const uint8_t *has_initial_state, void *stream);
 
+/* One token per row, the state read and written in place at
+ * ssm_pool[state_indices[i]] (the decode form; the in-place, index-addressed
+ * update is the one the vllm.cpp page, "The divergence", asks for). Same math
+ * and the same per-step arithmetic as mamba1_selective_scan_fwd, so T calls equal
+ * one T-token scan. u, delta_raw, z, y [batch][Dc]; B, C [batch][G][N].
+ * state_indices[i] < 0 marks a padding row (y = 0, no slot access); two rows
+ * on one slot race. */
+int mamba1_selective_state_update(const mamba1_dims *dims, const void *u, const void *delta_raw,
+                                  const float *A, const void *B, const void *C, const float *D,
+                                  const void *z, const float *delta_bias, int32_t delta_softplus,
+                                  void *y, void *ssm_pool, const int32_t *state_indices,
+                                  int32_t batch, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -91,6 +91,8 @@ _SIGS = {
     "mamba1_selective_scan_fwd": (ctypes.c_int, [ctypes.POINTER(CDims1), _P, _P, _P, _P, _P, _P, _P, _P,
                                                   ctypes.c_int32, _P, _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P,
                                                   _P]),
+    "mamba1_selective_state_update": (ctypes.c_int, [ctypes.POINTER(CDims1), _P, _P, _P, _P, _P, _P, _P, _P,
+                                                      ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P]),
     "mamba2_slots_create": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(_P)]),
     "mamba2_slot_alloc": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32)]),
     "mamba2_slot_free": (ctypes.c_int, [_P, ctypes.c_int32]),
@@ -386,6 +388,32 @@ def mamba1_selective_scan_fwd(d, u, delta_raw, A, B, C, D, z, delta_bias, y, ssm
                                            _ptr(D), _ptr(z), _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(y),
                                            _ptr(ssm_pool), _ptr(cu_seqlens), nseq, T, _ptr(state_indices),
                                            _ptr(has_initial_state), _stream(stream)), "mamba1_selective_scan_fwd")
+
+
+def mamba1_selective_state_update(d, u, delta_raw, A, B, C, D, z, delta_bias, y, ssm_pool, state_indices,
+                                  delta_softplus: bool = True, *, stream=None):
+    """One token per row of the Mamba-1 selective scan, in place at the slots.
+    u, delta_raw, z, y [batch, dim]; B, C [batch, ngroups, dstate]; ssm_pool [slots, dim, dstate]."""
+    Bd = state_indices.shape[0]
+    act = _TORCH_DT[d.act_dtype]
+    _want(u, "u", act, (Bd, d.dim))
+    _want(delta_raw, "delta_raw", act, (Bd, d.dim))
+    _want(A, "A", torch.float32, (d.dim, d.dstate))
+    _want(B, "B", act, (Bd, d.ngroups, d.dstate))
+    _want(C, "C", act, (Bd, d.ngroups, d.dstate))
+    _want(D, "D", torch.float32, (d.dim,), optional=True)
+    _want(z, "z", act, (Bd, d.dim), optional=True)
+    _want(delta_bias, "delta_bias", torch.float32, (d.dim,), optional=True)
+    _want(y, "y", _TORCH_DT[d.out_dtype], (Bd, d.dim))
+    _want(ssm_pool, "ssm_pool", _TORCH_DT[d.state_dtype])
+    if ssm_pool.dim() != 3 or tuple(ssm_pool.shape[1:]) != (d.dim, d.dstate):
+        raise ValueError("ssm_pool must be [slots, dim, dstate]")
+    _want(state_indices, "state_indices", torch.int32, (Bd,))
+    _check(lib().mamba1_selective_state_update(ctypes.byref(cdims1(d)), _ptr(u), _ptr(delta_raw), _ptr(A), _ptr(B),
+                                               _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                               1 if delta_softplus else 0, _ptr(y), _ptr(ssm_pool),
+                                               _ptr(state_indices), Bd, _stream(stream)),
+           "mamba1_selective_state_update")
 
 
 def mamba2_mixed_fwd(d: Dims, xbc, dt_raw, z, conv_w, conv_b, A_log, dt_bias, D, xbc_post, y, ssm_pool, conv_pool,

@@ -442,6 +442,24 @@ int mamba1_selective_scan_fwd(const mamba1_dims *d, const void *u, const void *d
     return hip_status(m2::launch_selective_scan(s, a, static_cast<hipStream_t>(stream)), "selective_scan launch");
 }
 
+int mamba1_selective_state_update(const mamba1_dims *d, const void *u, const void *delta_raw, const float *A,
+                                  const void *B, const void *C, const float *D, const void *z,
+                                  const float *delta_bias, int32_t delta_softplus, void *y, void *ssm_pool,
+                                  const int32_t *state_indices, int32_t batch, void *stream) {
+    int st = check_sel(d);
+    if (st) return st;
+    if (batch < 0) return fail(MAMBA2_ERR_INVALID_ARG, "batch < 0");
+    if (batch == 0) return ok();
+    REQUIRE_PTR(u); REQUIRE_PTR(delta_raw); REQUIRE_PTR(A); REQUIRE_PTR(B); REQUIRE_PTR(C); OPT_PTR(D); OPT_PTR(z);
+    OPT_PTR(delta_bias); REQUIRE_PTR(y); REQUIRE_PTR(ssm_pool); REQUIRE_IDX(state_indices);
+    if (y == u || y == delta_raw || (z && y == z)) return fail(MAMBA2_ERR_INVALID_ARG, "y must not alias inputs");
+    m2::SelShape s{d->dim, d->dstate, d->ngroups, d->act_dtype, d->state_dtype, d->out_dtype};
+    m2::SelUpdateArgs a{u, delta_raw, A, B, C, D, z, delta_bias, delta_softplus ? 1 : 0, y, ssm_pool, state_indices,
+                        batch};
+    return hip_status(m2::launch_selective_update(s, a, static_cast<hipStream_t>(stream)),
+                      "selective_state_update launch");
+}
+
 // ------------------------------------------------------------ slot allocator
 struct mamba2_slots {
     std::vector<int32_t> free_list;  // stack of free slot ids

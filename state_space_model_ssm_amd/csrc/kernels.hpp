@@ -126,6 +126,20 @@ struct SelScanArgs {
     int64_t T;
 };
 
+struct SelUpdateArgs {
+    const void *u, *delta;       // [batch][Dc]
+    const float *A;              // [Dc][N]
+    const void *B, *C;           // [batch][G][N]
+    const float *D;              // [Dc] or null
+    const void *z;               // [batch][Dc] or null
+    const float *delta_bias;     // [Dc] or null
+    int delta_softplus;
+    void *y;                     // [batch][Dc]
+    void *pool;                  // [slots][Dc][N]
+    const int32_t *idx;          // [batch]
+    int batch;
+};
+
 // Each returns hipSuccess or the launch error. `supported` queries return
 // false for shapes outside the compiled set (no launch happens).
 bool state_update_supported(const LayerShape &s);
@@ -150,6 +164,7 @@ hipError_t launch_gated_norm(const NormArgs &a, int y_dt, int z_dt, int64_t widt
 
 bool selective_scan_supported(const SelShape &s);
 hipError_t launch_selective_scan(const SelShape &s, const SelScanArgs &a, hipStream_t st);
+hipError_t launch_selective_update(const SelShape &s, const SelUpdateArgs &a, hipStream_t st);
 
 bool scan_supported(const LayerShape &s);
 hipError_t launch_chunk_scan(const LayerShape &s, const ScanArgs &a, hipStream_t st);

@@ -172,6 +172,87 @@ __global__ __launch_bounds__(256) void selective_scan_kernel(SelScanArgs a, int 
     Io<ST>::put(hp, 3, h[3]);
 }
 
+// One token per row, the state read and written in place at the row's slot
+// (the decode form of the same recurrence). Each thread owns 4 states of one
+// channel; the per-(token, channel) quantities and each state update use the
+// same arithmetic as the scan kernel above, so T single steps reproduce a
+// T-token scan bit for bit on an fp32 pool.
+template <int N, typename AT, typename ST, typename OT>
+__global__ __launch_bounds__(256) void selective_update_kernel(SelUpdateArgs a, int Dc, int G) {
+    constexpr int LPC = N / 4;
+    constexpr int CH = 256 / LPC;
+    constexpr float LOG2E = 1.4426950408889634f;
+    const int tid = threadIdx.x;
+    const int row = blockIdx.y;
+    const int cl = tid / LPC, sg = tid % LPC, n0 = 4 * sg;
+    const int ch = blockIdx.x * CH + cl;
+    const int g = (blockIdx.x * CH) / (Dc / G);
+    const int slot = a.idx[row];
+    OT *y = static_cast<OT *>(a.y);
+    if (slot < 0) {
+        if (sg == 0) Io<OT>::put(y, (int64_t)row * Dc + ch, 0.0f);
+        return;
+    }
+    const int64_t ro = (int64_t)row * Dc + ch;
+    ST *hp = static_cast<ST *>(a.pool) + ((int64_t)slot * Dc + ch) * N + n0;
+    float h[4], A2[4], b4[4], c4[4];
+    load_k<ST, 4>(hp, h);
+    load_k<float, 4>(a.A + (int64_t)ch * N + n0, A2);
+    load_k<AT, 4>(static_cast<const AT *>(a.B) + ((int64_t)row * G + g) * N + n0, b4);
+    load_k<AT, 4>(static_cast<const AT *>(a.C) + ((int64_t)row * G + g) * N + n0, c4);
+    const float uu = (float)static_cast<const AT *>(a.u)[ro];
+    float dl = (float)static_cast<const AT *>(a.delta)[ro] + (a.delta_bias ? a.delta_bias[ch] : 0.0f);
+    if (a.delta_softplus) dl = softplus_fast(dl);
+    const float du = dl * uu;
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        h[j] = __builtin_amdgcn_exp2f(dl * (A2[j] * LOG2E)) * h[j] + du * b4[j];
+        acc += c4[j] * h[j];
+    }
+    acc = lane_group_sum<LPC>(acc);
+    store_k<ST, 4>(hp, h);
+    if (sg == 0) {
+        const float sk = a.D ? a.D[ch] * uu : 0.0f;
+        const float gt = a.z ? silu_fast((float)static_cast<const AT *>(a.z)[ro]) : 1.0f;
+        Io<OT>::put(y, ro, (acc + sk) * gt);
+    }
+}
+
+template <int N, typename AT, typename ST, typename OT>
+static hipError_t launch_seu_t(const SelShape &s, const SelUpdateArgs &a, hipStream_t stream) {
+    constexpr int CH = 256 / (N / 4);
+    dim3 grid(s.Dc / CH, a.batch);
+    hipLaunchKernelGGL((selective_update_kernel<N, AT, ST, OT>), grid, dim3(256), 0, stream, a, s.Dc, s.G);
+    return hipGetLastError();
+}
+
+template <int N, typename AT, typename ST>
+static hipError_t launch_seu_o(const SelShape &s, const SelUpdateArgs &a, hipStream_t stream) {
+    return s.out_dt == DT_BF16 ? launch_seu_t<N, AT, ST, bf16>(s, a, stream)
+                               : launch_seu_t<N, AT, ST, float>(s, a, stream);
+}
+
+template <int N, typename AT>
+static hipError_t launch_seu_s(const SelShape &s, const SelUpdateArgs &a, hipStream_t stream) {
+    return s.state_dt == DT_BF16 ? launch_seu_o<N, AT, bf16>(s, a, stream) : launch_seu_o<N, AT, float>(s, a, stream);
+}
+
+template <int N>
+static hipError_t launch_seu_a(const SelShape &s, const SelUpdateArgs &a, hipStream_t stream) {
+    return s.act_dt == DT_BF16 ? launch_seu_s<N, bf16>(s, a, stream) : launch_seu_s<N, float>(s, a, stream);
+}
+
+hipError_t launch_selective_update(const SelShape &s, const SelUpdateArgs &a, hipStream_t stream) {
+    if (a.batch == 0) return hipSuccess;
+    switch (s.N) {
+        case 4: return launch_seu_a<4>(s, a, stream);
+        case 8: return launch_seu_a<8>(s, a, stream);
+        case 16: return launch_seu_a<16>(s, a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int N, typename AT, typename ST, typename OT>
 static hipError_t launch_sel_t(const SelShape &s, const SelScanArgs &a, hipStream_t stream) {
     constexpr int CH = 256 / (N / 4);

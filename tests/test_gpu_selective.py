@@ -133,3 +133,46 @@ def test_selective_scan_full_size_sampled():
                                            D=w["D"][chans], delta_bias=w["delta_bias"][chans])
         assert_close(yh[s:e, chans], yr, BF16, f"y seq {seq}")
         assert_close(host(pool[int(w["slots"][seq])][chans]), hr, F32, f"state seq {seq}")
+
+
+@pytest.mark.parametrize("dtypes", [(F32, F32, F32), (BF16, BF16, BF16)], ids=["f32", "bf16"])
+def test_selective_state_update_matches_oracle(dtypes):
+    """One token per row, in place at the slots (random permutation, one padding row)."""
+    act, state, out = dtypes
+    d = D256.with_(act_dtype=act, state_dtype=state, out_dtype=out)
+    rows = 7
+    w = synth.mamba1_batch(d, seed=55, seqlens=[1] * rows, num_slots=12, initial_state=True)
+    slots = w["slots"].copy()
+    slots[3] = -1
+    pool = dev(w["ssm_pool"], state)
+    y = torch.empty(rows, d.dim, dtype=B._TORCH_DT[out], device="cuda")
+    B.mamba1_selective_state_update(d, dev(w["u"], act), dev(w["delta_raw"], act), dev(w["A"], F32),
+                                    dev(w["B"], act), dev(w["C"], act), dev(w["D"], F32), dev(w["z"], act),
+                                    dev(w["delta_bias"], F32), y, pool, dev_i32(slots))
+    torch.cuda.synchronize()
+    y_ref, p_ref, used = oracle_sel(d, w, has_init=np.ones(rows, np.uint8), slots=slots)
+    assert_close(host(y), y_ref, out, "y")
+    assert torch.all(y[3] == 0).item()
+    assert_close(host(pool[used]), p_ref, state, "states")
+    pad = int(w["slots"][3])
+    assert np.array_equal(host(pool[pad]), w["ssm_pool"][pad].astype(np.float64))
+
+
+def test_selective_steps_equal_scan_bitwise_fp32():
+    """T one-token updates reproduce a T-token scan bit for bit (fp32 pool)."""
+    d = D256
+    T = 40
+    w = synth.mamba1_batch(d, seed=56, seqlens=[T], num_slots=2, initial_state=True)
+    y_scan, pool_scan = run_sel(d, w, has_init=np.array([1], np.uint8))
+    slot = int(w["slots"][0])
+    pool = dev(w["ssm_pool"], F32)
+    idx = dev_i32(np.array([slot], np.int32))
+    A, Dv, bias = dev(w["A"], F32), dev(w["D"], F32), dev(w["delta_bias"], F32)
+    for t in range(T):
+        yt = torch.empty(1, d.dim, device="cuda")
+        B.mamba1_selective_state_update(d, dev(w["u"][t:t + 1], F32), dev(w["delta_raw"][t:t + 1], F32), A,
+                                        dev(w["B"][t:t + 1], F32), dev(w["C"][t:t + 1], F32), Dv,
+                                        dev(w["z"][t:t + 1], F32), bias, yt, pool, idx)
+        torch.cuda.synchronize()
+        assert torch.equal(yt[0], y_scan[t]), f"y differs at token {t}"
+    assert torch.equal(pool[slot], pool_scan[slot])
