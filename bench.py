@@ -68,7 +68,10 @@ def profiled_traffic(kernel):
                 continue
             h = hashlib.sha256()
             for f in rec["sources"]:
-                h.update(open(os.path.join(ROOT, "state_space_model_ssm_amd", "csrc", f), "rb").read())
+                path_f = os.path.join(ROOT, "state_space_model_ssm_amd", "csrc", f)
+                if not os.path.exists(path_f):
+                    return None
+                h.update(open(path_f, "rb").read())
             return rec["bytes_per_launch"] if h.hexdigest()[:16] == rec["src_sha"] else None
     return None
 

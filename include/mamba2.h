@@ -206,9 +206,11 @@ int mamba2_mixed_fwd(const mamba2_dims *dims, const void *xbc, const void *dt_ra
                      void *stream);
 
 /* Workspace that mamba2_prefill_fwd needs for `total_tokens` packed tokens.
- * For the fused shape (headdim 64, dstate 128, chunk 64|128, out_dtype bf16)
- * it holds the post-conv B/C operand planes, 3*G*N bf16 per token; otherwise
- * the post-conv xBC, Cdim elements of xbc_dtype per token. */
+ * For the fused shape (headdim 64, dstate 128, out_dtype bf16) it holds the
+ * post-conv B/C operands of each 32-token block of the packed batch: C
+ * (G*N bf16 per token), B^T as hi/lo bf16 (2*G*N per token) and C.B^T
+ * (G*32 fp32 per token), each region rounded up to 256 bytes; otherwise the
+ * post-conv xBC, Cdim elements of xbc_dtype per token. */
 int mamba2_prefill_workspace_bytes(const mamba2_dims *dims, int64_t total_tokens, size_t *bytes);
 
 /* Whole prefill of the mixer's SSM core over packed sequences: conv1d + SiLU,

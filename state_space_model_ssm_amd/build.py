@@ -17,7 +17,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmamba2.so")
-SOURCES = ["api.cpp", "decode.hip", "conv.hip", "scan.hip", "prefill.hip", "norm.hip", "selective.hip"]
+SOURCES = ["api.cpp", "decode.hip", "conv.hip", "scan.hip", "fused.hip", "norm.hip", "selective.hip"]
 ARCH = "gfx950"
 
 

@@ -310,8 +310,8 @@ int mamba2_prefill_workspace_bytes(const mamba2_dims *d, int64_t total_tokens, s
     if (!bytes) return fail(MAMBA2_ERR_INVALID_ARG, "bytes is NULL");
     if (total_tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative total_tokens");
     const m2::LayerShape s = shape_of(d);
-    const size_t per_token = fused_path(d) ? (size_t)3 * s.G * s.N * 2 : (size_t)s.cdim() * dtype_bytes(d->xbc_dtype);
-    *bytes = per_token * (size_t)total_tokens;
+    *bytes = fused_path(d) ? (size_t)m2::fused_workspace_bytes(s, total_tokens)
+                           : (size_t)s.cdim() * dtype_bytes(d->xbc_dtype) * (size_t)total_tokens;
     return ok();
 }
 
@@ -371,11 +371,9 @@ int mamba2_prefill_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw
     m2::ConvFwdArgs ca{xbc, conv_w, conv_b, workspace, conv_pool, cu_seqlens, state_indices, has_initial_state, nseq,
                        total_tokens};
     if (fused_path(d)) {
-        st = hip_status(m2::launch_bc_planes(s, ca, strm), "prefill B/C conv launch");
-        if (st) return st;
-        m2::PrefillArgs pa{xbc, workspace, conv_w, conv_b, conv_pool, dt_raw, A_log, dt_bias, D, scan_z, y,
-                           ssm_pool, cu_seqlens, state_indices, has_initial_state, nseq, total_tokens};
-        st = hip_status(m2::launch_prefill_scan(s, pa, strm), "prefill scan launch");
+        m2::FusedArgs fa{xbc, conv_w, conv_b, conv_pool, dt_raw, A_log, dt_bias, D, scan_z, y, ssm_pool,
+                         cu_seqlens, state_indices, has_initial_state, nseq, total_tokens, nullptr, nullptr, nullptr};
+        st = hip_status(m2::launch_fused_prefill(s, fa, total_tokens > 0 ? workspace : nullptr, strm), "prefill launch");
         if (st) return st;
         st = hip_status(m2::launch_conv_state(s, ca, strm), "prefill conv state launch");
         if (st) return st;

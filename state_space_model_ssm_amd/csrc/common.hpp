@@ -160,6 +160,16 @@ __device__ __forceinline__ void st(void *p, int dt, int64_t i, float v) {
     else static_cast<float *>(p)[i] = v;
 }
 
+// Sequence of packed token t: the largest i with cu[i] <= t (sequences may be empty).
+__device__ __forceinline__ int find_seq(const int32_t *cu, int nseq, int64_t t) {
+    int lo = 0, hi = nseq;  // answer in [0, nseq-1]
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
 __device__ __forceinline__ float softplus_f(float v) { return fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v))); }
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + expf(-v)); }
 // softplus(v) = max(v, 0) + log1p(exp(-|v|)) from the hardware exp2/log2, with

@@ -17,36 +17,21 @@
 // The cache update runs as a second kernel after the conv (stream order),
 // because the conv reads the old cache: doing both in one grid would race.
 //
-// With BC set, the same kernel covers only the B and C channels and writes them
-// as the bf16 operand planes the fused prefill scan consumes, per token row
-// [B hi | B lo | C] (each G*N wide): hi = RNE(B), lo = RNE(B - hi), C = RNE(C).
-// Those are exactly the MFMA operands the scan would otherwise form itself, so
-// the conv of a group's B/C channels runs once instead of once per head.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace m2 {
 
-__device__ __forceinline__ int find_seq(const int32_t *cu, int nseq, int64_t t) {
-    // largest i with cu[i] <= t (sequences may be empty)
-    int lo = 0, hi = nseq;  // answer in [0, nseq-1]
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cu[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
-template <typename AT, typename ST, typename XT, int W, int TT, bool BC>
-__global__ __launch_bounds__(256) void conv_fwd_kernel(ConvFwdArgs a, int64_t cdim, int64_t cbeg, int64_t gn) {
+template <typename AT, typename ST, typename XT, int W, int TT>
+__global__ __launch_bounds__(256) void conv_fwd_kernel(ConvFwdArgs a, int64_t cdim) {
     const int cv = threadIdx.x & 63;
     const int tg = threadIdx.x >> 6;
-    const int64_t c0 = cbeg + ((int64_t)blockIdx.x * 64 + cv) * 8;
+    const int64_t c0 = ((int64_t)blockIdx.x * 64 + cv) * 8;
     const int64_t t0 = ((int64_t)blockIdx.y * 4 + tg) * TT;
     if (c0 >= cdim || t0 >= a.T) return;
     const int64_t t1 = t0 + TT < a.T ? t0 + TT : a.T;
     const AT *in = static_cast<const AT *>(a.xbc) + c0;
-    XT *out = static_cast<XT *>(a.out) + c0;  // unused with BC
+    XT *out = static_cast<XT *>(a.out) + c0;
 
     float w[8 * W];
     load_k<float, 8 * W>(a.w + c0 * W, w);
@@ -79,7 +64,7 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(ConvFwdArgs a, int64_t cd
 
     for (int64_t t = t0; t < t1; ++t) {
         if (t >= seq_end) {  // next non-empty sequence starts exactly at t
-            while (a.cu[seq + 1] <= t) ++seq;
+            while (seq + 1 < a.nseq && a.cu[seq + 1] <= t) ++seq;
             seq_start = a.cu[seq];
             seq_end = a.cu[seq + 1];
             slot = a.idx[seq];
@@ -100,23 +85,7 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(ConvFwdArgs a, int64_t cd
                 o[j] = silu_fast(v);
             }
         }
-        if constexpr (BC) {
-            bf16 *pl = static_cast<bf16 *>(a.out) + t * 3 * gn + (c0 - cbeg);
-            if (c0 - cbeg < gn) {  // B: hi and lo planes
-                float hi[8], lo[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    hi[j] = (float)f32_to_bf16(o[j]);
-                    lo[j] = o[j] - hi[j];
-                }
-                store_k<bf16, 8>(pl, hi);
-                store_k<bf16, 8>(pl + gn, lo);
-            } else {  // C: single plane, after B lo
-                store_k<bf16, 8>(pl + gn, o);
-            }
-        } else {
-            store_k<XT, 8>(out + t * cdim, o);
-        }
+        store_k<XT, 8>(out + t * cdim, o);
 #pragma unroll
         for (int k = 0; k < W - 2; ++k)
 #pragma unroll
@@ -161,27 +130,17 @@ __global__ __launch_bounds__(256) void conv_state_kernel(ConvFwdArgs a, int64_t 
     for (int k = 0; k < W - 1; ++k) store_k<ST, 8>(cache + k * cdim, nw[k]);
 }
 
-// mode 0: conv of every channel, then the cache update; mode 1: B/C planes only
-// (no cache update: the fused prefill writes the cache after its scan);
-// mode 2: the cache update alone.
+// mode 0: conv of every channel, then the cache update; mode 2: the cache update alone.
 template <typename AT, typename ST, typename XT, int W>
 static hipError_t launch_cf(const LayerShape &s, const ConvFwdArgs &a, hipStream_t stream, int mode) {
     constexpr int TT = 16;
     const int64_t cdim = s.cdim();
-    const int64_t gn = (int64_t)s.G * s.N;
-    if (a.T > 0 && mode != 2) {
-        const int64_t nch = mode == 1 ? 2 * gn : cdim;
-        dim3 grid((unsigned)((nch / 8 + 63) / 64), (unsigned)((a.T + 4 * TT - 1) / (4 * TT)));
-        if (mode == 1)
-            hipLaunchKernelGGL((conv_fwd_kernel<AT, ST, bf16, W, TT, true>), grid, dim3(256), 0, stream, a, cdim,
-                               cdim - 2 * gn, gn);
-        else
-            hipLaunchKernelGGL((conv_fwd_kernel<AT, ST, XT, W, TT, false>), grid, dim3(256), 0, stream, a, cdim,
-                               (int64_t)0, gn);
+    if (a.T > 0 && mode == 0) {
+        dim3 grid((unsigned)((cdim / 8 + 63) / 64), (unsigned)((a.T + 4 * TT - 1) / (4 * TT)));
+        hipLaunchKernelGGL((conv_fwd_kernel<AT, ST, XT, W, TT>), grid, dim3(256), 0, stream, a, cdim);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (mode == 1) return hipSuccess;
     dim3 g2((unsigned)((cdim / 8 + 255) / 256), a.nseq);
     hipLaunchKernelGGL((conv_state_kernel<AT, ST, W>), g2, dim3(256), 0, stream, a, cdim);
     return hipGetLastError();
@@ -218,11 +177,6 @@ bool conv_supported(const LayerShape &s) { return s.W >= 2 && s.W <= 4 && s.cdim
 
 hipError_t launch_conv_fwd(const LayerShape &s, const ConvFwdArgs &a, hipStream_t stream) {
     return launch_cf_a(s, a, stream, 0);
-}
-
-hipError_t launch_bc_planes(const LayerShape &s, const ConvFwdArgs &a, hipStream_t stream) {
-    if ((s.G * s.N) % 8 != 0) return hipErrorInvalidValue;
-    return launch_cf_a(s, a, stream, 1);
 }
 
 hipError_t launch_conv_state(const LayerShape &s, const ConvFwdArgs &a, hipStream_t stream) {

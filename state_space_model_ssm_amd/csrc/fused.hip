@@ -1,0 +1,681 @@
+// Fused prefill for the Nemotron-H head shape (P = 64, N = 128, y in bf16):
+// conv1d + SiLU and the chunked SSD scan in two kernels, with the x channels
+// going from raw input to y without a post-conv round trip through HBM.
+//
+// The record page ("Nemotron-H-8B-Base-8K", mixer tensors conv1d, A_log, D,
+// dt_bias, norm; section "REQUIRED KERNEL CLASS") fixes the layer's pieces;
+// the conv reading is the one the conv kernels use (last tap on the current
+// token, left context from the slot's cached raw inputs or zeros). The chunk
+// algebra is that of the chunked scan (scan.hip). Chunks here are blocks of L
+// tokens aligned to absolute token positions (block b = tokens [bL, bL + L)),
+// cut at sequence boundaries; any partition of a sequence into chunks gives
+// the same result in exact arithmetic.
+//
+// 1. prep kernel, one workgroup per (block, group): conv + SiLU of the group's
+//    B and C channels (once per group instead of once per head), written as
+//      Cp  [T][G][N] bf16, token-major, n permuted inside each 32-block so
+//          that one 16-byte read gives the k-slots of the carried-state
+//          product below,
+//      BT  [block][G][hi|lo][N][L] bf16, the B^T operand of the state update
+//          (hi = RNE(B), lo = RNE(B - hi)),
+//      CB  [block][G][L/16][L/32][64 lanes][8] fp32: C_t . B_s for the block,
+//          already in the per-lane layout of the intra-chunk MFMA operand.
+//    Rows of other sequences inside a block are harmless: the scan multiplies
+//    them by x = 0 and never stores their outputs.
+//
+// 2. scan kernel, one workgroup of four wavefronts per (sequence, head); wave
+//    w owns channels [16w, 16w + 16) of the head for the whole sequence:
+//      * the carried state H^T (N x 16 per wave) lives in MFMA accumulators;
+//        converted to bf16 in place, those registers are the A operand of
+//        the carried-state output (k-slots = the permuted n order of Cp), so
+//        H never goes through LDS;
+//      * each lane computes the conv + SiLU of its own channel for eight
+//        consecutive tokens per 32-token block: exactly the k-slots of the
+//        x operands (x dt for the output, x dt exp(lam_end - lam) as hi/lo
+//        for the state), so x never goes through LDS either;
+//      * D x is one more MFMA per t-tile, against a selector operand that
+//        holds D (hi and lo) on the diagonal;
+//      * LDS holds only what all waves share: B^T hi/lo, C and the decayed
+//        C.B^T tiles (each wave computes those of one t-tile), 64 KB, so two
+//        workgroups share a CU and overlap each other's phases;
+//      * the next block's tiles, dt and raw x are loaded into registers while
+//        the current block computes.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mfma.hpp"
+
+namespace m2 {
+
+namespace {
+
+template <typename T> __device__ __forceinline__ uint32_t ld_bits(const T *p) {
+    if constexpr (sizeof(T) == 4) return *reinterpret_cast<const uint32_t *>(p);
+    else return (uint32_t)*reinterpret_cast<const unsigned short *>(p);
+}
+template <typename T> __device__ __forceinline__ float bits_f(uint32_t v) {
+    if constexpr (sizeof(T) == 4) return __uint_as_float(v);
+    else return __uint_as_float(v << 16);
+}
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Inclusive prefix sum over the 64 lanes with DPP: shifts within rows of 16,
+// then row broadcasts of lane 15 and lane 31 (no LDS round trips).
+template <int CTRL, int ROWS> __device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, true));
+}
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+    v += dpp_f<0x111, 0xF>(v);  // row_shr:1
+    v += dpp_f<0x112, 0xF>(v);  // row_shr:2
+    v += dpp_f<0x114, 0xF>(v);  // row_shr:4
+    v += dpp_f<0x118, 0xF>(v);  // row_shr:8
+    v += dpp_f<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_f<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- prep
+template <typename AT, typename ST, int W, int L>
+__global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int G) {
+    constexpr int P = 64, N = 128;
+    constexpr int RL = L / 8;   // tokens per thread
+    constexpr int NS = N + 8;   // bf16 row stride of the token-major tiles
+    constexpr int CBS = L + 4;  // float row stride of the C.B^T tile
+    constexpr int TL = L / 16, KL = L / 32, KN = N / 32;
+    __shared__ __attribute__((aligned(16))) bf16 sB[2][L * NS];
+    __shared__ __attribute__((aligned(16))) bf16 sC[L * NS];
+    __shared__ __attribute__((aligned(16))) float sCB[L * CBS];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, q = lane >> 4;
+    const int blk = blockIdx.x, g = blockIdx.y;
+    const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N, cdim = HP + 2 * GN;
+    const int cg = tid & 31, run = tid >> 5;
+    const bool isC = cg >= 16;
+    const int n0 = 8 * (cg & 15);
+    const int64_t c0 = HP + (isC ? GN : 0) + (int64_t)g * N + n0;  // first of this thread's 8 channels
+    const int64_t t0 = (int64_t)blk * L + run * RL;
+
+    float w[8 * W], bias[8];
+    load_k<float, 8 * W>(a.conv_w + c0 * W, w);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bias[j] = a.conv_b ? a.conv_b[c0 + j] : 0.0f;
+
+    // conv + SiLU of 8 channels x RL tokens
+    const AT *in = static_cast<const AT *>(a.xbc) + c0;
+    float o[RL][8];
+#pragma unroll
+    for (int i = 0; i < RL; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[i][j] = 0.0f;
+    if (t0 < a.T) {
+        const int64_t tl = (t0 + RL < a.T ? t0 + RL : a.T) - 1;  // last token of the run
+        const int sa = find_seq(a.cu, a.nseq, t0), sb = find_seq(a.cu, a.nseq, tl);
+        if (sa == sb) {
+            // one sequence holds the whole run: every row is loaded up front, clamped into it
+            constexpr int NR = RL + W - 1;
+            const int64_t ss = a.cu[sa], se = a.cu[sa + 1];
+            const int slot = a.idx[sa];
+            float u[NR][8];
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                int64_t r = t0 - (W - 1) + i;
+                r = r < ss ? ss : (r > se - 1 ? se - 1 : r);
+                load_k<AT, 8>(in + r * cdim, u[i]);
+            }
+            if (t0 - (W - 1) < ss) {  // rows before the sequence: its cached raw inputs or zeros
+                const bool init = slot >= 0 && a.has_init && a.has_init[sa];
+                const ST *cache = static_cast<const ST *>(a.conv_pool) + (int64_t)(slot < 0 ? 0 : slot) * (W - 1) * cdim + c0;
+#pragma unroll
+                for (int i = 0; i < NR; ++i) {
+                    const int64_t d = ss - (t0 - (W - 1) + i);
+                    if (d > 0) {
+                        if (init && d <= W - 1) load_k<ST, 8>(cache + (int64_t)((W - 1) - d) * cdim, u[i]);
+                        else
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) u[i][j] = 0.0f;
+                    }
+                }
+            }
+            if (slot >= 0) {
+#pragma unroll
+                for (int i = 0; i < RL; ++i) {
+                    if (t0 + i > tl) break;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        float v = bias[j];
+#pragma unroll
+                        for (int k = 0; k < W; ++k) v += w[j * W + k] * u[i + k][j];
+                        o[i][j] = silu_fast(v);
+                    }
+                }
+            }
+        } else {
+            // a sequence boundary inside the run: token by token, restarting the window
+            int seq = sa;
+            int64_t seq_start = a.cu[seq], seq_end = a.cu[seq + 1];
+            int slot = a.idx[seq];
+            float win[W - 1][8];
+            auto fill_window = [&](int64_t t) {
+                const bool init = slot >= 0 && a.has_init && a.has_init[seq];
+                const ST *cache = static_cast<const ST *>(a.conv_pool) + (int64_t)(slot < 0 ? 0 : slot) * (W - 1) * cdim + c0;
+#pragma unroll
+                for (int k = 0; k < W - 1; ++k) {
+                    const int64_t src = t - (W - 1) + k;
+                    if (src >= seq_start) load_k<AT, 8>(in + src * cdim, win[k]);
+                    else if (init) load_k<ST, 8>(cache + (int64_t)((W - 1) - (seq_start - src)) * cdim, win[k]);
+                    else
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) win[k][j] = 0.0f;
+                }
+            };
+            fill_window(t0);
+            for (int i = 0; i < RL && t0 + i <= tl; ++i) {
+                const int64_t t = t0 + i;
+                if (t >= seq_end) {  // the next non-empty sequence starts exactly at t
+                    while (seq + 1 < a.nseq && a.cu[seq + 1] <= t) ++seq;
+                    seq_start = a.cu[seq];
+                    seq_end = a.cu[seq + 1];
+                    slot = a.idx[seq];
+                    fill_window(t);
+                }
+                float u[8];
+                load_k<AT, 8>(in + t * cdim, u);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    float v = bias[j];
+#pragma unroll
+                    for (int k = 0; k < W - 1; ++k) v += w[j * W + k] * win[k][j];
+                    v += w[j * W + W - 1] * u[j];
+                    const float r = silu_fast(v);
+#pragma unroll
+                    for (int ii = 0; ii < RL; ++ii)
+                        if (ii == i) o[ii][j] = slot >= 0 ? r : 0.0f;
+                }
+#pragma unroll
+                for (int k = 0; k < W - 2; ++k)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) win[k][j] = win[k + 1][j];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) win[W - 2][j] = u[j];
+            }
+        }
+    }
+
+    const int tl0 = run * RL;  // first token of the thread inside the block
+    if (!isC) {
+        // B: token-major hi / lo tiles (C.B^T below, and the transposed planes)
+#pragma unroll
+        for (int i = 0; i < RL; ++i) {
+            bf16x8 h, l;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                h[j] = f32_to_bf16(o[i][j]);
+                l[j] = f32_to_bf16(o[i][j] - (float)h[j]);
+            }
+            *reinterpret_cast<bf16x8 *>(&sB[0][(tl0 + i) * NS + n0]) = h;
+            *reinterpret_cast<bf16x8 *>(&sB[1][(tl0 + i) * NS + n0]) = l;
+        }
+    } else {
+        // C: natural order in LDS; permuted token-major rows in the workspace
+        bf16 *cp = static_cast<bf16 *>(a.cp) + (int64_t)g * N + (n0 & ~31);
+        const int u0 = n0 & 31;
+#pragma unroll
+        for (int i = 0; i < RL; ++i) {
+            bf16x8 c;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[j] = f32_to_bf16(o[i][j]);
+            *reinterpret_cast<bf16x8 *>(&sC[(tl0 + i) * NS + n0]) = c;
+            if (t0 + i < a.T) {
+                bf16 *row = cp + (t0 + i) * GN;
+                *reinterpret_cast<bf16x4 *>(row + perm32(u0)) = bf16x4{c[0], c[1], c[2], c[3]};
+                *reinterpret_cast<bf16x4 *>(row + perm32(u0 + 4)) = bf16x4{c[4], c[5], c[6], c[7]};
+            }
+        }
+    }
+    __syncthreads();
+
+    // B^T hi / lo planes [hl][n][L] from the token-major tiles: 16-byte pieces of 8 tokens,
+    // consecutive threads on consecutive pieces
+    {
+        constexpr int PCS = 2 * N * L / 8 / 256;
+        bf16 *bt = static_cast<bf16 *>(a.bt) + ((int64_t)blk * G + g) * (2 * N * L);
+#pragma unroll
+        for (int i = 0; i < PCS; ++i) {
+            const int id = tid + i * 256;
+            const int k = id % (L / 8), n = (id / (L / 8)) % N, hl = id / (N * L / 8);
+            bf16x8 v;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = sB[hl][(8 * k + j) * NS + n];
+            *reinterpret_cast<bf16x8 *>(bt + 8 * id) = v;
+        }
+    }
+
+    // C.B^T (B as hi + lo), rows t, columns s; every (t-tile, s-tile) pair so
+    // that the scan may load whole operand rows unconditionally.
+    for (int tt = wave; tt < TL; tt += 4) {
+        bf16x8 ca[KN];
+#pragma unroll
+        for (int kn = 0; kn < KN; ++kn) ca[kn] = *reinterpret_cast<const bf16x8 *>(&sC[(16 * tt + col) * NS + 32 * kn + 8 * q]);
+#pragma unroll
+        for (int si = 0; si < TL; ++si) {
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kn = 0; kn < KN; ++kn) {
+                const int off = (16 * si + col) * NS + 32 * kn + 8 * q;
+                acc = mma(ca[kn], *reinterpret_cast<const bf16x8 *>(&sB[0][off]), acc);
+                acc = mma(ca[kn], *reinterpret_cast<const bf16x8 *>(&sB[1][off]), acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sCB[(16 * tt + 4 * q + r) * CBS + 16 * si + col] = acc[r];
+        }
+        // the rows just written belong to this wave: a wave-level fence suffices
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float *cb = static_cast<float *>(a.cb) + (((int64_t)blk * G + g) * (TL * KL) + tt * KL) * 512 + lane * 8;
+#pragma unroll
+        for (int m = 0; m < KL; ++m) {
+            const float *src = &sCB[(16 * tt + col) * CBS + 32 * m + 8 * q];
+            *reinterpret_cast<f32x4 *>(cb + m * 512) = *reinterpret_cast<const f32x4 *>(src);
+            *reinterpret_cast<f32x4 *>(cb + m * 512 + 4) = *reinterpret_cast<const f32x4 *>(src + 4);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- scan
+template <int L, int NB, int W, typename ST, typename AT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fused_scan_kernel(FusedArgs a, int H, int G) {
+    constexpr int P = 64, N = 128, NT = 256;
+    constexpr int TL = L / 16, KL = L / 32, KN = N / 32, NTL = N / 16;
+    constexpr int BTS = L + 8;                // bf16 row stride of the B^T tiles [n][s]
+    constexpr int CS = N + 8;                 // bf16 row stride of the C tile [t][n]
+    constexpr int XR = 8 + W - 1;             // raw rows per 8-token run (with the conv context)
+    constexpr int BTP = (2 * N * L / 8) / NT; // 16-byte B^T pieces per thread
+    constexpr int CPC = (L * N / 8) / NT;     // 16-byte C pieces per thread
+    constexpr float LOG2E = 1.4426950408889634f;
+    static_assert(L == 32 || L == 64, "block of 32 or 64 tokens");
+    static_assert(BTP * NT * 8 == 2 * N * L && CPC * NT * 8 == L * N, "tile pieces divide over threads");
+
+    __shared__ __attribute__((aligned(16))) bf16 sBT[NB][2 * N * BTS];
+    __shared__ __attribute__((aligned(16))) bf16 sC[NB][L * CS];
+    __shared__ __attribute__((aligned(16))) bf16x8 sM[NB][TL * KL * 64];
+    __shared__ __attribute__((aligned(16))) float sTok[4][3][L];  // per wave: dt, lam (log2 units), state weight
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
+    const int col = lane & 15, q = lane >> 4;
+    const int head = xcd_head(blockIdx.x, H), seq = blockIdx.y;
+    const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N, cdim = HP + 2 * GN;
+    const int g = head / (H / G);
+    const int64_t start = a.cu[seq], end = a.cu[seq + 1];
+    const int slot = a.idx[seq];
+    bf16 *y = static_cast<bf16 *>(a.y);
+
+    if (slot < 0) {
+        for (int64_t i = tid; i < (end - start) * P; i += NT) y[(start + i / P) * HP + (int64_t)head * P + (i % P)] = f32_to_bf16(0.0f);
+        return;
+    }
+
+    const float A2 = -expf(a.A_log[head]) * LOG2E;  // log2 decay per unit dt
+    const float dtb = a.dt_bias[head];
+    const float Dh = a.D[head];
+    const int p = 16 * wv + col;  // this lane's channel inside the head (x operands, state column)
+    const int64_t chx = (int64_t)head * P + p;
+    const bool init = a.has_init && a.has_init[seq];
+
+    float cw[W], ctx[W - 1];
+#pragma unroll
+    for (int k = 0; k < W; ++k) cw[k] = a.conv_w[chx * W + k];
+    const float cbias = a.conv_b ? a.conv_b[chx] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < W - 1; ++k)
+        ctx[k] = init ? (float)static_cast<const ST *>(a.conv_pool)[((int64_t)slot * (W - 1) + k) * cdim + chx] : 0.0f;
+
+    // carried state: lane holds H[p][16 nt + 4q + r]
+    ST *pool_h = static_cast<ST *>(a.pool) + ((int64_t)slot * H + head) * (int64_t)P * N + (int64_t)p * N;
+    f32x4 Hacc[NTL];
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) {
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (init) load_k<ST, 4>(pool_h + 16 * nt + 4 * q, v);
+        Hacc[nt] = f32x4{v[0], v[1], v[2], v[3]};
+    }
+
+    // D x as an MFMA: column t of a 32-token block picks k-slot t with weight D (hi + lo)
+    bf16x8 Dsel[2][2];  // [hi, lo][t-tile parity]
+    {
+        const bf16 dh = f32_to_bf16(Dh), dl = f32_to_bf16(Dh - (float)dh), zero = f32_to_bf16(0.0f);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const bool on = 8 * q + j == 16 * h + col;
+                Dsel[0][h][j] = on ? dh : zero;
+                Dsel[1][h][j] = on ? dl : zero;
+            }
+    }
+
+    // ---- prefetch registers (raw bits; converted where used)
+    // The decayed C.B^T operands are split over the waves: with two t-tiles,
+    // wave w forms k-slots [4 (w & 1), 4 (w & 1) + 4) of t-tile w >> 1; with
+    // more, wave w forms all k-slots of t-tile w.
+    constexpr bool MSPLIT = TL == 2;
+    constexpr int MJ = MSPLIT ? 4 : 8;  // k-slots per lane this wave forms
+    const int ttw = MSPLIT ? (wv >> 1) : (wv < TL ? wv : TL - 1);
+    const int mj0 = MSPLIT ? 4 * (wv & 1) : 0;
+    u32x4 btr[BTP], cr[CPC];
+    f32x4 cbr[KL][MJ / 4];
+    uint32_t dtr;
+    uint32_t xr[KL][XR];
+    // Loads take a wave-uniform base plus a 32-bit unsigned byte offset per lane
+    // (the global_load scalar-base form: one vector add per load instead of
+    // 64-bit address arithmetic). Rows are clamped in offset space (offsets
+    // grow with the row), so a block at a sequence edge costs one v_med3 per
+    // load and every load stays unconditional; the values that do not belong
+    // to the sequence are replaced when staged.
+    constexpr uint32_t AS = sizeof(AT);
+    const uint32_t xrow = (uint32_t)cdim * AS;                           // bytes per xbc row
+    const uint32_t xlane = (8u * q) * xrow + col * AS;                   // this lane's run of rows, its channel
+    const uint32_t dtlane = (uint32_t)(lane < L ? lane : L - 1) * H * AS;
+    const uint32_t crow = (uint32_t)GN * 2;                              // bytes per Cp row
+    const uint32_t clane = (uint32_t)(tid / (N / 8)) * crow + 16 * (tid % (N / 8));
+    const uint32_t zrow = (uint32_t)HP * AS;                             // bytes per z row
+    const uint32_t ylane = col * (uint32_t)HP * 2 + 8 * q;               // y: row col of a t-tile, channels 4q..
+    auto prefetch = [&](int64_t b) {
+        const int64_t bL = b * L;
+        const char *btb = static_cast<const char *>(a.bt) + (b * G + g) * (int64_t)(2 * N * L * 2);
+#pragma unroll
+        for (int i = 0; i < BTP; ++i) btr[i] = *reinterpret_cast<const u32x4 *>(btb + 16u * (tid + i * NT));
+        // C rows bL + t for t <= tmax (the packed batch ends at T)
+        const int tmax = (int)(a.T - 1 - bL < L - 1 ? a.T - 1 - bL : L - 1);
+        const char *cpb = static_cast<const char *>(a.cp) + (bL * GN + (int64_t)g * N) * 2;
+        const uint32_t cmax = (uint32_t)tmax * crow + 16 * (tid % (N / 8));
+#pragma unroll
+        for (int i = 0; i < CPC; ++i)
+            cr[i] = *reinterpret_cast<const u32x4 *>(cpb + min(clane + (uint32_t)(i * (NT / (N / 8))) * crow, cmax));
+        // dt and x rows clamped into [start, end)
+        const int lo = (int)(start - bL > -W ? start - bL : -W);           // first valid row, block-relative
+        const int hi = (int)(end - 1 - bL < L + 8 ? end - 1 - bL : L + 8);  // last valid row
+        const char *dtc = static_cast<const char *>(a.dt_raw) + (bL * H + head) * AS;
+        dtr = ld_bits(reinterpret_cast<const AT *>(dtc + min(max(dtlane, (uint32_t)max(lo, 0) * H * AS), (uint32_t)hi * H * AS)));
+        // x rows from bL - (W-1): row rho at byte offset rho * xrow (+ the lane's channel)
+        const char *xc = static_cast<const char *>(a.xbc) + ((bL - (W - 1)) * cdim + (int64_t)head * P + 16 * wv) * AS;
+        const int rlo = lo + (W - 1) > 0 ? lo + (W - 1) : 0;
+        const int xlo = rlo * (int)xrow + col * AS, xhi = (hi + (W - 1)) * (int)xrow + col * AS;
+#pragma unroll
+        for (int m = 0; m < KL; ++m)
+#pragma unroll
+            for (int i = 0; i < XR; ++i) {
+                const int o = min(max((int)(xlane + (uint32_t)(32 * m + i) * xrow), xlo), xhi);
+                xr[m][i] = ld_bits(reinterpret_cast<const AT *>(xc + (uint32_t)o));
+            }
+        const char *cbb = static_cast<const char *>(a.cb) + ((b * G + g) * (int64_t)(TL * KL) + ttw * KL) * 512 * 4;
+#pragma unroll
+        for (int m = 0; m < KL; ++m)
+#pragma unroll
+            for (int h = 0; h < MJ / 4; ++h)
+                cbr[m][h] = *reinterpret_cast<const f32x4 *>(cbb + (lane * 32u + (uint32_t)(m * 2048 + 4 * mj0 + 16 * h)));
+    };
+
+    const int64_t b0 = start / L, b1 = end > start ? (end - 1) / L : b0 - 1;
+    if (b0 <= b1) prefetch(b0);
+
+    for (int64_t b = b0; b <= b1; ++b) {
+        const int buf = NB == 1 ? 0 : (int)((b - b0) & 1);
+        const int64_t bL = b * L;
+        const int lo = (int)(start - bL > 0 ? start - bL : 0);
+        const int hi = (int)(end - bL < L ? end - bL : L);
+        const int ctxlo = (int)(start - bL > -W ? start - bL : -W);  // sequence start, block-relative
+
+        Raw<AT, 4> zr[TL];
+        if (a.z) {  // gate rows of this block, clamped into the sequence at its edges
+            const char *zc = static_cast<const char *>(a.z) + (bL * HP + (int64_t)head * P + 16 * wv) * AS;
+            const uint32_t zlo = (uint32_t)lo * zrow, zhi = (uint32_t)(hi - 1) * zrow;
+#pragma unroll
+            for (int tt = 0; tt < TL; ++tt)
+                zr[tt].load(reinterpret_cast<const AT *>(
+                    zc + (min(max(col * zrow + (uint32_t)(16 * tt) * zrow, zlo), zhi) + 4 * q * AS)));
+        }
+
+        // (1) shared tiles into LDS
+        bf16 *sbt = sBT[buf];
+        bf16 *sc = sC[buf];
+#pragma unroll
+        for (int i = 0; i < BTP; ++i) {
+            const int id = tid + i * NT, n = (id / (L / 8)) % N, hl = id / (N * L / 8);
+            *reinterpret_cast<u32x4 *>(&sbt[hl * N * BTS + n * BTS + 8 * (id % (L / 8))]) = btr[i];
+        }
+#pragma unroll
+        for (int i = 0; i < CPC; ++i) {
+            const int id = tid + i * NT;
+            *reinterpret_cast<u32x4 *>(&sc[(id / (N / 8)) * CS + 8 * (id % (N / 8))]) = cr[i];
+        }
+
+        // (2) per-token arrays, every wave its own copy: dt, inclusive lam, dt exp(lam_end - lam)
+        float dec;
+        {
+            const bool ok = lane < L && lane >= lo && lane < hi;
+            const float dt = ok ? softplus_fast(bits_f<AT>(dtr) + dtb) : 0.0f;
+            const float v = wave_prefix_sum(dt * A2);
+            const float l2end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), L - 1));
+            if (lane < L) {
+                sTok[wv][0][lane] = dt;
+                sTok[wv][1][lane] = v;
+                sTok[wv][2][lane] = dt * __builtin_amdgcn_exp2f(l2end - v);
+            }
+            dec = __builtin_amdgcn_exp2f(l2end);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // (3) conv + SiLU of this lane's channel, tokens 32m + 8q + j: the k-slots of the x operands
+        bf16x8 X[KL], XD[KL], XSh[KL], XSl[KL];
+#pragma unroll
+        for (int m = 0; m < KL; ++m) {
+            float u[XR];
+#pragma unroll
+            for (int i = 0; i < XR; ++i) u[i] = bits_f<AT>(xr[m][i]);
+            if (ctxlo > 1 - W) {  // rows before the sequence: its cached context (or zeros)
+#pragma unroll
+                for (int i = 0; i < XR; ++i) {
+                    const int d = ctxlo - (32 * m + 8 * q - (W - 1) + i);
+                    if (d > 0) {
+                        float c = 0.0f;
+#pragma unroll
+                        for (int k = 0; k < W - 1; ++k) c = (d == W - 1 - k) ? ctx[k] : c;
+                        u[i] = c;
+                    }
+                }
+            }
+            const int s0 = 32 * m + 8 * q;
+            const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&sTok[wv][0][s0]);
+            const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&sTok[wv][0][s0 + 4]);
+            const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&sTok[wv][2][s0]);
+            const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&sTok[wv][2][s0 + 4]);
+            float xv[8], xd[8], xs[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float v = cbias;
+#pragma unroll
+                for (int k = 0; k < W; ++k) v += cw[k] * u[j + k];
+                const bool ok = s0 + j >= lo && s0 + j < hi;
+                const float x = ok ? silu_fast(v) : 0.0f;
+                xv[j] = x;
+                xd[j] = x * (j < 4 ? d0[j] : d1[j - 4]);
+                xs[j] = x * (j < 4 ? w0[j] : w1[j - 4]);
+            }
+            X[m] = cvt8(xv);
+            XD[m] = cvt8(xd);
+            split8(xs, XSh[m], XSl[m]);
+        }
+
+        // (4) decayed C.B^T of t-tile ttw, k-slots [mj0, mj0 + MJ): M[t][s] = CB[t][s] exp(lam_t - lam_s), s <= t
+        if (MSPLIT || wv < TL) {
+            const int t = 16 * ttw + col;
+            const float l2t = sTok[wv][1][t];
+#pragma unroll
+            for (int m = 0; m < KL; ++m) {
+                if (2 * m > ttw) break;
+                const int s0 = 32 * m + 8 * q + mj0;
+                float mv[MJ];
+#pragma unroll
+                for (int h = 0; h < MJ / 4; ++h) {
+                    const f32x4 ls = *reinterpret_cast<const f32x4 *>(&sTok[wv][1][s0 + 4 * h]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        mv[4 * h + j] = s0 + 4 * h + j <= t ? cbr[m][h][j] * __builtin_amdgcn_exp2f(l2t - ls[j]) : 0.0f;
+                }
+                bf16 *dst = reinterpret_cast<bf16 *>(&sM[buf][(ttw * KL + m) * 64 + lane]) + mj0;
+                if constexpr (MJ == 8) *reinterpret_cast<bf16x8 *>(dst) = cvt8(mv);
+                else *reinterpret_cast<bf16x4 *>(dst) = bf16x4{f32_to_bf16(mv[0]), f32_to_bf16(mv[1]), f32_to_bf16(mv[2]), f32_to_bf16(mv[3])};
+            }
+        }
+        __syncthreads();
+
+        // (5) next block's loads (the last block reloads itself, keeping them unconditional)
+        prefetch(b < b1 ? b + 1 : b);
+
+        // (6) outputs y[t][16 wv + 4q + r] for the block's t-tiles
+        f32x4 acc[TL];
+        {
+            bf16x8 Hb[KN];
+#pragma unroll
+            for (int kn = 0; kn < KN; ++kn)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    Hb[kn][r] = f32_to_bf16(Hacc[2 * kn][r]);
+                    Hb[kn][4 + r] = f32_to_bf16(Hacc[2 * kn + 1][r]);
+                }
+#pragma unroll
+            for (int tt = 0; tt < TL; ++tt) {
+                acc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kn = 0; kn < KN; ++kn)
+                    acc[tt] = mma(Hb[kn], *reinterpret_cast<const bf16x8 *>(&sc[(16 * tt + col) * CS + 32 * kn + 8 * q]),
+                                  acc[tt]);
+                acc[tt] *= __builtin_amdgcn_exp2f(sTok[wv][1][16 * tt + col]);
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < TL; ++tt) {
+#pragma unroll
+            for (int m = 0; m < KL; ++m)
+                if (2 * m <= tt) acc[tt] = mma(XD[m], sM[buf][(tt * KL + m) * 64 + lane], acc[tt]);
+            acc[tt] = mma(X[tt / 2], Dsel[0][tt & 1], acc[tt]);
+            acc[tt] = mma(X[tt / 2], Dsel[1][tt & 1], acc[tt]);
+        }
+        {
+            char *yc = reinterpret_cast<char *>(y + bL * HP + (int64_t)head * P + 16 * wv);
+#pragma unroll
+            for (int tt = 0; tt < TL; ++tt) {
+                const int t = 16 * tt + col;
+                float o[4];
+                if (a.z) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = acc[tt][r] * silu_fast(zr[tt][r]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = acc[tt][r];
+                }
+                if (t >= lo && t < hi)
+                    *reinterpret_cast<bf16x4 *>(yc + (ylane + (uint32_t)(tt * 16) * (uint32_t)HP * 2)) =
+                        bf16x4{f32_to_bf16(o[0]), f32_to_bf16(o[1]), f32_to_bf16(o[2]), f32_to_bf16(o[3])};
+            }
+        }
+
+        // (7) carried state: H^T <- exp(lam_end) H^T + sum_s B^T[n][s] (x w)[s][p]   (3-term split)
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt) Hacc[nt] *= dec;
+#pragma unroll
+        for (int m = 0; m < KL; ++m) {
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) {
+                const int off = (16 * nt + col) * BTS + 32 * m + 8 * q;
+                const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&sbt[off]);
+                const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&sbt[N * BTS + off]);
+                Hacc[nt] = mma(bh, XSh[m], Hacc[nt]);
+                Hacc[nt] = mma(bl, XSh[m], Hacc[nt]);
+                Hacc[nt] = mma(bh, XSl[m], Hacc[nt]);
+            }
+        }
+        if constexpr (NB == 1) __syncthreads();
+    }
+
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) {
+        const float v[4] = {Hacc[nt][0], Hacc[nt][1], Hacc[nt][2], Hacc[nt][3]};
+        store_k<ST, 4>(pool_h + 16 * nt + 4 * q, v);
+    }
+}
+
+// ---------------------------------------------------------------- launch
+namespace {
+
+constexpr int kFusedL = 32;
+constexpr int kFusedNB = 2;
+
+int64_t up256(int64_t v) { return (v + 255) / 256 * 256; }
+
+struct FusedLayout {
+    int64_t nblk, cp, bt, cb, bytes;  // block count and byte offsets / total
+};
+
+FusedLayout fused_layout(const LayerShape &s, int64_t T) {
+    FusedLayout f;
+    const int64_t L = kFusedL;
+    f.nblk = (T + L - 1) / L;
+    f.cp = 0;
+    f.bt = up256(T * s.G * s.N * 2);
+    f.cb = f.bt + up256(f.nblk * s.G * 2 * s.N * L * 2);
+    f.bytes = f.cb + up256(f.nblk * s.G * L * L * 4);
+    return f;
+}
+
+template <int W, typename ST, typename AT>
+hipError_t launch_fw(const LayerShape &s, const FusedArgs &a, int64_t nblk, hipStream_t stream) {
+    if (nblk > 0) {  // no tokens (only empty sequences): the scan alone writes their states
+        hipLaunchKernelGGL((fused_prep_kernel<AT, ST, W, kFusedL>), dim3((unsigned)nblk, s.G), dim3(256), 0, stream, a,
+                           s.H, s.G);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((fused_scan_kernel<kFusedL, kFusedNB, W, ST, AT>), dim3(s.H, a.nseq), dim3(256), 0, stream, a,
+                       s.H, s.G);
+    return hipGetLastError();
+}
+
+template <typename ST, typename AT>
+hipError_t launch_fa(const LayerShape &s, const FusedArgs &a, int64_t nblk, hipStream_t stream) {
+    switch (s.W) {
+        case 2: return launch_fw<2, ST, AT>(s, a, nblk, stream);
+        case 3: return launch_fw<3, ST, AT>(s, a, nblk, stream);
+        case 4: return launch_fw<4, ST, AT>(s, a, nblk, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool prefill_fused_supported(const LayerShape &s) {
+    return s.P == 64 && s.N == 128 && s.W >= 2 && s.W <= 4 && s.out_dt == DT_BF16 && s.H % s.G == 0;
+}
+
+int64_t fused_workspace_bytes(const LayerShape &s, int64_t T) { return fused_layout(s, T).bytes; }
+
+hipError_t launch_fused_prefill(const LayerShape &s, FusedArgs a, void *workspace, hipStream_t stream) {
+    if (a.nseq == 0) return hipSuccess;
+    const FusedLayout f = fused_layout(s, a.T);
+    char *ws = static_cast<char *>(workspace);
+    a.cp = ws ? ws + f.cp : nullptr;
+    a.bt = ws ? ws + f.bt : nullptr;
+    a.cb = ws ? ws + f.cb : nullptr;
+    if (s.state_dt == DT_BF16)
+        return s.act_dt == DT_BF16 ? launch_fa<bf16, bf16>(s, a, f.nblk, stream) : launch_fa<bf16, float>(s, a, f.nblk, stream);
+    return s.act_dt == DT_BF16 ? launch_fa<float, bf16>(s, a, f.nblk, stream) : launch_fa<float, float>(s, a, f.nblk, stream);
+}
+
+}  // namespace m2

@@ -79,9 +79,10 @@ struct ConvMultiArgs {
     int batch, T;
 };
 
-struct PrefillArgs {
+// Fused prefill (fused.hip); cp / bt / cb are the workspace planes, set by
+// launch_fused_prefill.
+struct FusedArgs {
     const void *xbc;      // [T][Cdim] raw (pre-conv), activation dtype
-    const void *bc;       // [T][3*G*N] bf16 planes B hi | B lo | C (post-conv), from launch_bc_planes
     const float *conv_w, *conv_b;  // [Cdim][W], [Cdim] or null
     const void *conv_pool;  // [slots][W-1][Cdim], read for the context before each sequence
     const void *dt_raw;   // [T][H]
@@ -93,6 +94,7 @@ struct PrefillArgs {
     const uint8_t *has_init;
     int nseq;
     int64_t T;
+    void *cp, *bt, *cb;
 };
 
 struct NormArgs {
@@ -152,12 +154,12 @@ bool conv_supported(const LayerShape &s);
 hipError_t launch_conv_update(const LayerShape &s, const ConvUpdateArgs &a, hipStream_t st);
 hipError_t launch_conv_fwd(const LayerShape &s, const ConvFwdArgs &a, hipStream_t st);
 // B/C channels only, as bf16 planes [B hi | B lo | C] per token (a.out); no cache update
-hipError_t launch_bc_planes(const LayerShape &s, const ConvFwdArgs &a, hipStream_t st);
 // the conv cache update of launch_conv_fwd alone
 hipError_t launch_conv_state(const LayerShape &s, const ConvFwdArgs &a, hipStream_t st);
 
 bool prefill_fused_supported(const LayerShape &s);
-hipError_t launch_prefill_scan(const LayerShape &s, const PrefillArgs &a, hipStream_t st);
+int64_t fused_workspace_bytes(const LayerShape &s, int64_t T);
+hipError_t launch_fused_prefill(const LayerShape &s, FusedArgs a, void *workspace, hipStream_t st);
 
 bool gated_norm_supported(int64_t width, int gs);
 hipError_t launch_gated_norm(const NormArgs &a, int y_dt, int z_dt, int64_t width, int gs, hipStream_t st);

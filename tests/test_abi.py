@@ -129,23 +129,28 @@ def test_binding_rejects_host_tensors(lib):
 
 
 def test_prefill_workspace_and_validation_without_gpu(lib):
-    """Workspace sizing of the fused prefill (B/C operand planes, 3*G*N bf16 per token) and of
-    the unfused composition (post-conv xBC), and the errors raised before any launch."""
+    """Workspace sizing of the fused prefill (B/C operand planes per 32-token block) and of the
+    unfused composition (post-conv xBC), and the errors raised before any launch."""
     P = ctypes.c_void_p
     good = P(0x10000)
     d8 = NEMOTRON_H_8B.with_(state_dtype=F32)  # bf16 y: fused shape
-    assert B.mamba2_prefill_workspace_bytes(d8, 32768) == 32768 * 3 * 8 * 128 * 2
+    # C, B^T hi/lo (bf16) and C.B^T (fp32 per 32-token block), each region padded to 256 bytes
+    assert B.mamba2_prefill_workspace_bytes(d8, 32768) == 32768 * (3 * 8 * 128 * 2 + 8 * 32 * 4)
+    pad = lambda v: -(-v // 256) * 256
+    assert B.mamba2_prefill_workspace_bytes(d8, 33) == (pad(33 * 8 * 128 * 2) + pad(2 * 8 * 2 * 128 * 32 * 2)
+                                                        + pad(2 * 8 * 32 * 32 * 4))
     d8f = d8.with_(out_dtype=F32)  # fp32 y: conv1d_fwd + chunk_scan_fwd through the workspace
     assert B.mamba2_prefill_workspace_bytes(d8f, 100) == 100 * d8f.conv_dim * 4
     assert B.mamba2_prefill_workspace_bytes(TINY, 64) == 64 * TINY.conv_dim * 4
     args = lambda ws, nbytes, norm=None, group=0: (_cd(d8), good, good, None, good, None, good, good, good, norm,
                                                    ctypes.c_float(1e-5), group, good, good, good, good, 1, 64, good,
                                                    None, ws, nbytes, None)
-    st = lib.mamba2_prefill_fwd(*args(good, 64 * 6144 - 16))
+    need = B.mamba2_prefill_workspace_bytes(d8, 64)
+    st = lib.mamba2_prefill_fwd(*args(good, need - 16))
     assert st == B.ERR_WORKSPACE and b"workspace" in lib.mamba2_last_error()
-    st = lib.mamba2_prefill_fwd(*args(None, 64 * 6144))
+    st = lib.mamba2_prefill_fwd(*args(None, need))
     assert st == B.ERR_INVALID_ARG and b"workspace" in lib.mamba2_last_error()
-    st = lib.mamba2_prefill_fwd(*args(good, 64 * 6144, norm=good, group=100))
+    st = lib.mamba2_prefill_fwd(*args(good, need, norm=good, group=100))
     assert st == B.ERR_UNSUPPORTED
     st = lib.mamba2_gated_rmsnorm(_cd(d8), good, None, good, ctypes.c_float(1e-5), 12, good, 4, None)
     assert st == B.ERR_UNSUPPORTED  # 12 does not divide H*P = 8192

@@ -119,20 +119,29 @@ def test_gated_rmsnorm_standalone(out_dtype):
     assert_close(host(y), ref, out_dtype, "norm in place")
 
 
-def test_fused_packed_equals_separate_runs_bitwise():
+def test_fused_packing_invariance():
+    """Chunks are 32-token blocks at absolute packed positions: a sequence that starts at a
+    multiple of 32 gives bit-identical y and states whatever else is packed around it (rows of
+    other sequences in a shared block contribute exact zeros); at any other offset only the
+    chunking, hence the rounding, differs."""
     d = D16B
-    w = synth.prefill_batch(d, seed=25, seqlens=[70, 3, 129], num_slots=3, initial_state=False)
+    w = synth.prefill_batch(d, seed=25, seqlens=[64, 3, 29, 129], num_slots=4, initial_state=True)
     y_all, ssm_all, conv_all = run_fused(d, w)
     cu = w["cu_seqlens"]
-    for i in range(3):
+    for i in range(4):
         s, e = int(cu[i]), int(cu[i + 1])
         wi = {**w, "xbc": w["xbc"][s:e], "dt_raw": w["dt_raw"][s:e], "z": w["z"][s:e],
               "cu_seqlens": np.array([0, e - s], np.int32), "slots": w["slots"][i:i + 1],
               "has_initial_state": w["has_initial_state"][i:i + 1]}
         yi, ssmi, convi = run_fused(d, wi)
-        assert torch.equal(yi, y_all[s:e])
         sl = int(w["slots"][i])
-        assert torch.equal(ssmi[sl], ssm_all[sl]) and torch.equal(convi[sl], conv_all[sl])
+        assert torch.equal(convi[sl], conv_all[sl])
+        if s % 32 == 0:
+            assert torch.equal(yi, y_all[s:e]), f"sequence {i} at offset {s}"
+            assert torch.equal(ssmi[sl], ssm_all[sl])
+        else:
+            assert_close(host(yi), host(y_all[s:e]), BF16, f"y of sequence {i} at offset {s}")
+            assert_close(host(ssmi[sl]), host(ssm_all[sl]), d.state_dtype, f"state of sequence {i}")
 
 
 def test_fused_padding_and_empty_sequences():
