@@ -286,23 +286,40 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
 }
 
 // ---------------------------------------------------------------- scan
-template <int L, int NB, int W, typename ST, typename AT>
+// Per block b the loop body computes block b (carried-state output, intra-block
+// output, D x, the state update: MFMA work on LDS tiles staged one iteration
+// earlier) and stages block b + 1 (tiles into the other LDS buffer, token
+// arrays, conv + SiLU of x, decayed C.B^T: VALU work), in one instruction
+// stream so the two overlap; then it issues the loads of block b + 2 and meets
+// the other waves at the one barrier of the iteration.
+template <int L, int W, typename ST, typename AT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fused_scan_kernel(FusedArgs a, int H, int G) {
     constexpr int P = 64, N = 128, NT = 256;
     constexpr int TL = L / 16, KL = L / 32, KN = N / 32, NTL = N / 16;
-    constexpr int BTS = L + 8;                // bf16 row stride of the B^T tiles [n][s]
-    constexpr int CS = N + 8;                 // bf16 row stride of the C tile [t][n]
-    constexpr int XR = 8 + W - 1;             // raw rows per 8-token run (with the conv context)
-    constexpr int BTP = (2 * N * L / 8) / NT; // 16-byte B^T pieces per thread
-    constexpr int CPC = (L * N / 8) / NT;     // 16-byte C pieces per thread
+    constexpr int BTS = L + 8;                 // bf16 row stride of the B^T tiles [n][s]
+    constexpr int CS = N + 8;                  // bf16 row stride of the C tile [t][n]
+    constexpr int XR = 8 + W - 1;              // raw x rows behind one lane's 8 tokens
+    constexpr int XRW = L + W - 1;             // raw x rows of a block
+    constexpr uint32_t AS = sizeof(AT);
+    constexpr int XRB = 16 * AS + 8;           // bytes per row of a wave's raw x tile (its 16 channels + pad)
+    constexpr int CPR = AS;                    // 16-byte pieces per raw row of 16 channels
+    constexpr int XP = (CPR * XRW + 63) / 64;  // raw x pieces per lane
+    constexpr int BTP = (2 * N * L / 8) / NT;  // 16-byte B^T pieces per thread
+    constexpr int CPC = (L * N / 8) / NT;      // 16-byte C pieces per thread
     constexpr float LOG2E = 1.4426950408889634f;
+    // The decayed C.B^T operands are split over the waves: with two t-tiles,
+    // wave w forms k-slots [4 (w & 1), 4 (w & 1) + 4) of t-tile w >> 1; with
+    // more, wave w forms all k-slots of t-tile w.
+    constexpr bool MSPLIT = TL == 2;
+    constexpr int MJ = MSPLIT ? 4 : 8;
     static_assert(L == 32 || L == 64, "block of 32 or 64 tokens");
     static_assert(BTP * NT * 8 == 2 * N * L && CPC * NT * 8 == L * N, "tile pieces divide over threads");
 
-    __shared__ __attribute__((aligned(16))) bf16 sBT[NB][2 * N * BTS];
-    __shared__ __attribute__((aligned(16))) bf16 sC[NB][L * CS];
-    __shared__ __attribute__((aligned(16))) bf16x8 sM[NB][TL * KL * 64];
-    __shared__ __attribute__((aligned(16))) float sTok[4][3][L];  // per wave: dt, lam (log2 units), state weight
+    __shared__ __attribute__((aligned(16))) bf16 sBT[2][2 * N * BTS];
+    __shared__ __attribute__((aligned(16))) bf16 sC[2][L * CS];
+    __shared__ __attribute__((aligned(16))) bf16x8 sM[2][TL * KL * 64];
+    __shared__ __attribute__((aligned(16))) float sTok[4][3][64];  // per wave: dt, lam (log2 units), state weight
+    __shared__ __attribute__((aligned(16))) char sXr[4][XRW * XRB];  // per wave: raw x rows of its channels
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
@@ -358,60 +375,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             }
     }
 
-    // ---- prefetch registers (raw bits; converted where used)
-    // The decayed C.B^T operands are split over the waves: with two t-tiles,
-    // wave w forms k-slots [4 (w & 1), 4 (w & 1) + 4) of t-tile w >> 1; with
-    // more, wave w forms all k-slots of t-tile w.
-    constexpr bool MSPLIT = TL == 2;
-    constexpr int MJ = MSPLIT ? 4 : 8;  // k-slots per lane this wave forms
+    // ---- loads of a block into registers (raw bits, converted where used)
     const int ttw = MSPLIT ? (wv >> 1) : (wv < TL ? wv : TL - 1);
     const int mj0 = MSPLIT ? 4 * (wv & 1) : 0;
-    u32x4 btr[BTP], cr[CPC];
+    u32x4 btr[BTP], cr[CPC], xq[XP];
     f32x4 cbr[KL][MJ / 4];
     uint32_t dtr;
-    uint32_t xr[KL][XR];
     // Loads take a wave-uniform base plus a 32-bit unsigned byte offset per lane
-    // (the global_load scalar-base form: one vector add per load instead of
-    // 64-bit address arithmetic). Rows are clamped in offset space (offsets
-    // grow with the row), so a block at a sequence edge costs one v_med3 per
-    // load and every load stays unconditional; the values that do not belong
-    // to the sequence are replaced when staged.
-    constexpr uint32_t AS = sizeof(AT);
-    const uint32_t xrow = (uint32_t)cdim * AS;                           // bytes per xbc row
-    const uint32_t xlane = (8u * q) * xrow + col * AS;                   // this lane's run of rows, its channel
+    // (the global_load scalar-base form). Rows are clamped in offset space
+    // (offsets grow with the row), so a block at a sequence edge costs one
+    // v_med3 per load and every load stays unconditional; values that do not
+    // belong to the sequence are replaced when staged.
+    const uint32_t xrow = (uint32_t)cdim * AS;                  // bytes per xbc row
+    uint32_t xq_off[XP], xq_part[XP];                           // raw x piece k of this lane: row, 16-byte part
+#pragma unroll
+    for (int k = 0; k < XP; ++k) {
+        const int id = lane + 64 * k, rho = min(id / CPR, XRW - 1);
+        xq_off[k] = (uint32_t)rho * xrow;
+        xq_part[k] = 16u * (id % CPR);
+    }
     const uint32_t dtlane = (uint32_t)(lane < L ? lane : L - 1) * H * AS;
-    const uint32_t crow = (uint32_t)GN * 2;                              // bytes per Cp row
+    const uint32_t crow = (uint32_t)GN * 2;                                // bytes per Cp row
     const uint32_t clane = (uint32_t)(tid / (N / 8)) * crow + 16 * (tid % (N / 8));
-    const uint32_t zrow = (uint32_t)HP * AS;                             // bytes per z row
-    const uint32_t ylane = col * (uint32_t)HP * 2 + 8 * q;               // y: row col of a t-tile, channels 4q..
+    const uint32_t zrow = (uint32_t)HP * AS;                               // bytes per z row
+    const uint32_t ylane = col * (uint32_t)HP * 2 + 8 * q;                 // y: row col of a t-tile, channels 4q..
     auto prefetch = [&](int64_t b) {
         const int64_t bL = b * L;
         const char *btb = static_cast<const char *>(a.bt) + (b * G + g) * (int64_t)(2 * N * L * 2);
 #pragma unroll
         for (int i = 0; i < BTP; ++i) btr[i] = *reinterpret_cast<const u32x4 *>(btb + 16u * (tid + i * NT));
-        // C rows bL + t for t <= tmax (the packed batch ends at T)
-        const int tmax = (int)(a.T - 1 - bL < L - 1 ? a.T - 1 - bL : L - 1);
+        const int tmax = (int)(a.T - 1 - bL < L - 1 ? a.T - 1 - bL : L - 1);  // C rows end at T
         const char *cpb = static_cast<const char *>(a.cp) + (bL * GN + (int64_t)g * N) * 2;
         const uint32_t cmax = (uint32_t)tmax * crow + 16 * (tid % (N / 8));
 #pragma unroll
         for (int i = 0; i < CPC; ++i)
             cr[i] = *reinterpret_cast<const u32x4 *>(cpb + min(clane + (uint32_t)(i * (NT / (N / 8))) * crow, cmax));
-        // dt and x rows clamped into [start, end)
         const int lo = (int)(start - bL > -W ? start - bL : -W);           // first valid row, block-relative
         const int hi = (int)(end - 1 - bL < L + 8 ? end - 1 - bL : L + 8);  // last valid row
         const char *dtc = static_cast<const char *>(a.dt_raw) + (bL * H + head) * AS;
         dtr = ld_bits(reinterpret_cast<const AT *>(dtc + min(max(dtlane, (uint32_t)max(lo, 0) * H * AS), (uint32_t)hi * H * AS)));
-        // x rows from bL - (W-1): row rho at byte offset rho * xrow (+ the lane's channel)
+        // raw x rows bL - (W-1) + rho, rho in [0, L + W - 1), of this wave's 16 channels
         const char *xc = static_cast<const char *>(a.xbc) + ((bL - (W - 1)) * cdim + (int64_t)head * P + 16 * wv) * AS;
-        const int rlo = lo + (W - 1) > 0 ? lo + (W - 1) : 0;
-        const int xlo = rlo * (int)xrow + col * AS, xhi = (hi + (W - 1)) * (int)xrow + col * AS;
+        const uint32_t xlo = (uint32_t)(lo + (W - 1) > 0 ? lo + (W - 1) : 0) * xrow, xhi = (uint32_t)(hi + (W - 1)) * xrow;
 #pragma unroll
-        for (int m = 0; m < KL; ++m)
-#pragma unroll
-            for (int i = 0; i < XR; ++i) {
-                const int o = min(max((int)(xlane + (uint32_t)(32 * m + i) * xrow), xlo), xhi);
-                xr[m][i] = ld_bits(reinterpret_cast<const AT *>(xc + (uint32_t)o));
-            }
+        for (int k = 0; k < XP; ++k)
+            xq[k] = *reinterpret_cast<const u32x4 *>(xc + (min(max(xq_off[k], xlo), xhi) + xq_part[k]));
         const char *cbb = static_cast<const char *>(a.cb) + ((b * G + g) * (int64_t)(TL * KL) + ttw * KL) * 512 * 4;
 #pragma unroll
         for (int m = 0; m < KL; ++m)
@@ -420,27 +428,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
                 cbr[m][h] = *reinterpret_cast<const f32x4 *>(cbb + (lane * 32u + (uint32_t)(m * 2048 + 4 * mj0 + 16 * h)));
     };
 
-    const int64_t b0 = start / L, b1 = end > start ? (end - 1) / L : b0 - 1;
-    if (b0 <= b1) prefetch(b0);
-
-    for (int64_t b = b0; b <= b1; ++b) {
-        const int buf = NB == 1 ? 0 : (int)((b - b0) & 1);
+    // ---- staging of a block (from the prefetch registers) for the next iteration
+    bf16x8 X[KL], XD[KL], XSh[KL], XSl[KL];  // x, x dt, (x w) hi / lo: k-slots 32m + 8q + j of channel p
+    float el[TL], dec = 1.0f;                // exp(lam_t) for t = 16 tt + col; exp(lam_end)
+    // tiles of block b into LDS buffer buf: B^T and C (shared), raw x rows (this wave's)
+    auto stage_tiles = [&](int64_t b, int buf) {
         const int64_t bL = b * L;
-        const int lo = (int)(start - bL > 0 ? start - bL : 0);
-        const int hi = (int)(end - bL < L ? end - bL : L);
-        const int ctxlo = (int)(start - bL > -W ? start - bL : -W);  // sequence start, block-relative
-
-        Raw<AT, 4> zr[TL];
-        if (a.z) {  // gate rows of this block, clamped into the sequence at its edges
-            const char *zc = static_cast<const char *>(a.z) + (bL * HP + (int64_t)head * P + 16 * wv) * AS;
-            const uint32_t zlo = (uint32_t)lo * zrow, zhi = (uint32_t)(hi - 1) * zrow;
-#pragma unroll
-            for (int tt = 0; tt < TL; ++tt)
-                zr[tt].load(reinterpret_cast<const AT *>(
-                    zc + (min(max(col * zrow + (uint32_t)(16 * tt) * zrow, zlo), zhi) + 4 * q * AS)));
-        }
-
-        // (1) shared tiles into LDS
+        // shared tiles
         bf16 *sbt = sBT[buf];
         bf16 *sc = sC[buf];
 #pragma unroll
@@ -453,57 +447,75 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             const int id = tid + i * NT;
             *reinterpret_cast<u32x4 *>(&sc[(id / (N / 8)) * CS + 8 * (id % (N / 8))]) = cr[i];
         }
-
-        // (2) per-token arrays, every wave its own copy: dt, inclusive lam, dt exp(lam_end - lam)
-        float dec;
+        // raw x rows into this wave's tile (lanes past the last piece repeat it)
+        char *xt = sXr[wv];
+#pragma unroll
+        for (int k = 0; k < XP; ++k) {
+            const int id = min(lane + 64 * k, CPR * XRW - 1);
+            char *d = xt + (id / CPR) * XRB + 16 * (id % CPR);
+            *reinterpret_cast<uint2 *>(d) = uint2{xq[k][0], xq[k][1]};
+            *reinterpret_cast<uint2 *>(d + 8) = uint2{xq[k][2], xq[k][3]};
+        }
+        const int ctxlo = (int)(start - bL > -W ? start - bL : -W);  // sequence start, block-relative
+        if (ctxlo > 1 - W) {
+            // rows before the sequence hold its cached context (or zeros): lanes of quad 0 rewrite them
+            if (q == 0)
+                for (int rho = 0; rho < ctxlo + W - 1 && rho < XRW; ++rho) {
+                    const int d = ctxlo + W - 1 - rho;  // rows before the start
+                    float c = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < W - 1; ++k) c = (d == W - 1 - k) ? ctx[k] : c;
+                    if constexpr (AS == 4) *reinterpret_cast<float *>(xt + rho * XRB + 4 * col) = c;
+                    else *reinterpret_cast<bf16 *>(xt + rho * XRB + 2 * col) = f32_to_bf16(c);
+                }
+        }
+    };
+    // operands of block b (token arrays, conv + SiLU of x, decayed C.B^T into sM[buf])
+    auto stage_ops = [&](int64_t b, int buf) {
+        const int64_t bL = b * L;
+        const int lo = (int)(start - bL > 0 ? start - bL : 0);
+        const int hi = (int)(end - bL < L ? end - bL : L);
+        // token arrays, every wave its own copy: dt, inclusive lam, dt exp(lam_end - lam)
         {
-            const bool ok = lane < L && lane >= lo && lane < hi;
-            const float dt = ok ? softplus_fast(bits_f<AT>(dtr) + dtb) : 0.0f;
+            // (softplus for every lane, then a multiply by 0 / 1: no branch around it)
+            const float dt = softplus_fast(bits_f<AT>(dtr) + dtb) * (lane < L && lane >= lo && lane < hi ? 1.0f : 0.0f);
             const float v = wave_prefix_sum(dt * A2);
             const float l2end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), L - 1));
-            if (lane < L) {
-                sTok[wv][0][lane] = dt;
-                sTok[wv][1][lane] = v;
-                sTok[wv][2][lane] = dt * __builtin_amdgcn_exp2f(l2end - v);
-            }
+            sTok[wv][0][lane] = dt;  // lanes >= L fill padding
+            sTok[wv][1][lane] = v;
+            sTok[wv][2][lane] = dt * __builtin_amdgcn_exp2f(l2end - v);
             dec = __builtin_amdgcn_exp2f(l2end);
         }
+        const char *xt = sXr[wv];  // (rows written by this wave in the tile pass)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        // (3) conv + SiLU of this lane's channel, tokens 32m + 8q + j: the k-slots of the x operands
-        bf16x8 X[KL], XD[KL], XSh[KL], XSl[KL];
+#pragma unroll
+        for (int tt = 0; tt < TL; ++tt) el[tt] = __builtin_amdgcn_exp2f(sTok[wv][1][16 * tt + col]);
+        // conv + SiLU of this lane's channel, tokens 32m + 8q + j
 #pragma unroll
         for (int m = 0; m < KL; ++m) {
             float u[XR];
+            const char *xr0 = xt + (32 * m + 8 * q) * XRB + AS * col;
 #pragma unroll
-            for (int i = 0; i < XR; ++i) u[i] = bits_f<AT>(xr[m][i]);
-            if (ctxlo > 1 - W) {  // rows before the sequence: its cached context (or zeros)
-#pragma unroll
-                for (int i = 0; i < XR; ++i) {
-                    const int d = ctxlo - (32 * m + 8 * q - (W - 1) + i);
-                    if (d > 0) {
-                        float c = 0.0f;
-#pragma unroll
-                        for (int k = 0; k < W - 1; ++k) c = (d == W - 1 - k) ? ctx[k] : c;
-                        u[i] = c;
-                    }
-                }
+            for (int i = 0; i < XR; ++i) {
+                if constexpr (AS == 4) u[i] = *reinterpret_cast<const float *>(xr0 + i * XRB);
+                else u[i] = bits_f<AT>(*reinterpret_cast<const unsigned short *>(xr0 + i * XRB));
             }
             const int s0 = 32 * m + 8 * q;
             const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&sTok[wv][0][s0]);
             const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&sTok[wv][0][s0 + 4]);
             const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&sTok[wv][2][s0]);
             const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&sTok[wv][2][s0 + 4]);
+            // Tokens outside the sequence need no mask: their dt and state weight are 0,
+            // and their x reaches only their own (unstored) output through D x.
             float xv[8], xd[8], xs[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 float v = cbias;
 #pragma unroll
                 for (int k = 0; k < W; ++k) v += cw[k] * u[j + k];
-                const bool ok = s0 + j >= lo && s0 + j < hi;
-                const float x = ok ? silu_fast(v) : 0.0f;
+                const float x = silu_fast(v);
                 xv[j] = x;
                 xd[j] = x * (j < 4 ? d0[j] : d1[j - 4]);
                 xs[j] = x * (j < 4 ? w0[j] : w1[j - 4]);
@@ -512,14 +524,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             XD[m] = cvt8(xd);
             split8(xs, XSh[m], XSl[m]);
         }
-
-        // (4) decayed C.B^T of t-tile ttw, k-slots [mj0, mj0 + MJ): M[t][s] = CB[t][s] exp(lam_t - lam_s), s <= t
+        // decayed C.B^T of t-tile ttw, k-slots [mj0, mj0 + MJ): M[t][s] = CB[t][s] exp(lam_t - lam_s), s <= t
         if (MSPLIT || wv < TL) {
             const int t = 16 * ttw + col;
             const float l2t = sTok[wv][1][t];
 #pragma unroll
             for (int m = 0; m < KL; ++m) {
-                if (2 * m > ttw) break;
+                if (KL > 1 && 2 * m > ttw) break;  // (one 32-token block: always m = 0 <= ttw)
                 const int s0 = 32 * m + 8 * q + mj0;
                 float mv[MJ];
 #pragma unroll
@@ -534,12 +545,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
                 else *reinterpret_cast<bf16x4 *>(dst) = bf16x4{f32_to_bf16(mv[0]), f32_to_bf16(mv[1]), f32_to_bf16(mv[2]), f32_to_bf16(mv[3])};
             }
         }
+    };
+
+    const int64_t b0 = start / L, b1 = end > start ? (end - 1) / L : b0 - 1;
+    if (b0 <= b1) {
+        prefetch(b0);
+        stage_tiles(b0, 0);
+        stage_ops(b0, 0);
+        prefetch(b0 < b1 ? b0 + 1 : b0);
         __syncthreads();
+    }
 
-        // (5) next block's loads (the last block reloads itself, keeping them unconditional)
-        prefetch(b < b1 ? b + 1 : b);
+    for (int64_t b = b0; b <= b1; ++b) {
+        const int buf = (int)((b - b0) & 1);
+        const int64_t bL = b * L;
+        const int lo = (int)(start - bL > 0 ? start - bL : 0);
+        const int hi = (int)(end - bL < L ? end - bL : L);
+        // this block's staged operands (the next stage overwrites the variables)
+        bf16x8 Xc[KL], XDc[KL], XShc[KL], XSlc[KL];
+        float elc[TL];
+        const float decc = dec;
+#pragma unroll
+        for (int m = 0; m < KL; ++m) { Xc[m] = X[m]; XDc[m] = XD[m]; XShc[m] = XSh[m]; XSlc[m] = XSl[m]; }
+#pragma unroll
+        for (int tt = 0; tt < TL; ++tt) elc[tt] = el[tt];
+        const bf16 *sbt = sBT[buf];
+        const bf16 *sc = sC[buf];
 
-        // (6) outputs y[t][16 wv + 4q + r] for the block's t-tiles
+        Raw<AT, 4> zr[TL];
+        if (a.z) {  // gate rows of this block, clamped into the sequence at its edges
+            const char *zc = static_cast<const char *>(a.z) + (bL * HP + (int64_t)head * P + 16 * wv) * AS;
+            const uint32_t zlo = (uint32_t)lo * zrow, zhi = (uint32_t)(hi - 1) * zrow;
+#pragma unroll
+            for (int tt = 0; tt < TL; ++tt)
+                zr[tt].load(reinterpret_cast<const AT *>(
+                    zc + (min(max(col * zrow + (uint32_t)(16 * tt) * zrow, zlo), zhi) + 4 * q * AS)));
+        }
+
+        // tiles of the next block into the other buffer
+        stage_tiles(b < b1 ? b + 1 : b, buf ^ 1);
+
+        // carried-state output: y[t][p] = exp(lam_t) sum_n C_t[n] H[p][n]
         f32x4 acc[TL];
         {
             bf16x8 Hb[KN];
@@ -557,16 +603,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
                 for (int kn = 0; kn < KN; ++kn)
                     acc[tt] = mma(Hb[kn], *reinterpret_cast<const bf16x8 *>(&sc[(16 * tt + col) * CS + 32 * kn + 8 * q]),
                                   acc[tt]);
-                acc[tt] *= __builtin_amdgcn_exp2f(sTok[wv][1][16 * tt + col]);
             }
         }
+
+        // operands of the next block (the last block restages itself into the unused buffer)
+        stage_ops(b < b1 ? b + 1 : b, buf ^ 1);
+
+        // intra-block output and D x, then the epilogue
 #pragma unroll
         for (int tt = 0; tt < TL; ++tt) {
+            acc[tt] *= elc[tt];
 #pragma unroll
             for (int m = 0; m < KL; ++m)
-                if (2 * m <= tt) acc[tt] = mma(XD[m], sM[buf][(tt * KL + m) * 64 + lane], acc[tt]);
-            acc[tt] = mma(X[tt / 2], Dsel[0][tt & 1], acc[tt]);
-            acc[tt] = mma(X[tt / 2], Dsel[1][tt & 1], acc[tt]);
+                if (2 * m <= tt) acc[tt] = mma(XDc[m], sM[buf][(tt * KL + m) * 64 + lane], acc[tt]);
+            acc[tt] = mma(Xc[tt / 2], Dsel[0][tt & 1], acc[tt]);
+            acc[tt] = mma(Xc[tt / 2], Dsel[1][tt & 1], acc[tt]);
+        }
+        // carried state: H^T <- exp(lam_end) H^T + sum_s B^T[n][s] (x w)[s][p]   (3-term split)
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt) Hacc[nt] *= decc;
+#pragma unroll
+        for (int m = 0; m < KL; ++m) {
+#pragma unroll
+            for (int nt = 0; nt < NTL; ++nt) {
+                const int off = (16 * nt + col) * BTS + 32 * m + 8 * q;
+                const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&sbt[off]);
+                const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&sbt[N * BTS + off]);
+                Hacc[nt] = mma(bh, XShc[m], Hacc[nt]);
+                Hacc[nt] = mma(bl, XShc[m], Hacc[nt]);
+                Hacc[nt] = mma(bh, XSlc[m], Hacc[nt]);
+            }
         }
         {
             char *yc = reinterpret_cast<char *>(y + bL * HP + (int64_t)head * P + 16 * wv);
@@ -587,22 +653,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             }
         }
 
-        // (7) carried state: H^T <- exp(lam_end) H^T + sum_s B^T[n][s] (x w)[s][p]   (3-term split)
-#pragma unroll
-        for (int nt = 0; nt < NTL; ++nt) Hacc[nt] *= dec;
-#pragma unroll
-        for (int m = 0; m < KL; ++m) {
-#pragma unroll
-            for (int nt = 0; nt < NTL; ++nt) {
-                const int off = (16 * nt + col) * BTS + 32 * m + 8 * q;
-                const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&sbt[off]);
-                const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&sbt[N * BTS + off]);
-                Hacc[nt] = mma(bh, XSh[m], Hacc[nt]);
-                Hacc[nt] = mma(bl, XSh[m], Hacc[nt]);
-                Hacc[nt] = mma(bh, XSl[m], Hacc[nt]);
-            }
-        }
-        if constexpr (NB == 1) __syncthreads();
+        // loads of block b + 2 (the last blocks reload themselves, keeping the loads unconditional)
+        prefetch(b + 2 <= b1 ? b + 2 : b1);
+        __syncthreads();
     }
 
 #pragma unroll
@@ -616,7 +669,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 namespace {
 
 constexpr int kFusedL = 32;
-constexpr int kFusedNB = 2;
 
 int64_t up256(int64_t v) { return (v + 255) / 256 * 256; }
 
@@ -643,7 +695,7 @@ hipError_t launch_fw(const LayerShape &s, const FusedArgs &a, int64_t nblk, hipS
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((fused_scan_kernel<kFusedL, kFusedNB, W, ST, AT>), dim3(s.H, a.nseq), dim3(256), 0, stream, a,
+    hipLaunchKernelGGL((fused_scan_kernel<kFusedL, W, ST, AT>), dim3(s.H, a.nseq), dim3(256), 0, stream, a,
                        s.H, s.G);
     return hipGetLastError();
 }
