@@ -359,7 +359,7 @@ def main():
             conv_fwd()
             scan()
 
-        def prefill_step():  # conv of B/C to operand planes, fused conv(x) + scan, conv cache update
+        def prefill_step():  # per-group B/C prep, fused conv(x) + scan, conv cache update
             B.mamba2_prefill_fwd(d2, xbc2, dt2, None, cw2, None, A2, dtb2, D2, y2, pool2, convp2, cu2, idx2, hi2,
                                  ws2)
 
@@ -388,7 +388,8 @@ def main():
             "steps": args.prefill_steps,
             "workload": "Nemotron-H-8B layer prefill: 4 x 8192 tokens (cu_seqlens), chunk 128, bf16 inputs, "
                         "fp32 state, bf16 y, zero initial state, final conv/SSM states to pool slots; "
-                        "step = mamba2_prefill_fwd (B/C conv pass + fused conv/scan kernel + conv cache update)",
+                        "step = mamba2_prefill_fwd (per-group B/C prep kernel + fused conv/scan kernel over "
+                        "32-token blocks + conv cache update); the unfused detail runs chunk_scan_fwd at chunk 128",
             "roofline": {"bound": "hbm", "kernel": "mamba2_prefill_fwd (whole call)", "achieved": round(pre_gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(pre_gbs / HBM_PEAK_GBS, 4),
                          "traffic": profiled_traffic("mamba2_prefill_fwd"),

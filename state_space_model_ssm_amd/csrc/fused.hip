@@ -456,25 +456,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             *reinterpret_cast<uint2 *>(d) = uint2{xq[k][0], xq[k][1]};
             *reinterpret_cast<uint2 *>(d + 8) = uint2{xq[k][2], xq[k][3]};
         }
-        const int ctxlo = (int)(start - bL > -W ? start - bL : -W);  // sequence start, block-relative
-        if (ctxlo > 1 - W) {
-            // rows before the sequence hold its cached context (or zeros): lanes of quad 0 rewrite them
-            if (q == 0)
-                for (int rho = 0; rho < ctxlo + W - 1 && rho < XRW; ++rho) {
-                    const int d = ctxlo + W - 1 - rho;  // rows before the start
-                    float c = 0.0f;
-#pragma unroll
-                    for (int k = 0; k < W - 1; ++k) c = (d == W - 1 - k) ? ctx[k] : c;
-                    if constexpr (AS == 4) *reinterpret_cast<float *>(xt + rho * XRB + 4 * col) = c;
-                    else *reinterpret_cast<bf16 *>(xt + rho * XRB + 2 * col) = f32_to_bf16(c);
-                }
-        }
     };
     // operands of block b (token arrays, conv + SiLU of x, decayed C.B^T into sM[buf])
     auto stage_ops = [&](int64_t b, int buf) {
         const int64_t bL = b * L;
         const int lo = (int)(start - bL > 0 ? start - bL : 0);
         const int hi = (int)(end - bL < L ? end - bL : L);
+        const int ctxlo = (int)(start - bL > -W ? start - bL : -W);  // sequence start, block-relative
         // token arrays, every wave its own copy: dt, inclusive lam, dt exp(lam_end - lam)
         {
             // (softplus for every lane, then a multiply by 0 / 1: no branch around it)
@@ -501,6 +489,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             for (int i = 0; i < XR; ++i) {
                 if constexpr (AS == 4) u[i] = *reinterpret_cast<const float *>(xr0 + i * XRB);
                 else u[i] = bits_f<AT>(*reinterpret_cast<const unsigned short *>(xr0 + i * XRB));
+            }
+            if (ctxlo > 1 - W) {  // rows before the sequence: its cached raw inputs (or zeros), at full precision
+#pragma unroll
+                for (int i = 0; i < XR; ++i) {
+                    const int d = ctxlo - (32 * m + 8 * q - (W - 1) + i);  // rows before the start
+                    if (d > 0) {
+                        float c = 0.0f;
+#pragma unroll
+                        for (int k = 0; k < W - 1; ++k) c = (d == W - 1 - k) ? ctx[k] : c;
+                        u[i] = c;
+                    }
+                }
             }
             const int s0 = 32 * m + 8 * q;
             const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&sTok[wv][0][s0]);
