@@ -87,10 +87,19 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
     __shared__ __attribute__((aligned(16))) bf16 sB[2][L * NS];
     __shared__ __attribute__((aligned(16))) bf16 sC[L * NS];
     __shared__ __attribute__((aligned(16))) float sCB[L * CBS];
+    constexpr int kCu = 256;  // cu_seqlens entries staged in LDS for the sequence search
+    __shared__ int32_t sCu[kCu + 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, q = lane >> 4;
     const int blk = blockIdx.x, g = blockIdx.y;
+    // one coalesced load of cu_seqlens per workgroup, then searches in LDS (global
+    // binary search, one dependent load per step, past kCu sequences)
+    const bool cu_lds = a.nseq <= kCu;
+    if (cu_lds)
+        for (int i = tid; i <= a.nseq; i += 256) sCu[i] = a.cu[i];
+    __syncthreads();
+    const int32_t *cus = cu_lds ? sCu : a.cu;
     const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N, cdim = HP + 2 * GN;
     const int cg = tid & 31, run = tid >> 5;
     const bool isC = cg >= 16;
@@ -112,11 +121,11 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
         for (int j = 0; j < 8; ++j) o[i][j] = 0.0f;
     if (t0 < a.T) {
         const int64_t tl = (t0 + RL < a.T ? t0 + RL : a.T) - 1;  // last token of the run
-        const int sa = find_seq(a.cu, a.nseq, t0), sb = find_seq(a.cu, a.nseq, tl);
+        const int sa = find_seq(cus, a.nseq, t0), sb = find_seq(cus, a.nseq, tl);
         if (sa == sb) {
             // one sequence holds the whole run: every row is loaded up front, clamped into it
             constexpr int NR = RL + W - 1;
-            const int64_t ss = a.cu[sa], se = a.cu[sa + 1];
+            const int64_t ss = cus[sa], se = cus[sa + 1];
             const int slot = a.idx[sa];
             float u[NR][8];
 #pragma unroll
@@ -155,7 +164,7 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
         } else {
             // a sequence boundary inside the run: token by token, restarting the window
             int seq = sa;
-            int64_t seq_start = a.cu[seq], seq_end = a.cu[seq + 1];
+            int64_t seq_start = cus[seq], seq_end = cus[seq + 1];
             int slot = a.idx[seq];
             float win[W - 1][8];
             auto fill_window = [&](int64_t t) {
@@ -175,9 +184,9 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
             for (int i = 0; i < RL && t0 + i <= tl; ++i) {
                 const int64_t t = t0 + i;
                 if (t >= seq_end) {  // the next non-empty sequence starts exactly at t
-                    while (seq + 1 < a.nseq && a.cu[seq + 1] <= t) ++seq;
-                    seq_start = a.cu[seq];
-                    seq_end = a.cu[seq + 1];
+                    while (seq + 1 < a.nseq && cus[seq + 1] <= t) ++seq;
+                    seq_start = cus[seq];
+                    seq_end = cus[seq + 1];
                     slot = a.idx[seq];
                     fill_window(t);
                 }
@@ -255,32 +264,55 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
 
     // C.B^T (B as hi + lo), rows t, columns s; every (t-tile, s-tile) pair so
     // that the scan may load whole operand rows unconditionally.
-    for (int tt = wave; tt < TL; tt += 4) {
-        bf16x8 ca[KN];
+    float *cbg = static_cast<float *>(a.cb) + ((int64_t)blk * G + g) * (TL * KL) * 512;
+    if constexpr (TL == 2) {
+        // one 16x16 tile per wave: t-tile wave >> 1, s-tile wave & 1
+        const int tt = wave >> 1, si = wave & 1;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int kn = 0; kn < KN; ++kn) ca[kn] = *reinterpret_cast<const bf16x8 *>(&sC[(16 * tt + col) * NS + 32 * kn + 8 * q]);
-#pragma unroll
-        for (int si = 0; si < TL; ++si) {
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int kn = 0; kn < KN; ++kn) {
-                const int off = (16 * si + col) * NS + 32 * kn + 8 * q;
-                acc = mma(ca[kn], *reinterpret_cast<const bf16x8 *>(&sB[0][off]), acc);
-                acc = mma(ca[kn], *reinterpret_cast<const bf16x8 *>(&sB[1][off]), acc);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sCB[(16 * tt + 4 * q + r) * CBS + 16 * si + col] = acc[r];
+        for (int kn = 0; kn < KN; ++kn) {
+            const bf16x8 ca = *reinterpret_cast<const bf16x8 *>(&sC[(16 * tt + col) * NS + 32 * kn + 8 * q]);
+            const int off = (16 * si + col) * NS + 32 * kn + 8 * q;
+            acc = mma(ca, *reinterpret_cast<const bf16x8 *>(&sB[0][off]), acc);
+            acc = mma(ca, *reinterpret_cast<const bf16x8 *>(&sB[1][off]), acc);
         }
-        // the rows just written belong to this wave: a wave-level fence suffices
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sCB[(16 * tt + 4 * q + r) * CBS + 16 * si + col] = acc[r];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        float *cb = static_cast<float *>(a.cb) + (((int64_t)blk * G + g) * (TL * KL) + tt * KL) * 512 + lane * 8;
+        // this wave's columns are k-slots 8 qo + [0, 8) for qo in {2 si, 2 si + 1}: 16 bytes per lane
+        const int co = lane & 15, qo = 2 * si + ((lane >> 4) & 1), half = lane >> 5;
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(&sCB[(16 * tt + co) * CBS + 8 * qo + 4 * half]);
+        *reinterpret_cast<f32x4 *>(cbg + (tt * KL) * 512 + (qo * 16 + co) * 8 + 4 * half) = v;
+    } else {
+        for (int tt = wave; tt < TL; tt += 4) {
+            bf16x8 ca[KN];
 #pragma unroll
-        for (int m = 0; m < KL; ++m) {
-            const float *src = &sCB[(16 * tt + col) * CBS + 32 * m + 8 * q];
-            *reinterpret_cast<f32x4 *>(cb + m * 512) = *reinterpret_cast<const f32x4 *>(src);
-            *reinterpret_cast<f32x4 *>(cb + m * 512 + 4) = *reinterpret_cast<const f32x4 *>(src + 4);
+            for (int kn = 0; kn < KN; ++kn) ca[kn] = *reinterpret_cast<const bf16x8 *>(&sC[(16 * tt + col) * NS + 32 * kn + 8 * q]);
+#pragma unroll
+            for (int si = 0; si < TL; ++si) {
+                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kn = 0; kn < KN; ++kn) {
+                    const int off = (16 * si + col) * NS + 32 * kn + 8 * q;
+                    acc = mma(ca[kn], *reinterpret_cast<const bf16x8 *>(&sB[0][off]), acc);
+                    acc = mma(ca[kn], *reinterpret_cast<const bf16x8 *>(&sB[1][off]), acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sCB[(16 * tt + 4 * q + r) * CBS + 16 * si + col] = acc[r];
+            }
+            // the rows just written belong to this wave: a wave-level fence suffices
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            float *cb = cbg + (tt * KL) * 512 + lane * 8;
+#pragma unroll
+            for (int m = 0; m < KL; ++m) {
+                const float *src = &sCB[(16 * tt + col) * CBS + 32 * m + 8 * q];
+                *reinterpret_cast<f32x4 *>(cb + m * 512) = *reinterpret_cast<const f32x4 *>(src);
+                *reinterpret_cast<f32x4 *>(cb + m * 512 + 4) = *reinterpret_cast<const f32x4 *>(src + 4);
+            }
         }
     }
 }
