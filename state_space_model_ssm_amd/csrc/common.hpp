@@ -160,6 +160,23 @@ __device__ __forceinline__ void st(void *p, int dt, int64_t i, float v) {
     else static_cast<float *>(p)[i] = v;
 }
 
+// Sum over each aligned group of K lanes (K a power of two, 2..32), left in the
+// group's last lane (the others hold partial sums): DPP shifts inside rows of
+// 16 lanes (a window sum ending at each lane), then for K = 32 a broadcast of
+// lane 15 into the next row. VALU only, no LDS round trips.
+template <int CTRL, int ROWS> __device__ __forceinline__ float dpp_add_src(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, true));
+}
+template <int K> __device__ __forceinline__ float group_sum_last(float v) {
+    static_assert(K >= 1 && K <= 32 && (K & (K - 1)) == 0, "group of 1..32 lanes");
+    if constexpr (K >= 2) v += dpp_add_src<0x111, 0xF>(v);   // row_shr:1
+    if constexpr (K >= 4) v += dpp_add_src<0x112, 0xF>(v);   // row_shr:2
+    if constexpr (K >= 8) v += dpp_add_src<0x114, 0xF>(v);   // row_shr:4
+    if constexpr (K >= 16) v += dpp_add_src<0x118, 0xF>(v);  // row_shr:8
+    if constexpr (K >= 32) v += dpp_add_src<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    return v;
+}
+
 // Sequence of packed token t: the largest i with cu[i] <= t (sequences may be empty).
 __device__ __forceinline__ int find_seq(const int32_t *cu, int nseq, int64_t t) {
     int lo = 0, hi = nseq;  // answer in [0, nseq-1]

@@ -18,7 +18,8 @@
 //   * the state is read and written with nontemporal 16-byte accesses: each
 //     tile is touched once per step, so it should not evict reusable lines
 //     (measured: 5.0 -> 6.0 TB/s on the 256-row bf16 workload);
-//   * y[p] = sum_n C[n] h[p][n] is a butterfly over the kLpr lanes of a row;
+//   * y[p] = sum_n C[n] h[p][n] is a DPP window sum over the kLpr lanes of a row,
+//     left in the row's last lane;
 //   * B and C of the row's group and the per-head scalars are read once per
 //     lane (they hit L2: the 16 heads of a group share them);
 //   * a head's tile is split across `psplit` workgroups when rows x heads alone
@@ -98,9 +99,8 @@ __global__ __launch_bounds__(256) void state_update_kernel(StateUpdateArgs a, in
             acc += Cv[j] * s;
         }
         if (p < P) nt_store16<ST>(tile + (int64_t)p * N + n0, out);
-#pragma unroll
-        for (int m = kLpr / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-        if (lr == 0 && p < P) {
+        acc = group_sum_last<kLpr>(acc);
+        if (lr == kLpr - 1 && p < P) {
             float yv = acc + Dh * xv[it];
             if (a.z) yv *= silu_f(zg[it]);
             st(a.y, out_dt, yrow + p, yv);
@@ -221,16 +221,27 @@ __global__ __launch_bounds__(256) void state_update_multi_kernel(MultiStepArgs a
                           v);
             *reinterpret_cast<f32x4 *>(&sBC[u][which][4 * n4]) = f32x4{v[0], v[1], v[2], v[3]};
         }
-        float xv[TB][ITERS], zv[TB][ITERS], dtr[TB];
+        float xv[TB][ITERS], zv[TB][ITERS];
+        const XT *xh = static_cast<const XT *>(a.xbc) + (int64_t)row * T * cdim + (int64_t)head * P;
 #pragma unroll
-        for (int u = 0; u < TB; ++u) {
-            const int64_t r = (int64_t)row * T + min(t0 + u, T - 1);
-            dtr[u] = (float)static_cast<const AT *>(a.dt_raw)[r * H + head];
+        for (int u = 0; u < TB; ++u)
 #pragma unroll
-            for (int it = 0; it < ITERS; ++it) {
-                xv[u][it] = (float)static_cast<const XT *>(a.xbc)[r * cdim + (int64_t)head * P + pr[it]];
-                zv[u][it] = (float)zsrc[a.z ? r * HP + (int64_t)head * P + pr[it] : 0];
-            }
+            for (int it = 0; it < ITERS; ++it) xv[u][it] = (float)xh[(int64_t)min(t0 + u, T - 1) * cdim + pr[it]];
+        if (a.z) {
+            const AT *zh = zsrc + (int64_t)row * T * HP + (int64_t)head * P;
+#pragma unroll
+            for (int u = 0; u < TB; ++u)
+#pragma unroll
+                for (int it = 0; it < ITERS; ++it) zv[u][it] = (float)zh[(int64_t)min(t0 + u, T - 1) * HP + pr[it]];
+        }
+        // dt and the decay of the block's tokens: lane u of each wave computes token t0 + u,
+        // the token loop reads them back as wave-uniform values
+        float dt_l, dec_l;
+        {
+            const int u = (tid & 63) & (TB - 1);
+            const float dr = (float)static_cast<const AT *>(a.dt_raw)[((int64_t)row * T + min(t0 + u, T - 1)) * H + head];
+            dt_l = softplus_f(dr + dtb);
+            dec_l = expf(dt_l * A);
         }
         __syncthreads();
 #pragma unroll
@@ -245,8 +256,8 @@ __global__ __launch_bounds__(256) void state_update_multi_kernel(MultiStepArgs a
 #pragma unroll
                 for (int e = 0; e < 4; ++e) { Bv[j + e] = bq[e]; Cv[j + e] = cq[e]; }
             }
-            const float dt = softplus_f(dtr[u] + dtb);
-            const float decay = expf(dt * A);
+            const float dt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dt_l), u));
+            const float decay = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dec_l), u));
             const int d = a.dst ? a.dst[(int64_t)row * T + t] : -1;
 #pragma unroll
             for (int it = 0; it < ITERS; ++it) {
@@ -259,9 +270,8 @@ __global__ __launch_bounds__(256) void state_update_multi_kernel(MultiStepArgs a
                     acc += Cv[j] * h[it][j];
                 }
                 if (d >= 0 && p < P) nt_store16<ST>(pool + (int64_t)d * H * P * N + tile0 + (int64_t)p * N, h[it]);
-#pragma unroll
-                for (int m = kLpr / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-                if (lr == 0 && p < P) {
+                acc = group_sum_last<kLpr>(acc);
+                if (lr == kLpr - 1 && p < P) {
                     float yv = acc + Dh * xv[u][it];
                     if (a.z) yv *= silu_f(zv[u][it]);
                     st(a.y, out_dt, ((int64_t)row * T + t) * HP + (int64_t)head * P + p, yv);

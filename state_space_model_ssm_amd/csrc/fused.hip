@@ -61,16 +61,10 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // Inclusive prefix sum over the 64 lanes with DPP: shifts within rows of 16,
 // then row broadcasts of lane 15 and lane 31 (no LDS round trips).
-template <int CTRL, int ROWS> __device__ __forceinline__ float dpp_f(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, true));
-}
 __device__ __forceinline__ float wave_prefix_sum(float v) {
-    v += dpp_f<0x111, 0xF>(v);  // row_shr:1
-    v += dpp_f<0x112, 0xF>(v);  // row_shr:2
-    v += dpp_f<0x114, 0xF>(v);  // row_shr:4
-    v += dpp_f<0x118, 0xF>(v);  // row_shr:8
-    v += dpp_f<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-    v += dpp_f<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    v = group_sum_last<16>(v);              // window sums inside each row of 16
+    v += dpp_add_src<0x142, 0xA>(v);        // row_bcast:15 into rows 1 and 3
+    v += dpp_add_src<0x143, 0xC>(v);        // row_bcast:31 into rows 2 and 3
     return v;
 }
 
