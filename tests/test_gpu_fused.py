@@ -161,6 +161,35 @@ def test_fused_padding_and_empty_sequences():
     check_fused(d, w, has_init=has_init, slots=slots)
 
 
+def test_fused_many_short_sequences():
+    """300 sequences of 0..5 tokens packed back to back: many sequences share each 32-token
+    block, most start mid-block (conv context from the slot), and the B/C prep searches
+    cu_seqlens past the entries it stages in LDS."""
+    d = D16B.with_(nheads=8, ngroups=2)
+    rng = np.random.default_rng(31)
+    seqlens = [int(v) for v in rng.integers(0, 6, size=300)]
+    w = synth.prefill_batch(d, seed=31, seqlens=seqlens, num_slots=300, initial_state=True)
+    has_init = (rng.random(300) < 0.5).astype(np.uint8)
+    print(f"[fused] {len(seqlens)} sequences, {sum(seqlens)} tokens", flush=True)
+    check_fused(d, w, has_init=has_init)
+
+
+def test_fused_all_sequences_empty():
+    """No tokens at all: every slot still ends with its sequence's state (the initial one when
+    given, zeros otherwise) and no token row is touched."""
+    d = D16B
+    w = synth.prefill_batch(d, seed=32, seqlens=[0, 0, 0], num_slots=5, initial_state=True)
+    has_init = np.array([1, 0, 1], np.uint8)
+    y, ssm, conv = run_fused(d, w, has_init=has_init)
+    assert y.shape[0] == 0
+    for i, sl in enumerate(int(v) for v in w["slots"]):
+        if has_init[i]:
+            assert np.array_equal(host(ssm[sl]), w["ssm_pool"][sl].astype(np.float64))
+            assert np.array_equal(host(conv[sl]), w["conv_pool"][sl].astype(np.float64))
+        else:
+            assert torch.all(ssm[sl] == 0).item() and torch.all(conv[sl] == 0).item()
+
+
 def test_fused_prefill_equals_repeated_steps():
     """Equivalence contract on the fused path: the prefill of T tokens equals T one-token
     conv updates + state updates (bf16 y on both sides, fp32 state)."""
