@@ -51,8 +51,11 @@ __global__ __launch_bounds__(256) void selective_scan_kernel(SelScanArgs a, int 
     constexpr float LOG2E = 1.4426950408889634f;
     static_assert(N % 4 == 0 && LPC >= 1 && LPC <= 16, "dstate must be a multiple of 4, at most 64");
 
-    __shared__ __attribute__((aligned(16))) float sDl[TT][CS];   // delta
-    __shared__ __attribute__((aligned(16))) float sDu[TT][CS];   // delta * u; then y of the chunk
+    constexpr int TS = TT + 4;          // row stride of the per-channel token arrays (floats)
+    // delta and delta * u per channel, tokens contiguous (one 16-byte read gives a lane
+    // 4 tokens of its channel); the recurrence overwrites delta * u with the C.h sums
+    __shared__ __attribute__((aligned(16))) float sDl[CH][TS];
+    __shared__ __attribute__((aligned(16))) float sDu[CH][TS];
     __shared__ __attribute__((aligned(16))) float sSk[TT][CS];   // D * u
     __shared__ __attribute__((aligned(16))) float sGt[TT][CS];   // SiLU(z) or 1
     __shared__ __attribute__((aligned(16))) float sB[TT][N];
@@ -104,64 +107,106 @@ __global__ __launch_bounds__(256) void selective_scan_kernel(SelScanArgs a, int 
     const AT *bin = static_cast<const AT *>(a.B);
     const AT *cin = static_cast<const AT *>(a.C);
 
+    // The next chunk's rows are loaded into registers while the current chunk
+    // runs its recurrence (rows clamped into the sequence: every load is
+    // unconditional; rows past the chunk are zeroed when staged).
+    constexpr int RPT = TT / SR;                 // staged token rows per thread
+    constexpr int KBC = TT * (N / 4) * 2;        // 4-element pieces of the chunk's B | C
+    constexpr int BCP = (KBC + 255) / 256;
+    Raw<AT, 4> ur[RPT], dr[RPT], zr[RPT], bcr[BCP];
+    auto prefetch = [&](int64_t t0) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int64_t row = t0 + sr0 + i * SR < end ? t0 + sr0 + i * SR : end - 1;
+            const int64_t off = row * Dc + c0 + 4 * sc;
+            ur[i].load(uin + off);
+            dr[i].load(din + off);
+        }
+        if (zin)
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int64_t row = t0 + sr0 + i * SR < end ? t0 + sr0 + i * SR : end - 1;
+                zr[i].load(zin + row * Dc + c0 + 4 * sc);
+            }
+#pragma unroll
+        for (int i = 0; i < BCP; ++i) {
+            const int k = min(tid + i * 256, KBC - 1);
+            const int which = k / (TT * (N / 4)), rem = k % (TT * (N / 4)), r = rem / (N / 4), q4 = rem % (N / 4);
+            const int64_t row = t0 + r < end ? t0 + r : end - 1;
+            bcr[i].load((which ? cin : bin) + (row * G + g) * N + 4 * q4);
+        }
+    };
+    if (start < end) prefetch(start);
+
     for (int64_t t0 = start; t0 < end; t0 += TT) {
         const int cl_n = (int)((end - t0) < TT ? (end - t0) : TT);
-        // ---------------- stage the chunk
-        for (int r = sr0; r < TT; r += SR) {
+        // ---------------- stage the chunk (from the prefetched rows)
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = sr0 + i * SR;
             float dl[4], du[4], sk[4], gt[4];
-            if (r < cl_n) {
-                const int64_t off = (t0 + r) * Dc + c0 + 4 * sc;
-                float uu[4], dd[4];
-                load_k<AT, 4>(uin + off, uu);
-                load_k<AT, 4>(din + off, dd);
-                if (zin) load_k<AT, 4>(zin + off, gt);
+            const bool ok = r < cl_n;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float v = dd[j] + bias[j];
-                    if (a.delta_softplus) v = softplus_fast(v);
-                    dl[j] = v;
-                    du[j] = v * uu[j];
-                    sk[j] = Dv[j] * uu[j];
-                    gt[j] = zin ? silu_fast(gt[j]) : 1.0f;
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dl[j] = du[j] = sk[j] = gt[j] = 0.0f;
+            for (int j = 0; j < 4; ++j) {
+                const float uu = ur[i][j];
+                float v = dr[i][j] + bias[j];
+                if (a.delta_softplus) v = softplus_fast(v);
+                dl[j] = ok ? v : 0.0f;
+                du[j] = ok ? v * uu : 0.0f;
+                sk[j] = ok ? Dv[j] * uu : 0.0f;
+                gt[j] = ok ? (zin ? silu_fast(zr[i][j]) : 1.0f) : 0.0f;
             }
-            *reinterpret_cast<f32x4 *>(&sDl[r][4 * sc]) = f32x4{dl[0], dl[1], dl[2], dl[3]};
-            *reinterpret_cast<f32x4 *>(&sDu[r][4 * sc]) = f32x4{du[0], du[1], du[2], du[3]};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sDl[4 * sc + j][r] = dl[j];
+                sDu[4 * sc + j][r] = du[j];
+            }
             *reinterpret_cast<f32x4 *>(&sSk[r][4 * sc]) = f32x4{sk[0], sk[1], sk[2], sk[3]};
             *reinterpret_cast<f32x4 *>(&sGt[r][4 * sc]) = f32x4{gt[0], gt[1], gt[2], gt[3]};
         }
-        for (int k = tid; k < TT * (N / 4) * 2; k += 256) {
-            const int which = k / (TT * (N / 4)), rem = k % (TT * (N / 4)), r = rem / (N / 4), q4 = rem % (N / 4);
-            float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (r < cl_n) load_k<AT, 4>((which ? cin : bin) + ((t0 + r) * G + g) * N + 4 * q4, v);
-            *reinterpret_cast<f32x4 *>(which ? &sC[r][4 * q4] : &sB[r][4 * q4]) = f32x4{v[0], v[1], v[2], v[3]};
-        }
-        __syncthreads();
-
-        // ---------------- recurrence over the chunk
-#pragma unroll 4
-        for (int t = 0; t < cl_n; ++t) {
-            const float dl = sDl[t][cl], du = sDu[t][cl];
-            const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&sB[t][n0]);
-            const f32x4 c4 = *reinterpret_cast<const f32x4 *>(&sC[t][n0]);
-            float acc = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                h[j] = __builtin_amdgcn_exp2f(dl * A2[j]) * h[j] + du * b4[j];
-                acc += c4[j] * h[j];
+        for (int i = 0; i < BCP; ++i) {
+            const int k = tid + i * 256;
+            if (k < KBC) {
+                const int which = k / (TT * (N / 4)), rem = k % (TT * (N / 4)), r = rem / (N / 4), q4 = rem % (N / 4);
+                const bool ok = r < cl_n;
+                const f32x4 v = {ok ? bcr[i][0] : 0.0f, ok ? bcr[i][1] : 0.0f, ok ? bcr[i][2] : 0.0f, ok ? bcr[i][3] : 0.0f};
+                *reinterpret_cast<f32x4 *>(which ? &sC[r][4 * q4] : &sB[r][4 * q4]) = v;
             }
-            acc = lane_group_sum<LPC>(acc);
-            if (sg == 0) sDu[t][cl] = (acc + sSk[t][cl]) * sGt[t][cl];
+        }
+        __syncthreads();
+        prefetch(t0 + TT < end ? t0 + TT : t0);  // the last chunk reloads itself (unused)
+
+        // ---------------- recurrence over the chunk, 4 tokens per step (tokens past the
+        // chunk's end were staged with delta = delta * u = 0: they leave h unchanged)
+        for (int t = 0; t < cl_n; t += 4) {
+            const f32x4 dl4 = *reinterpret_cast<const f32x4 *>(&sDl[cl][t]);
+            const f32x4 du4 = *reinterpret_cast<const f32x4 *>(&sDu[cl][t]);
+            float ys[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&sB[t + u][n0]);
+                const f32x4 c4 = *reinterpret_cast<const f32x4 *>(&sC[t + u][n0]);
+                float acc = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    h[j] = __builtin_amdgcn_exp2f(dl4[u] * A2[j]) * h[j] + du4[u] * b4[j];
+                    acc += c4[j] * h[j];
+                }
+                ys[u] = lane_group_sum<LPC>(acc);  // every lane of the channel holds the sum
+            }
+            // C.h of the 4 tokens over delta * u (already read); the channel's lanes write equal values
+            *reinterpret_cast<f32x4 *>(&sDu[cl][t]) = f32x4{ys[0], ys[1], ys[2], ys[3]};
         }
         __syncthreads();
 
-        // ---------------- store the y tile (rows of CH channels)
+        // ---------------- store the y tile (rows of CH channels): (C.h + D u) * gate
         for (int r = sr0; r < cl_n; r += SR) {
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(&sDu[r][4 * sc]);
-            const float o[4] = {v[0], v[1], v[2], v[3]};
+            const f32x4 sk = *reinterpret_cast<const f32x4 *>(&sSk[r][4 * sc]);
+            const f32x4 gt = *reinterpret_cast<const f32x4 *>(&sGt[r][4 * sc]);
+            float o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = (sDu[4 * sc + j][r] + sk[j]) * gt[j];
             store_k<OT, 4>(y + (t0 + r) * Dc + c0 + 4 * sc, o);
         }
         __syncthreads();
