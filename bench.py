@@ -349,11 +349,16 @@ def main():
         del w2
 
         ws2 = B.prefill_workspace(d2, T)
+        # chunk_scan_fwd's workspace has the prefill's layout and size; the calls below never overlap
+        assert B.mamba2_chunk_scan_workspace_bytes(d2, T, 4) == ws2.numel()
 
         def conv_fwd():
             B.mamba2_conv1d_fwd(d2, xbc2, cw2, None, post2, convp2, cu2, idx2, hi2)
 
-        def scan():
+        def scan():  # with a workspace: 32-token blocks, B/C planes formed once per group
+            B.mamba2_chunk_scan_fwd(d2, post2, dt2, A2, dtb2, D2, None, y2, pool2, cu2, idx2, hi2, ws2)
+
+        def scan_chunks():  # without one: chunks of 128 on chip
             B.mamba2_chunk_scan_fwd(d2, post2, dt2, A2, dtb2, D2, None, y2, pool2, cu2, idx2, hi2)
 
         def unfused_step():
@@ -373,6 +378,9 @@ def main():
         ms_pre = time_region(prefill_step, args.prefill_steps, torch)
         ms_unf = time_region(unfused_step, args.prefill_steps, torch)
         ms_scan = time_region(scan, args.prefill_steps, torch)
+        for _ in range(2):
+            scan_chunks()
+        ms_chunks = time_region(scan_chunks, args.prefill_steps, torch)
         ms_cf = time_region(conv_fwd, args.prefill_steps, torch)
         # algorithmic minimum of the whole prefill: raw bf16 xBC + dt in, bf16 y out, final fp32 states
         pb, pf = scan_algorithmic(d2, T, 4, 2, 2, 4)
@@ -381,17 +389,20 @@ def main():
         sb, sf = scan_algorithmic(d2, T, 4, 4, 2, 4)
         scan_gbs = sb / (ms_scan * 1e-3) / 1e9
         scan_tfs = sf / (ms_scan * 1e-3) / 1e12
+        chunks_gbs = sb / (ms_chunks * 1e-3) / 1e9
+        chunks_tfs = sf / (ms_chunks * 1e-3) / 1e12
         pre_tok_s = T / (ms_pre * 1e-3)
         log(f"prefill (fused): {ms_pre * 1e3:.1f} us/step ({pre_tok_s / 1e6:.2f} M tok/s, {pre_gbs:.0f} GB/s, "
             f"{pre_tfs:.1f} TFLOP/s); unfused {ms_unf * 1e3:.1f} us = conv1d_fwd {ms_cf * 1e3:.1f} + chunk_scan "
-            f"{ms_scan * 1e3:.1f}")
+            f"{ms_scan * 1e3:.1f} (without a workspace {ms_chunks * 1e3:.1f})")
         result["prefill"] = {
             "value": round(pre_tok_s, 1), "unit": "tok/s", "ms_per_step": round(ms_pre, 4),
             "steps": args.prefill_steps,
             "workload": "Nemotron-H-8B layer prefill: 4 x 8192 tokens (cu_seqlens), chunk 128, bf16 inputs, "
                         "fp32 state, bf16 y, zero initial state, final conv/SSM states to pool slots; "
                         "step = mamba2_prefill_fwd (per-group B/C prep kernel + fused conv/scan kernel over "
-                        "32-token blocks + conv cache update); the unfused detail runs chunk_scan_fwd at chunk 128",
+                        "32-token blocks + conv cache update); the unfused detail runs conv1d_fwd and "
+                        "chunk_scan_fwd, with a workspace (32-token blocks) and without (chunks of 128)",
             "roofline": {"bound": "hbm", "kernel": "mamba2_prefill_fwd (whole call)", "achieved": round(pre_gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(pre_gbs / HBM_PEAK_GBS, 4),
                          "traffic": profiled_traffic("mamba2_prefill_fwd"),
@@ -400,15 +411,23 @@ def main():
                          "mfma_frac": round(pre_tfs / MFMA_BF16_PEAK_TFLOPS, 4)},
             "unfused": {
                 "ms_per_step": round(ms_unf, 4), "tok_s": round(T / (ms_unf * 1e-3), 1),
-                "step": "conv1d_fwd (fp32 post-conv xBC) + chunk_scan_fwd",
+                "step": "conv1d_fwd (fp32 post-conv xBC) + chunk_scan_fwd with a workspace",
                 "chunk_scan_us": round(ms_scan * 1e3, 2), "conv1d_fwd_us": round(ms_cf * 1e3, 2),
-                "chunk_scan_roofline": {"bound": "mfma", "kernel": "chunk_scan_fast_kernel",
+                "chunk_scan_roofline": {"bound": "mfma", "kernel": "chunk_scan_fwd (whole call: prep + block scan)",
                                         "achieved": round(scan_tfs, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                                         "unit": "TFLOP/s", "frac": round(scan_tfs / MFMA_BF16_PEAK_TFLOPS, 4),
-                                        "traffic": profiled_traffic("chunk_scan_fast_kernel"),
+                                        "traffic": profiled_traffic("chunk_scan_fwd"),
                                         "algorithmic_flops_per_launch": sf, "algorithmic_bytes_per_launch": sb,
                                         "hbm_achieved_gbs": round(scan_gbs, 1),
                                         "hbm_frac": round(scan_gbs / HBM_PEAK_GBS, 4)},
+                "chunk_scan_no_workspace_us": round(ms_chunks * 1e3, 2),
+                "chunk_scan_no_workspace_roofline": {
+                    "bound": "mfma", "kernel": "chunk_scan_fast_kernel", "achieved": round(chunks_tfs, 2),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(chunks_tfs / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": profiled_traffic("chunk_scan_fast_kernel"),
+                    "algorithmic_flops_per_launch": sf, "algorithmic_bytes_per_launch": sb,
+                    "hbm_achieved_gbs": round(chunks_gbs, 1), "hbm_frac": round(chunks_gbs / HBM_PEAK_GBS, 4)},
             },
         }
         del xbc2, dt2, pool2, convp2, post2, y2, ws2

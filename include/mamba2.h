@@ -101,9 +101,13 @@ size_t mamba2_ssm_slot_bytes(const mamba2_dims *dims);
 /* Bytes of one conv pool slot: (W-1)*Cdim*sizeof(state). 0 for invalid dims. */
 size_t mamba2_conv_slot_bytes(const mamba2_dims *dims);
 
-/* Workspace the chunk scan needs for `total_tokens` packed tokens in `nseq`
- * sequences (written to *bytes). The gfx950 scan keeps chunk states on chip,
- * so this is 0 for every supported shape. */
+/* Workspace for the faster form of mamba2_chunk_scan_fwd with `total_tokens`
+ * packed tokens in `nseq` sequences (written to *bytes). For headdim 64,
+ * dstate 128 with bf16 act_dtype and out_dtype it is the B/C operand planes of
+ * each 32-token block (the same layout and size as
+ * mamba2_prefill_workspace_bytes); 0 for every other shape, whose scan keeps
+ * all chunk data on chip. The workspace is optional: a call without one runs
+ * the workspace-free chunk kernel. */
 int mamba2_chunk_scan_workspace_bytes(const mamba2_dims *dims, int64_t total_tokens, int32_t nseq,
                                       size_t *bytes);
 
@@ -139,8 +143,13 @@ int mamba2_conv1d_update(const mamba2_dims *dims, const void *xbc, const float *
  *   ssm_pool: the initial state is read from slot state_indices[i] when
  *   has_initial_state[i] is 1 (zeros otherwise); the final state is written
  *   to that slot. dims->chunk_size is the SSD chunk length.
- *   workspace/workspace_bytes: as sized by mamba2_chunk_scan_workspace_bytes
- *   (may be NULL/0 when that is 0). */
+ *   workspace/workspace_bytes: NULL/0, or device memory of at least
+ *   mamba2_chunk_scan_workspace_bytes (MAMBA2_ERR_WORKSPACE if smaller), not
+ *   aliasing xbc or y. With one, the shapes that size it nonzero run as
+ *   32-token blocks whose B/C operands are formed once per group in the
+ *   workspace (the mamba2_prefill_fwd kernels with the conv left out); without
+ *   one, as chunks of dims->chunk_size on chip. Both give the scan's result up
+ *   to rounding order. */
 int mamba2_chunk_scan_fwd(const mamba2_dims *dims, const void *xbc, const void *dt_raw,
                           const float *A_log, const float *dt_bias, const float *D, const void *z,
                           void *y, void *ssm_pool, const int32_t *cu_seqlens, int32_t nseq,

@@ -129,7 +129,8 @@ int mamba2_chunk_scan_workspace_bytes(const mamba2_dims *d, int64_t total_tokens
     if (st) return st;
     if (!bytes) return fail(MAMBA2_ERR_INVALID_ARG, "bytes is NULL");
     if (total_tokens < 0 || nseq < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative size");
-    *bytes = 0;
+    const m2::LayerShape s = shape_of(d);
+    *bytes = m2::chunk_scan_blocks_supported(s) ? (size_t)m2::fused_workspace_bytes(s, total_tokens) : 0;
     return ok();
 }
 
@@ -169,8 +170,6 @@ int mamba2_chunk_scan_fwd(const mamba2_dims *d, const void *xbc, const void *dt_
                           const float *dt_bias, const float *D, const void *z, void *y, void *ssm_pool,
                           const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens, const int32_t *state_indices,
                           const uint8_t *has_initial_state, void *workspace, size_t workspace_bytes, void *stream) {
-    (void)workspace;
-    (void)workspace_bytes;  // the scan keeps chunk states on chip: no workspace needed
     int st = check_scan(d);
     if (st) return st;
     if (nseq < 0 || total_tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative nseq or total_tokens");
@@ -181,9 +180,22 @@ int mamba2_chunk_scan_fwd(const mamba2_dims *d, const void *xbc, const void *dt_
     REQUIRE_PTR(A_log); REQUIRE_PTR(dt_bias); REQUIRE_PTR(D); REQUIRE_PTR(ssm_pool);
     REQUIRE_IDX(cu_seqlens); REQUIRE_IDX(state_indices);
     if (total_tokens > 0) { REQUIRE_PTR(xbc); REQUIRE_PTR(dt_raw); REQUIRE_PTR(y); OPT_PTR(z); }
+    const m2::LayerShape s = shape_of(d);
+    if (workspace && total_tokens > 0 && m2::chunk_scan_blocks_supported(s)) {
+        // 32-token blocks with B/C operand planes in the workspace; without one, the chunk kernel
+        const size_t need = (size_t)m2::fused_workspace_bytes(s, total_tokens);
+        if (workspace_bytes < need)
+            return fail(MAMBA2_ERR_WORKSPACE, "chunk scan needs %zu workspace bytes, got %zu", need, workspace_bytes);
+        OPT_PTR(workspace);
+        if (workspace == xbc || workspace == y) return fail(MAMBA2_ERR_INVALID_ARG, "xbc, y and workspace must not alias");
+        m2::FusedArgs fa{xbc, nullptr, nullptr, nullptr, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, cu_seqlens,
+                         state_indices, has_initial_state, nseq, total_tokens, nullptr, nullptr, nullptr};
+        return hip_status(m2::launch_block_scan(s, fa, workspace, static_cast<hipStream_t>(stream)),
+                          "chunk_scan launch");
+    }
     m2::ScanArgs a{xbc, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, cu_seqlens, state_indices, has_initial_state,
                    nseq, total_tokens};
-    return hip_status(m2::launch_chunk_scan(shape_of(d), a, static_cast<hipStream_t>(stream)), "chunk_scan launch");
+    return hip_status(m2::launch_chunk_scan(s, a, static_cast<hipStream_t>(stream)), "chunk_scan launch");
 }
 
 int mamba2_state_update(const mamba2_dims *d, const void *xbc, const void *dt_raw, const float *A_log,

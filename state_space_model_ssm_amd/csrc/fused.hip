@@ -71,8 +71,11 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
 }  // namespace
 
 // ---------------------------------------------------------------- prep
-template <typename AT, typename ST, int W, int L>
+// XT: xbc element type. W == 1: xbc is already conv + SiLU output and its B/C
+// rows are taken as they are.
+template <typename XT, typename ST, int W, int L>
 __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int G) {
+    constexpr bool CONV = W > 1;
     constexpr int P = 64, N = 128;
     constexpr int RL = L / 8;   // tokens per thread
     constexpr int NS = N + 8;   // bf16 row stride of the token-major tiles
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
     const int blk = blockIdx.x, g = blockIdx.y;
     // one coalesced load of cu_seqlens per workgroup, then searches in LDS (global
     // binary search, one dependent load per step, past kCu sequences)
-    const bool cu_lds = a.nseq <= kCu;
+    const bool cu_lds = CONV && a.nseq <= kCu;
     if (cu_lds)
         for (int i = tid; i <= a.nseq; i += 256) sCu[i] = a.cu[i];
     __syncthreads();
@@ -102,18 +105,25 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
     const int64_t t0 = (int64_t)blk * L + run * RL;
 
     float w[8 * W], bias[8];
-    load_k<float, 8 * W>(a.conv_w + c0 * W, w);
+    if constexpr (CONV) {
+        load_k<float, 8 * W>(a.conv_w + c0 * W, w);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) bias[j] = a.conv_b ? a.conv_b[c0 + j] : 0.0f;
+        for (int j = 0; j < 8; ++j) bias[j] = a.conv_b ? a.conv_b[c0 + j] : 0.0f;
+    }
 
     // conv + SiLU of 8 channels x RL tokens
-    const AT *in = static_cast<const AT *>(a.xbc) + c0;
+    const XT *in = static_cast<const XT *>(a.xbc) + c0;
     float o[RL][8];
 #pragma unroll
     for (int i = 0; i < RL; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) o[i][j] = 0.0f;
-    if (t0 < a.T) {
+    if constexpr (!CONV) {
+        // post-conv rows as they are (rows past T stay 0)
+#pragma unroll
+        for (int i = 0; i < RL; ++i)
+            if (t0 + i < a.T) load_k<XT, 8>(in + (t0 + i) * cdim, o[i]);
+    } else if (t0 < a.T) {
         const int64_t tl = (t0 + RL < a.T ? t0 + RL : a.T) - 1;  // last token of the run
         const int sa = find_seq(cus, a.nseq, t0), sb = find_seq(cus, a.nseq, tl);
         if (sa == sb) {
@@ -126,7 +136,7 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
             for (int i = 0; i < NR; ++i) {
                 int64_t r = t0 - (W - 1) + i;
                 r = r < ss ? ss : (r > se - 1 ? se - 1 : r);
-                load_k<AT, 8>(in + r * cdim, u[i]);
+                load_k<XT, 8>(in + r * cdim, u[i]);
             }
             if (t0 - (W - 1) < ss) {  // rows before the sequence: its cached raw inputs or zeros
                 const bool init = slot >= 0 && a.has_init && a.has_init[sa];
@@ -167,7 +177,7 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
 #pragma unroll
                 for (int k = 0; k < W - 1; ++k) {
                     const int64_t src = t - (W - 1) + k;
-                    if (src >= seq_start) load_k<AT, 8>(in + src * cdim, win[k]);
+                    if (src >= seq_start) load_k<XT, 8>(in + src * cdim, win[k]);
                     else if (init) load_k<ST, 8>(cache + (int64_t)((W - 1) - (seq_start - src)) * cdim, win[k]);
                     else
 #pragma unroll
@@ -185,7 +195,7 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
                     fill_window(t);
                 }
                 float u[8];
-                load_k<AT, 8>(in + t * cdim, u);
+                load_k<XT, 8>(in + t * cdim, u);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     float v = bias[j];
@@ -318,17 +328,19 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
 // arrays, conv + SiLU of x, decayed C.B^T: VALU work), in one instruction
 // stream so the two overlap; then it issues the loads of block b + 2 and meets
 // the other waves at the one barrier of the iteration.
-template <int L, int W, typename ST, typename AT>
+template <int L, int W, typename ST, typename AT, typename XT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fused_scan_kernel(FusedArgs a, int H, int G) {
     constexpr int P = 64, N = 128, NT = 256;
     constexpr int TL = L / 16, KL = L / 32, KN = N / 32, NTL = N / 16;
     constexpr int BTS = L + 8;                 // bf16 row stride of the B^T tiles [n][s]
     constexpr int CS = N + 8;                  // bf16 row stride of the C tile [t][n]
+    constexpr bool CONV = W > 1;               // W == 1: xbc is already conv + SiLU output (taken as is)
     constexpr int XR = 8 + W - 1;              // raw x rows behind one lane's 8 tokens
     constexpr int XRW = L + W - 1;             // raw x rows of a block
-    constexpr uint32_t AS = sizeof(AT);
-    constexpr int XRB = 16 * AS + 8;           // bytes per row of a wave's raw x tile (its 16 channels + pad)
-    constexpr int CPR = AS;                    // 16-byte pieces per raw row of 16 channels
+    constexpr uint32_t AS = sizeof(AT);        // dt_raw and z elements
+    constexpr uint32_t XS = sizeof(XT);        // xbc elements
+    constexpr int XRB = 16 * XS + 8;           // bytes per row of a wave's raw x tile (its 16 channels + pad)
+    constexpr int CPR = XS;                    // 16-byte pieces per raw row of 16 channels
     constexpr int XP = (CPR * XRW + 63) / 64;  // raw x pieces per lane
     constexpr int BTP = (2 * N * L / 8) / NT;  // 16-byte B^T pieces per thread
     constexpr int CPC = (L * N / 8) / NT;      // 16-byte C pieces per thread
@@ -369,10 +381,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     const int64_t chx = (int64_t)head * P + p;
     const bool init = a.has_init && a.has_init[seq];
 
-    float cw[W], ctx[W - 1];
+    float cw[W], ctx[CONV ? W - 1 : 1];
+    float cbias = 0.0f;
+    if constexpr (CONV) {
 #pragma unroll
-    for (int k = 0; k < W; ++k) cw[k] = a.conv_w[chx * W + k];
-    const float cbias = a.conv_b ? a.conv_b[chx] : 0.0f;
+        for (int k = 0; k < W; ++k) cw[k] = a.conv_w[chx * W + k];
+        cbias = a.conv_b ? a.conv_b[chx] : 0.0f;
+    }
 #pragma unroll
     for (int k = 0; k < W - 1; ++k)
         ctx[k] = init ? (float)static_cast<const ST *>(a.conv_pool)[((int64_t)slot * (W - 1) + k) * cdim + chx] : 0.0f;
@@ -412,7 +427,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     // (offsets grow with the row), so a block at a sequence edge costs one
     // v_med3 per load and every load stays unconditional; values that do not
     // belong to the sequence are replaced when staged.
-    const uint32_t xrow = (uint32_t)cdim * AS;                  // bytes per xbc row
+    const uint32_t xrow = (uint32_t)cdim * XS;                  // bytes per xbc row
     uint32_t xq_off[XP], xq_part[XP];                           // raw x piece k of this lane: row, 16-byte part
 #pragma unroll
     for (int k = 0; k < XP; ++k) {
@@ -441,7 +456,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
         const char *dtc = static_cast<const char *>(a.dt_raw) + (bL * H + head) * AS;
         dtr = ld_bits(reinterpret_cast<const AT *>(dtc + min(max(dtlane, (uint32_t)max(lo, 0) * H * AS), (uint32_t)hi * H * AS)));
         // raw x rows bL - (W-1) + rho, rho in [0, L + W - 1), of this wave's 16 channels
-        const char *xc = static_cast<const char *>(a.xbc) + ((bL - (W - 1)) * cdim + (int64_t)head * P + 16 * wv) * AS;
+        const char *xc = static_cast<const char *>(a.xbc) + ((bL - (W - 1)) * cdim + (int64_t)head * P + 16 * wv) * XS;
         const uint32_t xlo = (uint32_t)(lo + (W - 1) > 0 ? lo + (W - 1) : 0) * xrow, xhi = (uint32_t)(hi + (W - 1)) * xrow;
 #pragma unroll
         for (int k = 0; k < XP; ++k)
@@ -510,13 +525,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 #pragma unroll
         for (int m = 0; m < KL; ++m) {
             float u[XR];
-            const char *xr0 = xt + (32 * m + 8 * q) * XRB + AS * col;
+            const char *xr0 = xt + (32 * m + 8 * q) * XRB + XS * col;
 #pragma unroll
             for (int i = 0; i < XR; ++i) {
-                if constexpr (AS == 4) u[i] = *reinterpret_cast<const float *>(xr0 + i * XRB);
-                else u[i] = bits_f<AT>(*reinterpret_cast<const unsigned short *>(xr0 + i * XRB));
+                if constexpr (XS == 4) u[i] = *reinterpret_cast<const float *>(xr0 + i * XRB);
+                else u[i] = bits_f<XT>(*reinterpret_cast<const unsigned short *>(xr0 + i * XRB));
             }
-            if (ctxlo > 1 - W) {  // rows before the sequence: its cached raw inputs (or zeros), at full precision
+            // rows before the sequence: its cached raw inputs (or zeros), at full precision
+            // (post-conv input has no context: those rows only reach their own unstored outputs)
+            if (CONV && ctxlo > 1 - W) {
 #pragma unroll
                 for (int i = 0; i < XR; ++i) {
                     const int d = ctxlo - (32 * m + 8 * q - (W - 1) + i);  // rows before the start
@@ -538,10 +555,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             float xv[8], xd[8], xs[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                float v = cbias;
+                float x = u[j];
+                if constexpr (CONV) {
+                    float v = cbias;
 #pragma unroll
-                for (int k = 0; k < W; ++k) v += cw[k] * u[j + k];
-                const float x = silu_fast(v);
+                    for (int k = 0; k < W; ++k) v += cw[k] * u[j + k];
+                    x = silu_fast(v);
+                }
                 xv[j] = x;
                 xd[j] = x * (j < 4 ? d0[j] : d1[j - 4]);
                 xs[j] = x * (j < 4 ? w0[j] : w1[j - 4]);
@@ -713,15 +733,16 @@ FusedLayout fused_layout(const LayerShape &s, int64_t T) {
     return f;
 }
 
-template <int W, typename ST, typename AT>
+// W == 1: post-conv xbc of type XT (chunk scan alone); W >= 2: raw xbc of type AT
+template <int W, typename ST, typename AT, typename XT>
 hipError_t launch_fw(const LayerShape &s, const FusedArgs &a, int64_t nblk, hipStream_t stream) {
     if (nblk > 0) {  // no tokens (only empty sequences): the scan alone writes their states
-        hipLaunchKernelGGL((fused_prep_kernel<AT, ST, W, kFusedL>), dim3((unsigned)nblk, s.G), dim3(256), 0, stream, a,
+        hipLaunchKernelGGL((fused_prep_kernel<XT, ST, W, kFusedL>), dim3((unsigned)nblk, s.G), dim3(256), 0, stream, a,
                            s.H, s.G);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((fused_scan_kernel<kFusedL, W, ST, AT>), dim3(s.H, a.nseq), dim3(256), 0, stream, a,
+    hipLaunchKernelGGL((fused_scan_kernel<kFusedL, W, ST, AT, XT>), dim3(s.H, a.nseq), dim3(256), 0, stream, a,
                        s.H, s.G);
     return hipGetLastError();
 }
@@ -729,11 +750,20 @@ hipError_t launch_fw(const LayerShape &s, const FusedArgs &a, int64_t nblk, hipS
 template <typename ST, typename AT>
 hipError_t launch_fa(const LayerShape &s, const FusedArgs &a, int64_t nblk, hipStream_t stream) {
     switch (s.W) {
-        case 2: return launch_fw<2, ST, AT>(s, a, nblk, stream);
-        case 3: return launch_fw<3, ST, AT>(s, a, nblk, stream);
-        case 4: return launch_fw<4, ST, AT>(s, a, nblk, stream);
+        case 2: return launch_fw<2, ST, AT, AT>(s, a, nblk, stream);
+        case 3: return launch_fw<3, ST, AT, AT>(s, a, nblk, stream);
+        case 4: return launch_fw<4, ST, AT, AT>(s, a, nblk, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+void set_workspace(const LayerShape &s, FusedArgs &a, void *workspace, int64_t *nblk) {
+    const FusedLayout f = fused_layout(s, a.T);
+    char *ws = static_cast<char *>(workspace);
+    a.cp = ws ? ws + f.cp : nullptr;
+    a.bt = ws ? ws + f.bt : nullptr;
+    a.cb = ws ? ws + f.cb : nullptr;
+    *nblk = f.nblk;
 }
 
 }  // namespace
@@ -742,18 +772,30 @@ bool prefill_fused_supported(const LayerShape &s) {
     return s.P == 64 && s.N == 128 && s.W >= 2 && s.W <= 4 && s.out_dt == DT_BF16 && s.H % s.G == 0;
 }
 
+bool chunk_scan_blocks_supported(const LayerShape &s) {
+    return s.P == 64 && s.N == 128 && s.out_dt == DT_BF16 && s.act_dt == DT_BF16 && s.H % s.G == 0;
+}
+
 int64_t fused_workspace_bytes(const LayerShape &s, int64_t T) { return fused_layout(s, T).bytes; }
 
 hipError_t launch_fused_prefill(const LayerShape &s, FusedArgs a, void *workspace, hipStream_t stream) {
     if (a.nseq == 0) return hipSuccess;
-    const FusedLayout f = fused_layout(s, a.T);
-    char *ws = static_cast<char *>(workspace);
-    a.cp = ws ? ws + f.cp : nullptr;
-    a.bt = ws ? ws + f.bt : nullptr;
-    a.cb = ws ? ws + f.cb : nullptr;
+    int64_t nblk = 0;
+    set_workspace(s, a, workspace, &nblk);
     if (s.state_dt == DT_BF16)
-        return s.act_dt == DT_BF16 ? launch_fa<bf16, bf16>(s, a, f.nblk, stream) : launch_fa<bf16, float>(s, a, f.nblk, stream);
-    return s.act_dt == DT_BF16 ? launch_fa<float, bf16>(s, a, f.nblk, stream) : launch_fa<float, float>(s, a, f.nblk, stream);
+        return s.act_dt == DT_BF16 ? launch_fa<bf16, bf16>(s, a, nblk, stream) : launch_fa<bf16, float>(s, a, nblk, stream);
+    return s.act_dt == DT_BF16 ? launch_fa<float, bf16>(s, a, nblk, stream) : launch_fa<float, float>(s, a, nblk, stream);
+}
+
+hipError_t launch_block_scan(const LayerShape &s, FusedArgs a, void *workspace, hipStream_t stream) {
+    if (a.nseq == 0) return hipSuccess;
+    int64_t nblk = 0;
+    set_workspace(s, a, workspace, &nblk);
+    if (s.state_dt == DT_BF16)
+        return s.xbc_dt == DT_BF16 ? launch_fw<1, bf16, bf16, bf16>(s, a, nblk, stream)
+                                   : launch_fw<1, bf16, bf16, float>(s, a, nblk, stream);
+    return s.xbc_dt == DT_BF16 ? launch_fw<1, float, bf16, bf16>(s, a, nblk, stream)
+                               : launch_fw<1, float, bf16, float>(s, a, nblk, stream);
 }
 
 }  // namespace m2

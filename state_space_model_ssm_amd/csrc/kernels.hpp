@@ -80,11 +80,12 @@ struct ConvMultiArgs {
 };
 
 // Fused prefill (fused.hip); cp / bt / cb are the workspace planes, set by
-// launch_fused_prefill.
+// launch_fused_prefill / launch_block_scan.
 struct FusedArgs {
-    const void *xbc;      // [T][Cdim] raw (pre-conv), activation dtype
-    const float *conv_w, *conv_b;  // [Cdim][W], [Cdim] or null
-    const void *conv_pool;  // [slots][W-1][Cdim], read for the context before each sequence
+    const void *xbc;      // [T][Cdim]: raw (pre-conv, activation dtype) for launch_fused_prefill,
+                          // post-conv (xbc dtype) for launch_block_scan
+    const float *conv_w, *conv_b;  // [Cdim][W], [Cdim] or null (unused by launch_block_scan)
+    const void *conv_pool;  // [slots][W-1][Cdim], read for the context before each sequence (idem)
     const void *dt_raw;   // [T][H]
     const float *A_log, *dt_bias, *D;
     const void *z;        // [T][H*P] or null
@@ -160,6 +161,10 @@ hipError_t launch_conv_state(const LayerShape &s, const ConvFwdArgs &a, hipStrea
 bool prefill_fused_supported(const LayerShape &s);
 int64_t fused_workspace_bytes(const LayerShape &s, int64_t T);
 hipError_t launch_fused_prefill(const LayerShape &s, FusedArgs a, void *workspace, hipStream_t st);
+// The same 32-token-block scan on post-conv xbc (chunk_scan_fwd with a workspace of
+// fused_workspace_bytes): P = 64, N = 128, bf16 activations and y.
+bool chunk_scan_blocks_supported(const LayerShape &s);
+hipError_t launch_block_scan(const LayerShape &s, FusedArgs a, void *workspace, hipStream_t st);
 
 bool gated_norm_supported(int64_t width, int gs);
 hipError_t launch_gated_norm(const NormArgs &a, int y_dt, int z_dt, int64_t width, int gs, hipStream_t st);

@@ -50,7 +50,13 @@ def test_slot_sizes_match_page_arithmetic(lib):
     assert NEMOTRON_H_8B_MAMBA_LAYERS == g["mamba_layers"]
     assert B.mamba2_ssm_slot_bytes(d.with_(state_dtype=F32)) == 2 * g["ssm_bytes_per_layer_per_seq"]
     assert B.mamba2_conv_slot_bytes(d) == 3 * (128 * 64 + 2 * 8 * 128) * 2
-    assert B.mamba2_chunk_scan_workspace_bytes(NEMOTRON_H_8B, 32768, 4) == 0
+    # the chunk scan's optional workspace: the prefill's B/C planes for P=64, N=128, bf16 act/y; none elsewhere
+    assert B.mamba2_chunk_scan_workspace_bytes(NEMOTRON_H_8B, 32768, 4) == 32768 * (3 * 8 * 128 * 2 + 8 * 32 * 4)
+    assert (B.mamba2_chunk_scan_workspace_bytes(NEMOTRON_H_8B, 1000, 3)
+            == B.mamba2_prefill_workspace_bytes(NEMOTRON_H_8B.with_(state_dtype=F32), 1000))
+    assert B.mamba2_chunk_scan_workspace_bytes(NEMOTRON_H_8B.with_(out_dtype=F32), 32768, 4) == 0
+    assert B.mamba2_chunk_scan_workspace_bytes(NEMOTRON_H_8B.with_(act_dtype=F32), 32768, 4) == 0
+    assert B.mamba2_chunk_scan_workspace_bytes(TINY, 64, 1) == 0
 
 
 def test_check_dims(lib):
@@ -95,6 +101,10 @@ def test_invalid_arguments_rejected_without_gpu(lib):
     st = lib.mamba2_chunk_scan_fwd(_cd(), good, good, good, good, good, None, good, good, good, 0, 5, good, None,
                                    None, 0, None)
     assert st == B.ERR_INVALID_ARG
+    # a workspace smaller than the block form needs
+    st = lib.mamba2_chunk_scan_fwd(_cd(), good, good, good, good, good, None, good, good, good, 1, 64, good, None,
+                                   good, 1024, None)
+    assert st == B.ERR_WORKSPACE and b"workspace" in lib.mamba2_last_error()
     # unsupported chunk
     st = lib.mamba2_chunk_scan_fwd(_cd(NEMOTRON_H_8B.with_(chunk_size=96)), good, good, good, good, good, None, good,
                                    good, good, 1, 5, good, None, None, 0, None)

@@ -17,7 +17,13 @@ pytestmark = pytest.mark.gpu
 D16 = NEMOTRON_H_8B.with_(nheads=16, ngroups=2, chunk_size=64, state_dtype=F32, out_dtype=F32)
 
 
-def run_prefill(d, w, has_init=None, slots=None):
+def scan_workspace(d, T, nseq):
+    """Workspace for chunk_scan_fwd's 32-token-block form (None where the shape has none)."""
+    n = B.mamba2_chunk_scan_workspace_bytes(d, T, nseq)
+    return torch.empty(n, dtype=torch.uint8, device="cuda") if n > 0 else None
+
+
+def run_prefill(d, w, has_init=None, slots=None, ws=False):
     pd = params_dev(w["params"])
     T = w["xbc"].shape[0]
     slots = w["slots"] if slots is None else slots
@@ -30,7 +36,8 @@ def run_prefill(d, w, has_init=None, slots=None):
     y = torch.empty(T, d.d_inner, dtype=B._TORCH_DT[d.out_dtype], device="cuda")
     cu, idx, hi = dev_i32(w["cu_seqlens"]), dev_i32(slots), dev_u8(has_init)
     B.mamba2_conv1d_fwd(d, xbc, pd["conv_w"], pd["conv_b"], post, conv, cu, idx, hi)
-    B.mamba2_chunk_scan_fwd(d, post, dt, pd["A_log"], pd["dt_bias"], pd["D"], z, y, ssm, cu, idx, hi)
+    wsp = scan_workspace(d, T, len(slots)) if ws else None
+    B.mamba2_chunk_scan_fwd(d, post, dt, pd["A_log"], pd["dt_bias"], pd["D"], z, y, ssm, cu, idx, hi, wsp)
     torch.cuda.synchronize()
     return y, post, ssm, conv
 
@@ -47,8 +54,8 @@ def oracle_prefill(d, w, has_init=None, slots=None):
     return y, post, cp, sp, used
 
 
-def check_prefill(d, w, has_init=None, slots=None):
-    y, post, ssm, conv = run_prefill(d, w, has_init, slots)
+def check_prefill(d, w, has_init=None, slots=None, ws=False):
+    y, post, ssm, conv = run_prefill(d, w, has_init, slots, ws)
     y_ref, post_ref, cp, sp, used = oracle_prefill(d, w, has_init, slots)
     e_post = assert_close(host(post), post_ref, d.post_dtype, "post-conv xBC")
     e_y = assert_close(host(y), y_ref, d.out_dtype, "y")
@@ -89,16 +96,21 @@ def test_tiny_prefill_then_decode():
     assert np.array_equal(host(conv[slot:slot + 1]), cp)
 
 
+@pytest.mark.parametrize("ws", [False, True], ids=["chunks", "blocks"])
 @pytest.mark.parametrize("out_dtype", [F32, BF16])
 @pytest.mark.parametrize("state_dtype", [F32, BF16])
-def test_varlen_prefill_matches_oracle(out_dtype, state_dtype):
+def test_varlen_prefill_matches_oracle(out_dtype, state_dtype, ws):
     """Several chunks per sequence with ragged tails (lengths 1, 37, 130, 200 at chunk 64),
-    half of the sequences resuming from a saved state."""
+    half of the sequences resuming from a saved state. With a workspace, the bf16-y shapes run
+    the scan as 32-token blocks (post-conv xBC in fp32 with an fp32 state, bf16 with a bf16
+    state)."""
     d = D16.with_(out_dtype=out_dtype, state_dtype=state_dtype)
-    print(f"[prefill parity] out={out_dtype} state={state_dtype}", flush=True)
+    print(f"[prefill parity] out={out_dtype} state={state_dtype} ws={ws}", flush=True)
+    if ws and out_dtype == BF16:
+        assert B.mamba2_chunk_scan_workspace_bytes(d, 368, 4) > 0
     w = synth.prefill_batch(d, seed=7, seqlens=[1, 37, 130, 200], num_slots=9, initial_state=True)
     has_init = np.array([1, 0, 1, 0], np.uint8)
-    check_prefill(d, w, has_init=has_init)
+    check_prefill(d, w, has_init=has_init, ws=ws)
 
 
 def test_prefill_with_z_gate_and_tiny_dims():
@@ -122,6 +134,42 @@ def test_packed_equals_separate_runs_bitwise():
         assert torch.equal(yi, y_all[s:e])
         sl = int(w["slots"][i])
         assert torch.equal(ssmi[sl], ssm_all[sl])
+
+
+def test_block_scan_packing_invariance():
+    """chunk_scan_fwd with a workspace: 32-token blocks at absolute packed positions, so a
+    sequence starting at a multiple of 32 is bit-identical packed or alone; elsewhere only the
+    rounding order differs."""
+    d = D16.with_(out_dtype=BF16)
+    w = synth.prefill_batch(d, seed=9, seqlens=[64, 3, 29, 129], num_slots=4, initial_state=True)
+    y_all, _, ssm_all, _ = run_prefill(d, w, ws=True)
+    cu = w["cu_seqlens"]
+    for i in range(4):
+        s, e = int(cu[i]), int(cu[i + 1])
+        wi = {**w, "xbc": w["xbc"][s:e], "dt_raw": w["dt_raw"][s:e], "z": w["z"][s:e],
+              "cu_seqlens": np.array([0, e - s], np.int32), "slots": w["slots"][i:i + 1],
+              "has_initial_state": w["has_initial_state"][i:i + 1]}
+        yi, _, ssmi, _ = run_prefill(d, wi, ws=True)
+        sl = int(w["slots"][i])
+        if s % 32 == 0:
+            assert torch.equal(yi, y_all[s:e]), f"sequence {i} at offset {s}"
+            assert torch.equal(ssmi[sl], ssm_all[sl])
+        else:
+            assert_close(host(yi), host(y_all[s:e]), BF16, f"y of sequence {i} at offset {s}")
+            assert_close(host(ssmi[sl]), host(ssm_all[sl]), d.state_dtype, f"state of sequence {i}")
+
+
+def test_block_scan_equals_chunk_scan():
+    """The two forms of chunk_scan_fwd (32-token blocks with a workspace, chunks of 64
+    without) agree within the bf16 y / fp32 state tolerances on the same post-conv input."""
+    d = D16.with_(out_dtype=BF16)
+    w = synth.prefill_batch(d, seed=13, seqlens=[300, 45, 1], num_slots=3, initial_state=True)
+    hi = np.array([1, 0, 1], np.uint8)
+    y0, post0, s0, _ = run_prefill(d, w, has_init=hi, ws=False)
+    y1, post1, s1, _ = run_prefill(d, w, has_init=hi, ws=True)
+    assert torch.equal(post0, post1)
+    assert_close(host(y1), host(y0), BF16, "y: blocks vs chunks")
+    assert_close(host(s1), host(s0), F32, "state: blocks vs chunks")
 
 
 @pytest.mark.parametrize("dims,qs", [(D16, (64, 128)), (TINY, (16, 32))])
@@ -156,13 +204,14 @@ def test_equivalence_contract_scan_equals_repeated_steps():
     assert torch.equal(conv_scan, conv)
 
 
-def test_padding_and_empty_sequences():
-    d = D16
+@pytest.mark.parametrize("out_dtype,ws", [(F32, False), (BF16, True)], ids=["chunks", "blocks"])
+def test_padding_and_empty_sequences(out_dtype, ws):
+    d = D16.with_(out_dtype=out_dtype)
     w = synth.prefill_batch(d, seed=12, seqlens=[40, 0, 33, 0], num_slots=6, initial_state=True)
     slots = w["slots"].copy()
     slots[2] = -1  # padding sequence
     has_init = np.array([1, 1, 0, 0], np.uint8)
-    y, post, ssm, conv = run_prefill(d, w, has_init=has_init, slots=slots)
+    y, post, ssm, conv = run_prefill(d, w, has_init=has_init, slots=slots, ws=ws)
     cu = w["cu_seqlens"]
     assert torch.all(y[int(cu[2]):int(cu[3])] == 0).item()
     pad_slot = int(w["slots"][2])
@@ -170,16 +219,18 @@ def test_padding_and_empty_sequences():
     # empty sequence with a saved state keeps it; empty sequence without one ends at zero
     assert np.array_equal(host(ssm[int(slots[1])]), w["ssm_pool"][slots[1]].astype(np.float64))
     assert torch.all(ssm[int(slots[3])] == 0).item()
-    check_prefill(d, w, has_init=has_init, slots=slots)
+    check_prefill(d, w, has_init=has_init, slots=slots, ws=ws)
 
 
-def test_full_size_prefill_sampled():
+@pytest.mark.parametrize("ws", [False, True], ids=["chunks", "blocks"])
+def test_full_size_prefill_sampled(ws):
     """The timed prefill workload (4 x 8192 tokens, 128 heads, chunk 128, bf16 y, fp32 state)
-    in the benchmark's launch configuration, checked on sampled (sequence, head) pairs."""
+    in the benchmark's launch configurations (chunk_scan_fwd without and with a workspace),
+    checked on sampled (sequence, head) pairs."""
     d = NEMOTRON_H_8B.with_(state_dtype=F32)
-    print("[prefill parity] full size 4x8192", flush=True)
+    print(f"[prefill parity] full size 4x8192 ws={ws}", flush=True)
     w = synth.prefill_batch(d, seed=2, seqlens=[8192] * 4, num_slots=8, with_z=False)
-    y, _, ssm, _ = run_prefill(d, w)
+    y, _, ssm, _ = run_prefill(d, w, ws=ws)
     yh = y.float().cpu().numpy()
     cu = w["cu_seqlens"]
     for seq, head in [(0, 0), (1, 37), (2, 77), (3, 127), (0, 64), (3, 15)]:
