@@ -94,14 +94,14 @@ __global__ __launch_bounds__(256) void state_update_kernel(StateUpdateArgs a, in
         float out[kVec];
 #pragma unroll
         for (int j = 0; j < kVec; ++j) {
-            const float s = decay * h[it][j] + dx * Bv[j];
+            const float s = fmaf(decay, h[it][j], dx * Bv[j]);  // explicit: the multi-token kernel rounds alike
             out[j] = s;
-            acc += Cv[j] * s;
+            acc = fmaf(Cv[j], s, acc);
         }
         if (p < P) nt_store16<ST>(tile + (int64_t)p * N + n0, out);
         acc = group_sum_last<kLpr>(acc);
         if (lr == kLpr - 1 && p < P) {
-            float yv = acc + Dh * xv[it];
+            float yv = fmaf(Dh, xv[it], acc);
             if (a.z) yv *= silu_f(zg[it]);
             st(a.y, out_dt, yrow + p, yv);
         }
@@ -161,88 +161,178 @@ hipError_t launch_state_update(const LayerShape &s, const StateUpdateArgs &a, hi
 // snapshot the caller can roll back to); with no dst table only the final state
 // is written, in place. Per step and lane the inputs are the same handful of
 // values as the one-token update.
-template <typename ST, typename XT, typename AT, int N, int ITERS>
+// K consecutive elements of T kept as their raw bits after one load of 2, 4, 8 or
+// 16 bytes (widened where used, so the load is not waited for at once).
+template <typename T, int K> struct RawRow {
+    static constexpr int kB = K * (int)sizeof(T);
+    static_assert(kB == 2 || kB == 4 || kB == 8 || kB == 16, "RawRow: 2, 4, 8 or 16 bytes");
+    uint32_t w[(kB + 3) / 4];
+    __device__ __forceinline__ void load(const T *p) {
+        if constexpr (kB == 16) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(p);
+            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        } else if constexpr (kB == 8) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(p);
+            w[0] = v.x; w[1] = v.y;
+        } else if constexpr (kB == 4) {
+            w[0] = *reinterpret_cast<const uint32_t *>(p);
+        } else {
+            w[0] = *reinterpret_cast<const unsigned short *>(p);
+        }
+    }
+    __device__ __forceinline__ float operator[](int i) const {
+        if constexpr (sizeof(T) == 4) return __uint_as_float(w[i]);
+        else return __uint_as_float((i & 1) ? (w[i >> 1] & 0xffff0000u) : (w[i >> 1] << 16));
+    }
+};
+
+// K consecutive outputs in one store (y of a thread's K rows)
+template <int K> __device__ __forceinline__ void store_row(void *p, int dt, int64_t i, const float *v) {
+    if (dt == DT_BF16) {
+        bf16 *q = static_cast<bf16 *>(p) + i;
+        if constexpr (K == 4) {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<bf16x4 *>(q) = bf16x4{f32_to_bf16(v[0]), f32_to_bf16(v[1]), f32_to_bf16(v[2]), f32_to_bf16(v[3])};
+        } else if constexpr (K == 2) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<bf16x2 *>(q) = bf16x2{f32_to_bf16(v[0]), f32_to_bf16(v[1])};
+        } else {
+            *q = f32_to_bf16(v[0]);
+        }
+    } else {
+        float *q = static_cast<float *>(p) + i;
+        if constexpr (K == 4) *reinterpret_cast<f32x4 *>(q) = f32x4{v[0], v[1], v[2], v[3]};
+        else if constexpr (K == 2) *reinterpret_cast<float2 *>(q) = float2{v[0], v[1]};
+        else *q = v[0];
+    }
+}
+
+// T tokens per row with the state in registers. kLpr lanes cover one p-row's N
+// values (kVec each) and each group of kLpr lanes holds ITERS p-rows:
+//   CONSEC (final state only): rows p0 .. p0 + ITERS - 1, so x of a token is one
+//     vector load and its y leaves the group in one store;
+//   otherwise (a snapshot after every token): rows base + g + it * kGrp, so one
+//     store instruction of a wave writes consecutive rows (1 KiB contiguous at
+//     N = 128 bf16); measured faster for the snapshot stream, slower without it.
+template <typename ST, typename XT, typename AT, int N, int ITERS, bool CONSEC>
 __global__ __launch_bounds__(256) void state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt,
                                                                  int psplit) {
     constexpr int kVec = Io<ST>::kVec;
     constexpr int kLpr = N / kVec;
-    constexpr int kRpi = 256 / kLpr;  // p-rows per pass; each thread holds ITERS rows
+    constexpr int kGrp = 256 / kLpr;  // row groups per workgroup
+    constexpr int XK = CONSEC ? ITERS : 1, XI = CONSEC ? 1 : ITERS;  // x / z: XI loads of XK rows
     const int tid = threadIdx.x;
     const int head = blockIdx.x / psplit;
     const int pblk = blockIdx.x - head * psplit;
     const int row = blockIdx.y;
     const int lr = tid & (kLpr - 1);
+    const int grp = tid / kLpr;
     const int n0 = lr * kVec;
-    const int p_first = pblk * kRpi * ITERS + tid / kLpr;
+    // (P % 4 == 0 and ITERS | 4: a consecutive group is wholly inside P or outside it)
+    auto prow = [&](int it) { return CONSEC ? (pblk * kGrp + grp) * ITERS + it : pblk * kGrp * ITERS + grp + it * kGrp; };
+    int pr[ITERS];  // rows for loads, clamped into the tile; stores are guarded by prow(it) < P
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) pr[it] = min(prow(it), P - 1);
+    if constexpr (CONSEC) {
+        if (prow(0) >= P)
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) pr[it] = P - ITERS + it;
+    }
+    const bool ylane = lr == kLpr - 1;
     const int64_t HP = (int64_t)H * P;
     const int64_t cdim = HP + 2LL * G * N;
     const int T = a.T;
-    const int src = a.src[row];
-    if (src < 0) {
-        if (lr == 0)
+    const int64_t ybase = (int64_t)row * T * HP + (int64_t)head * P;
+    // y of a token: CONSEC, one store of the group's ITERS rows; otherwise one per row
+    auto store_y = [&](int t, const float *yv) {
+        if (!ylane) return;
+        if constexpr (CONSEC) {
+            if (prow(0) < P) store_row<ITERS>(a.y, out_dt, ybase + (int64_t)t * HP + prow(0), yv);
+        } else {
 #pragma unroll
-            for (int it = 0; it < ITERS; ++it) {
-                const int p = p_first + it * kRpi;
-                if (p < P)
-                    for (int t = 0; t < T; ++t) st(a.y, out_dt, ((int64_t)row * T + t) * HP + (int64_t)head * P + p, 0.0f);
-            }
+            for (int it = 0; it < ITERS; ++it)
+                if (prow(it) < P) st(a.y, out_dt, ybase + (int64_t)t * HP + prow(it), yv[it]);
+        }
+    };
+    const int src = a.src[row];
+    if (src < 0) {  // padding row: y = 0, no state access
+        if (ylane)
+            for (int it = 0; it < ITERS; ++it)
+                if (prow(it) < P)
+                    for (int t = 0; t < T; ++t) st(a.y, out_dt, ybase + (int64_t)t * HP + prow(it), 0.0f);
         return;
     }
     const int g = head / (H / G);
     ST *pool = static_cast<ST *>(a.pool);
     const int64_t tile0 = (int64_t)head * P * N + n0;
-    float h[ITERS][kVec];
-    int pr[ITERS];
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-        pr[it] = min(p_first + it * kRpi, P - 1);  // loads clamped; stores guarded
-        nt_load16<ST>(pool + (int64_t)src * H * P * N + tile0 + (int64_t)pr[it] * N, h[it]);
-    }
     const float A = -expf(a.A_log[head]);
     const float dtb = a.dt_bias[head];
     const float Dh = a.D[head];
-    const AT *zsrc = a.z ? static_cast<const AT *>(a.z) : static_cast<const AT *>(a.dt_raw);
 
-    // B and C of a block of TB tokens are loaded once per workgroup into LDS
-    // (every p-row of the head uses the same vectors: re-reading them per row
-    // would move TB * 2 * N values per row through L1/L2 against N state
-    // values); x, dt and z of the block are loaded together, so a block of TB
-    // steps waits on memory once. Tokens past T are clamped and unused.
+    // Per block of TB tokens: B and C are loaded once per workgroup into LDS (every
+    // p-row of the head uses the same vectors: re-reading them per row would move
+    // TB * 2 * N values per row through L1/L2 against N state values); lane u of
+    // each wave takes dt of token t0 + u (read back with readlane). The first
+    // block's loads are issued before the state's, so its staging and dt overlap
+    // the state's latency.
     constexpr int TB = 4;
     constexpr int NT4 = TB * 2 * N / 4;  // 4-element pieces of the block's B|C
+    static_assert(NT4 <= 256, "one B|C piece per thread");
     __shared__ __attribute__((aligned(16))) float sBC[TB][2][N];
-    for (int t0 = 0; t0 < T; t0 += TB) {
-        if (t0 > 0) __syncthreads();  // previous block's B/C fully read
-        for (int k = tid; k < NT4; k += 256) {
-            const int u = k / (N / 2), rem = k % (N / 2), which = rem / (N / 4), n4 = rem % (N / 4);
+    Raw<XT, 4> bcr;
+    RawRow<XT, XK> xr[TB][XI];
+    RawRow<AT, XK> zr[TB][XI];
+    float dr = 0.0f;
+    const XT *xh = static_cast<const XT *>(a.xbc) + (int64_t)row * T * cdim + (int64_t)head * P;
+    // (without z the pointer is formed over dt_raw and never read)
+    const AT *zh = static_cast<const AT *>(a.z ? a.z : a.dt_raw) + (a.z ? ybase : 0);
+    auto xval = [&](int u, int it) {
+        if constexpr (CONSEC) return xr[u][0][it];
+        else return xr[u][it][0];
+    };
+    auto zval = [&](int u, int it) {
+        if constexpr (CONSEC) return zr[u][0][it];
+        else return zr[u][it][0];
+    };
+    auto load_block = [&](int t0) {
+        if (tid < NT4) {
+            const int u = tid / (N / 2), rem = tid % (N / 2), which = rem / (N / 4), n4 = rem % (N / 4);
             const int64_t r = (int64_t)row * T + min(t0 + u, T - 1);
-            float v[4];
-            load_k<XT, 4>(static_cast<const XT *>(a.xbc) + r * cdim + HP + (int64_t)which * G * N + (int64_t)g * N + 4 * n4,
-                          v);
-            *reinterpret_cast<f32x4 *>(&sBC[u][which][4 * n4]) = f32x4{v[0], v[1], v[2], v[3]};
+            bcr.load(static_cast<const XT *>(a.xbc) + r * cdim + HP + (int64_t)which * G * N + (int64_t)g * N + 4 * n4);
         }
-        float xv[TB][ITERS], zv[TB][ITERS];
-        const XT *xh = static_cast<const XT *>(a.xbc) + (int64_t)row * T * cdim + (int64_t)head * P;
 #pragma unroll
         for (int u = 0; u < TB; ++u)
 #pragma unroll
-            for (int it = 0; it < ITERS; ++it) xv[u][it] = (float)xh[(int64_t)min(t0 + u, T - 1) * cdim + pr[it]];
-        if (a.z) {
-            const AT *zh = zsrc + (int64_t)row * T * HP + (int64_t)head * P;
+            for (int i = 0; i < XI; ++i) xr[u][i].load(xh + (int64_t)min(t0 + u, T - 1) * cdim + pr[i]);
+        if (a.z)
 #pragma unroll
             for (int u = 0; u < TB; ++u)
 #pragma unroll
-                for (int it = 0; it < ITERS; ++it) zv[u][it] = (float)zh[(int64_t)min(t0 + u, T - 1) * HP + pr[it]];
+                for (int i = 0; i < XI; ++i) zr[u][i].load(zh + (int64_t)min(t0 + u, T - 1) * HP + pr[i]);
+        const int u = (tid & 63) & (TB - 1);
+        dr = (float)static_cast<const AT *>(a.dt_raw)[((int64_t)row * T + min(t0 + u, T - 1)) * H + head];
+    };
+    auto stage_block = [&](float &dt_l, float &dec_l) {
+        if (tid < NT4) {
+            const int u = tid / (N / 2), rem = tid % (N / 2), which = rem / (N / 4), n4 = rem % (N / 4);
+            *reinterpret_cast<f32x4 *>(&sBC[u][which][4 * n4]) = f32x4{bcr[0], bcr[1], bcr[2], bcr[3]};
         }
-        // dt and the decay of the block's tokens: lane u of each wave computes token t0 + u,
-        // the token loop reads them back as wave-uniform values
+        dt_l = softplus_f(dr + dtb);
+        dec_l = expf(dt_l * A);
+    };
+
+    load_block(0);
+    float h[ITERS][kVec];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) nt_load16<ST>(pool + (int64_t)src * H * P * N + tile0 + (int64_t)pr[it] * N, h[it]);
+
+    for (int t0 = 0; t0 < T; t0 += TB) {
+        if (t0 > 0) {
+            __syncthreads();  // previous block's B/C fully read
+            load_block(t0);
+        }
         float dt_l, dec_l;
-        {
-            const int u = (tid & 63) & (TB - 1);
-            const float dr = (float)static_cast<const AT *>(a.dt_raw)[((int64_t)row * T + min(t0 + u, T - 1)) * H + head];
-            dt_l = softplus_f(dr + dtb);
-            dec_l = expf(dt_l * A);
-        }
+        stage_block(dt_l, dec_l);
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
@@ -259,44 +349,53 @@ __global__ __launch_bounds__(256) void state_update_multi_kernel(MultiStepArgs a
             const float dt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dt_l), u));
             const float decay = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dec_l), u));
             const int d = a.dst ? a.dst[(int64_t)row * T + t] : -1;
+            float yv[ITERS];
 #pragma unroll
             for (int it = 0; it < ITERS; ++it) {
-                const int p = p_first + it * kRpi;
-                const float dx = dt * xv[u][it];
+                const float x = xval(u, it);
+                const float dx = dt * x;
                 float acc = 0.0f;
 #pragma unroll
                 for (int j = 0; j < kVec; ++j) {
-                    h[it][j] = decay * h[it][j] + dx * Bv[j];
-                    acc += Cv[j] * h[it][j];
+                    h[it][j] = fmaf(decay, h[it][j], dx * Bv[j]);  // as the one-token kernel
+                    acc = fmaf(Cv[j], h[it][j], acc);
                 }
-                if (d >= 0 && p < P) nt_store16<ST>(pool + (int64_t)d * H * P * N + tile0 + (int64_t)p * N, h[it]);
+                if (d >= 0 && prow(it) < P) nt_store16<ST>(pool + (int64_t)d * H * P * N + tile0 + (int64_t)prow(it) * N, h[it]);
                 acc = group_sum_last<kLpr>(acc);
-                if (lr == kLpr - 1 && p < P) {
-                    float yv = acc + Dh * xv[u][it];
-                    if (a.z) yv *= silu_f(zv[u][it]);
-                    st(a.y, out_dt, ((int64_t)row * T + t) * HP + (int64_t)head * P + p, yv);
-                }
+                yv[it] = fmaf(Dh, x, acc);
+                if (a.z) yv[it] *= silu_f(zval(u, it));
+                if constexpr (!CONSEC)  // (stored at once: holding them costs registers here)
+                    if (ylane && prow(it) < P)
+                        st(a.y, out_dt, ((int64_t)row * T + t) * HP + (int64_t)head * P + prow(it), yv[it]);
             }
+            if constexpr (CONSEC) store_y(t, yv);
         }
     }
     if (!a.dst)
 #pragma unroll
-        for (int it = 0; it < ITERS; ++it) {
-            const int p = p_first + it * kRpi;
-            if (p < P) nt_store16<ST>(pool + (int64_t)src * H * P * N + tile0 + (int64_t)p * N, h[it]);
-        }
+        for (int it = 0; it < ITERS; ++it)
+            if (prow(it) < P) nt_store16<ST>(pool + (int64_t)src * H * P * N + tile0 + (int64_t)prow(it) * N, h[it]);
 }
 
 template <typename ST, typename XT, int N, int ITERS>
 static hipError_t launch_sum(const LayerShape &s, const MultiStepArgs &a, hipStream_t stream, int rows_needed) {
     const int psplit = (rows_needed + ITERS - 1) / ITERS;
     dim3 grid(s.H * psplit, a.batch);
-    if (s.act_dt == DT_BF16)
-        hipLaunchKernelGGL((state_update_multi_kernel<ST, XT, bf16, N, ITERS>), grid, dim3(256), 0, stream, a, s.H,
-                           s.P, s.G, s.out_dt, psplit);
-    else
-        hipLaunchKernelGGL((state_update_multi_kernel<ST, XT, float, N, ITERS>), grid, dim3(256), 0, stream, a, s.H,
-                           s.P, s.G, s.out_dt, psplit);
+    if (s.act_dt == DT_BF16) {
+        if (a.dst)
+            hipLaunchKernelGGL((state_update_multi_kernel<ST, XT, bf16, N, ITERS, false>), grid, dim3(256), 0, stream, a,
+                               s.H, s.P, s.G, s.out_dt, psplit);
+        else
+            hipLaunchKernelGGL((state_update_multi_kernel<ST, XT, bf16, N, ITERS, true>), grid, dim3(256), 0, stream, a,
+                               s.H, s.P, s.G, s.out_dt, psplit);
+    } else {
+        if (a.dst)
+            hipLaunchKernelGGL((state_update_multi_kernel<ST, XT, float, N, ITERS, false>), grid, dim3(256), 0, stream, a,
+                               s.H, s.P, s.G, s.out_dt, psplit);
+        else
+            hipLaunchKernelGGL((state_update_multi_kernel<ST, XT, float, N, ITERS, true>), grid, dim3(256), 0, stream, a,
+                               s.H, s.P, s.G, s.out_dt, psplit);
+    }
     return hipGetLastError();
 }
 

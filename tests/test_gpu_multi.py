@@ -89,7 +89,7 @@ def test_multi_token_equals_single_steps_bitwise_fp32():
         B.mamba2_state_update(d, post, dev(dt[:, t], A), pd["A_log"], pd["dt_bias"], pd["D"], dev(z[:, t], A), yt,
                               ssm, si)
         torch.cuda.synchronize()
-        assert torch.equal(yt, y_m[:, t]), f"y differs at token {t}"
+        assert torch.equal(yt, y_m[:, t]), f"y differs at token {t}: max |d| {(yt - y_m[:, t]).abs().max().item():.3e}"
     assert torch.equal(ssm, ssm_m) and torch.equal(conv, conv_m)
 
 
@@ -113,3 +113,29 @@ def test_multi_token_full_dims_sampled():
         u = used[1:]
         assert_close(host(ssm[u]), sp[1:], BF16, f"snapshots row {r}")
         assert np.array_equal(host(conv[u]), cp[1:])
+
+
+@pytest.mark.parametrize("out_dtype,with_z", [(BF16, False), (F32, True)])
+def test_multi_token_final_state_only_full_dims(out_dtype, with_z):
+    """Final state only (no snapshots) at Nemotron-H-8B dims: the layout that holds four
+    consecutive p-rows per lane group and writes a token's y in one store per group.
+    64 rows x 6 tokens (two blocks of staged B/C), one padding row, sampled rows checked."""
+    d = NEMOTRON_H_8B.with_(out_dtype=out_dtype)
+    print(f"[multi decode] 8B dims, final state only, out={out_dtype} z={with_z}", flush=True)
+    rows, T = 64, 6
+    params, x, dt, z, pl = make_inputs(d, 44, rows, T, rows, with_z)
+    src = np.arange(rows, dtype=np.int32)[::-1].copy()
+    src[5] = -1  # padding row
+    y, conv, ssm = run_multi(d, params, x, dt, z, pl, src, None)
+    assert torch.all(y[5] == 0).item()
+    assert np.array_equal(host(ssm[int(rows - 1 - 5)]), pl["ssm_pool"][rows - 1 - 5].astype(np.float64))
+    for r in (0, 31, 63):
+        s = int(src[r])
+        cp = pl["conv_pool"][[s]].astype(np.float64)
+        sp = pl["ssm_pool"][[s]].astype(np.float64)
+        zr = None if z is None else z[r:r + 1]
+        y_ref, _ = oracle.decode_multi(x[r:r + 1], dt[r:r + 1], params, np.array([0]), None, cp, sp, z=zr,
+                                       **oracle_kw(d))
+        assert_close(host(y[r:r + 1]), y_ref, out_dtype, f"y row {r}")
+        assert_close(host(ssm[[s]]), sp, BF16, f"final state row {r}")
+        assert np.array_equal(host(conv[[s]]), cp)
