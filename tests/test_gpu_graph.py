@@ -1,6 +1,7 @@
-"""The decode entry points are HIP-graph capturable (no allocation, memset or host
-sync inside), and a captured multi-layer decode step replays bit-identically to
-eager execution, replay after replay."""
+"""The entry points are HIP-graph capturable (no allocation, memset or host sync
+inside): a captured multi-layer decode step, and a captured mixed prefill + decode
+call followed by a multi-token step, replay bit-identically to eager execution,
+replay after replay."""
 import numpy as np
 import pytest
 import torch
@@ -68,4 +69,77 @@ def test_graph_replay_matches_eager_every_time():
             assert torch.equal(s, rs) and torch.equal(v, rv), f"replay {rep}: pools differ"
         # some eager work on the same pools between replays
         run()
+        torch.cuda.synchronize()
+
+
+def test_graph_replay_mixed_batch_and_multi_token():
+    """A mixed prefill + decode call (the prefill through the fused kernels and their workspace)
+    followed by a 3-token decode step of other rows, captured as one graph: every replay equals
+    the eager result, with eager work on the same pools between replays."""
+    from state_space_model_ssm_amd.configs import BF16, F32
+    d = NEMOTRON_H_8B.with_(nheads=16, ngroups=2, state_dtype=F32, out_dtype=BF16)
+    w = synth.mixed_batch(d, seed=31, num_prefill=3, len_lo=20, len_hi=150, decode_rows=5, num_slots=16,
+                          with_z=True)
+    T = int(w["cu_seqlens"][-1])
+    rows = T + 5
+    f = lambda a: dev(a, "bf16")
+    xbc = f(np.concatenate([w["prefill"]["xbc"], w["decode"]["xbc"]]))
+    dt = f(np.concatenate([w["prefill"]["dt_raw"], w["decode"]["dt_raw"]]))
+    z = f(np.concatenate([w["prefill"]["z"], w["decode"]["z"]]))
+    P_ = {k: dev(w["params"][k], "f32") for k in ("conv_w", "A_log", "dt_bias", "D")}
+    ssm0, conv0 = dev(w["ssm_pool"], "f32"), dev(w["conv_pool"], "f32")
+    cu = torch.from_numpy(w["cu_seqlens"]).cuda()
+    pidx = torch.from_numpy(w["prefill_slots"]).cuda()
+    didx = torch.from_numpy(w["decode_slots"]).cuda()
+    hi = torch.from_numpy(w["has_initial_state"]).cuda()
+    ws = B.prefill_workspace(d, T)
+    post = torch.empty(rows, d.conv_dim, dtype=torch.float32, device="cuda")
+    y = torch.empty(rows, d.d_inner, dtype=torch.bfloat16, device="cuda")
+    # multi-token rows: 2 rows x 3 tokens on slots the mixed call does not touch
+    used = set(int(v) for v in np.concatenate([w["prefill_slots"], w["decode_slots"]]))
+    free = [s for s in range(16) if s not in used][:2]
+    rng = np.random.default_rng(32)
+    mx = f(rng.standard_normal((2, 3, d.conv_dim)))
+    mdt = f(rng.standard_normal((2, 3, d.nheads)) * 0.5)
+    msrc = torch.tensor(free, dtype=torch.int32, device="cuda")
+    mpost = torch.empty(2, 3, d.conv_dim, dtype=torch.float32, device="cuda")
+    my = torch.empty(2, 3, d.d_inner, dtype=torch.bfloat16, device="cuda")
+    ssm, conv = ssm0.clone(), conv0.clone()
+
+    def run():
+        B.mamba2_mixed_fwd(d, xbc, dt, z, P_["conv_w"], None, P_["A_log"], P_["dt_bias"], P_["D"], post, y, ssm, conv,
+                           cu, pidx, hi, didx, ws)
+        B.mamba2_conv1d_update_multi(d, mx, P_["conv_w"], None, mpost, conv, msrc)
+        B.mamba2_state_update_multi(d, mpost, mdt, P_["A_log"], P_["dt_bias"], P_["D"], None, my, ssm, msrc)
+
+    def reset():
+        ssm.copy_(ssm0)
+        conv.copy_(conv0)
+
+    run()
+    torch.cuda.synchronize()
+    ref = (y.clone(), my.clone(), ssm.clone(), conv.clone())
+    reset()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        graph.capture_begin()
+        run()
+        graph.capture_end()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        reset()
+        y.zero_()
+        my.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (y, my, ssm, conv)
+        for name, a, b in zip(("y", "multi y", "ssm pool", "conv pool"), got, ref):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs"
+        reset()
+        run()  # eager work on the same buffers between replays
         torch.cuda.synchronize()
