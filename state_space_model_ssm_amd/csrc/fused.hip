@@ -40,6 +40,10 @@
 //        workgroups share a CU and overlap each other's phases;
 //      * the next block's tiles, dt and raw x are loaded into registers while
 //        the current block computes.
+//
+// With conv width W = 1 both kernels take post-conv xBC as it is (no conv, no
+// SiLU, no context rows): that instantiation is mamba2_chunk_scan_fwd's form
+// when the caller passes a workspace.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma.hpp"
