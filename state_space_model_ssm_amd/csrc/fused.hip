@@ -78,7 +78,7 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
 // XT: xbc element type. W == 1: xbc is already conv + SiLU output and its B/C
 // rows are taken as they are.
 template <typename XT, typename ST, int W, int L>
-__global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int G) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(XT) == 2 ? 4 : 1))) void fused_prep_kernel(FusedArgs a, int H, int G) {
     constexpr bool CONV = W > 1;
     constexpr int P = 64, N = 128;
     constexpr int RL = L / 8;   // tokens per thread
@@ -115,18 +115,52 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
         for (int j = 0; j < 8; ++j) bias[j] = a.conv_b ? a.conv_b[c0 + j] : 0.0f;
     }
 
-    // conv + SiLU of 8 channels x RL tokens
+    // Token i of the thread's run leaves as soon as it is computed: B as hi / lo rows of
+    // the token-major tiles (C.B^T below, and the transposed planes); C in natural order
+    // in LDS and as a permuted token-major row of the workspace. Rows past T or of
+    // padding sequences are zeros.
     const XT *in = static_cast<const XT *>(a.xbc) + c0;
-    float o[RL][8];
+    const int tl0 = run * RL;  // first token of the thread inside the block
+    bf16 *cp = static_cast<bf16 *>(a.cp) + (int64_t)g * N + (n0 & ~31);
+    const int u0 = n0 & 31;
+    auto emit = [&](int i, const float *o) {
+        if (!isC) {
+            bf16x8 h, l;
 #pragma unroll
-    for (int i = 0; i < RL; ++i)
+            for (int j = 0; j < 8; ++j) {
+                h[j] = f32_to_bf16(o[j]);
+                l[j] = f32_to_bf16(o[j] - (float)h[j]);
+            }
+            *reinterpret_cast<bf16x8 *>(&sB[0][(tl0 + i) * NS + n0]) = h;
+            *reinterpret_cast<bf16x8 *>(&sB[1][(tl0 + i) * NS + n0]) = l;
+        } else {
+            bf16x8 c;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[i][j] = 0.0f;
+            for (int j = 0; j < 8; ++j) c[j] = f32_to_bf16(o[j]);
+            *reinterpret_cast<bf16x8 *>(&sC[(tl0 + i) * NS + n0]) = c;
+            if (t0 + i < a.T) {
+                bf16 *row = cp + (t0 + i) * GN;
+                *reinterpret_cast<bf16x4 *>(row + perm32(u0)) = bf16x4{c[0], c[1], c[2], c[3]};
+                *reinterpret_cast<bf16x4 *>(row + perm32(u0 + 4)) = bf16x4{c[4], c[5], c[6], c[7]};
+            }
+        }
+    };
+    const float zero8[8] = {};
+    int done = 0;  // tokens of the run emitted so far (the rest are emitted as zeros below)
+
+    // conv + SiLU of 8 channels x RL tokens
     if constexpr (!CONV) {
-        // post-conv rows as they are (rows past T stay 0)
+        // post-conv rows as they are
 #pragma unroll
-        for (int i = 0; i < RL; ++i)
-            if (t0 + i < a.T) load_k<XT, 8>(in + (t0 + i) * cdim, o[i]);
+        for (int i = 0; i < RL; ++i) {
+            float o[8];
+            if (t0 + i < a.T) load_k<XT, 8>(in + (t0 + i) * cdim, o);
+            else
+#pragma unroll
+                for (int j = 0; j < 8; ++j) o[j] = 0.0f;
+            emit(i, o);
+        }
+        done = RL;
     } else if (t0 < a.T) {
         const int64_t tl = (t0 + RL < a.T ? t0 + RL : a.T) - 1;  // last token of the run
         const int sa = find_seq(cus, a.nseq, t0), sb = find_seq(cus, a.nseq, tl);
@@ -135,24 +169,35 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
             constexpr int NR = RL + W - 1;
             const int64_t ss = cus[sa], se = cus[sa + 1];
             const int slot = a.idx[sa];
-            float u[NR][8];
+            // rows as raw bits (widened where used) at 32-bit offsets from the window's
+            // first row: fewer registers, so more workgroups share a CU
+            const int64_t r0 = t0 - (W - 1);
+            const char *wbase = reinterpret_cast<const char *>(in + r0 * cdim);
+            const uint32_t rowb = (uint32_t)(cdim * (int64_t)sizeof(XT));
+            Raw<XT, 8> rw[NR];
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
-                int64_t r = t0 - (W - 1) + i;
+                int64_t r = r0 + i;
                 r = r < ss ? ss : (r > se - 1 ? se - 1 : r);
-                load_k<XT, 8>(in + r * cdim, u[i]);
+                rw[i].load(reinterpret_cast<const XT *>(wbase + (uint32_t)(r - r0) * rowb));
             }
-            if (t0 - (W - 1) < ss) {  // rows before the sequence: its cached raw inputs or zeros
+            // rows before the sequence (only among the first W - 1): its cached raw inputs or zeros
+            const bool head = r0 < ss;
+            float ctx[W - 1][8];
+            if (head) {
                 const bool init = slot >= 0 && a.has_init && a.has_init[sa];
                 const ST *cache = static_cast<const ST *>(a.conv_pool) + (int64_t)(slot < 0 ? 0 : slot) * (W - 1) * cdim + c0;
 #pragma unroll
-                for (int i = 0; i < NR; ++i) {
-                    const int64_t d = ss - (t0 - (W - 1) + i);
-                    if (d > 0) {
-                        if (init && d <= W - 1) load_k<ST, 8>(cache + (int64_t)((W - 1) - d) * cdim, u[i]);
-                        else
+                for (int k = 0; k < W - 1; ++k) {
+                    const int64_t d = ss - (r0 + k);
+                    if (d <= 0) {
 #pragma unroll
-                            for (int j = 0; j < 8; ++j) u[i][j] = 0.0f;
+                        for (int j = 0; j < 8; ++j) ctx[k][j] = rw[k][j];
+                    } else if (init) {
+                        load_k<ST, 8>(cache + (int64_t)((W - 1) - d) * cdim, ctx[k]);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) ctx[k][j] = 0.0f;
                     }
                 }
             }
@@ -160,13 +205,19 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
 #pragma unroll
                 for (int i = 0; i < RL; ++i) {
                     if (t0 + i > tl) break;
+                    float o[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         float v = bias[j];
 #pragma unroll
-                        for (int k = 0; k < W; ++k) v += w[j * W + k] * u[i + k][j];
-                        o[i][j] = silu_fast(v);
+                        for (int k = 0; k < W; ++k) {
+                            const int rr = i + k;
+                            v += w[j * W + k] * ((rr < W - 1 && head) ? ctx[rr][j] : rw[rr][j]);
+                        }
+                        o[j] = silu_fast(v);
                     }
+                    emit(i, o);
+                    done = i + 1;
                 }
             }
         } else {
@@ -198,7 +249,7 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
                     slot = a.idx[seq];
                     fill_window(t);
                 }
-                float u[8];
+                float u[8], o[8];
                 load_k<XT, 8>(in + t * cdim, u);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
@@ -206,11 +257,10 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
 #pragma unroll
                     for (int k = 0; k < W - 1; ++k) v += w[j * W + k] * win[k][j];
                     v += w[j * W + W - 1] * u[j];
-                    const float r = silu_fast(v);
-#pragma unroll
-                    for (int ii = 0; ii < RL; ++ii)
-                        if (ii == i) o[ii][j] = slot >= 0 ? r : 0.0f;
+                    o[j] = slot >= 0 ? silu_fast(v) : 0.0f;
                 }
+                emit(i, o);
+                done = i + 1;
 #pragma unroll
                 for (int k = 0; k < W - 2; ++k)
 #pragma unroll
@@ -221,37 +271,7 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(FusedArgs a, int H, int
         }
     }
 
-    const int tl0 = run * RL;  // first token of the thread inside the block
-    if (!isC) {
-        // B: token-major hi / lo tiles (C.B^T below, and the transposed planes)
-#pragma unroll
-        for (int i = 0; i < RL; ++i) {
-            bf16x8 h, l;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                h[j] = f32_to_bf16(o[i][j]);
-                l[j] = f32_to_bf16(o[i][j] - (float)h[j]);
-            }
-            *reinterpret_cast<bf16x8 *>(&sB[0][(tl0 + i) * NS + n0]) = h;
-            *reinterpret_cast<bf16x8 *>(&sB[1][(tl0 + i) * NS + n0]) = l;
-        }
-    } else {
-        // C: natural order in LDS; permuted token-major rows in the workspace
-        bf16 *cp = static_cast<bf16 *>(a.cp) + (int64_t)g * N + (n0 & ~31);
-        const int u0 = n0 & 31;
-#pragma unroll
-        for (int i = 0; i < RL; ++i) {
-            bf16x8 c;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) c[j] = f32_to_bf16(o[i][j]);
-            *reinterpret_cast<bf16x8 *>(&sC[(tl0 + i) * NS + n0]) = c;
-            if (t0 + i < a.T) {
-                bf16 *row = cp + (t0 + i) * GN;
-                *reinterpret_cast<bf16x4 *>(row + perm32(u0)) = bf16x4{c[0], c[1], c[2], c[3]};
-                *reinterpret_cast<bf16x4 *>(row + perm32(u0 + 4)) = bf16x4{c[4], c[5], c[6], c[7]};
-            }
-        }
-    }
+    for (int i = done; i < RL; ++i) emit(i, zero8);
     __syncthreads();
 
     // B^T hi / lo planes [hl][n][L] from the token-major tiles: 16-byte pieces of 8 tokens,
