@@ -110,7 +110,7 @@ def conv1d_seq(u, w, bias, state):
     T, C = u.shape
     W = w.shape[1]
     assert w.shape == (C, W) and 1 <= W <= 16
-    st = np.array(state, dtype=np.float64, copy=True).reshape(W - 1, C)
+    st = np.array(state, dtype=np.float64, copy=True, order="C").reshape(W - 1, C)
     out = np.empty((T, C), dtype=np.float64)
     _load().oracle_conv1d_seq(T, C, W, _ptr(u), _ptr(w), _ptr(_f64(bias)), _ptr(st), _ptr(out))
     return out, st
@@ -126,7 +126,7 @@ def ssm_seq(xbc_post, dt_raw, A_log, dt_bias, D, h0, *, H, P, N, G, z=None, roun
     T = xbc_post.shape[0]
     assert xbc_post.shape[1] == H * P + 2 * G * N and H % G == 0
     dt_raw = _f64(dt_raw).reshape(T, H)
-    h = np.array(h0, dtype=np.float64, copy=True).reshape(H, P, N)
+    h = np.array(h0, dtype=np.float64, copy=True, order="C").reshape(H, P, N)
     y = np.empty((T, H * P), dtype=np.float64)
     zz = None if z is None else _f64(z).reshape(T, H * P)
     _load().oracle_ssm_seq(T, H, P, N, G, _ptr(xbc_post), _ptr(dt_raw), _ptr(_f64(A_log)),
@@ -217,7 +217,7 @@ def selective_scan_seq(u, delta_raw, A, B, C, h0, *, D=None, z=None, delta_bias=
     assert B.ndim == 3 and B.shape[0] == T and B.shape[2] == N, "B must be [T, G, N]"
     G = B.shape[1]
     assert Dc % G == 0
-    h = np.array(h0, dtype=np.float64, copy=True).reshape(Dc, N)
+    h = np.array(h0, dtype=np.float64, copy=True, order="C").reshape(Dc, N)
     y = np.empty((T, Dc), dtype=np.float64)
     _load().oracle_selective_scan_seq(T, Dc, N, G, _ptr(u), _ptr(_f64(delta_raw).reshape(T, Dc)), _ptr(A), _ptr(B),
                                       _ptr(_f64(C).reshape(T, G, N)), _ptr(_f64(D)),

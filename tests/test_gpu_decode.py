@@ -113,3 +113,31 @@ def test_decode_makes_no_allocation():
         B.mamba2_state_update(d, post, dt, pd["A_log"], pd["dt_bias"], pd["D"], None, y, ssm, ii)
     torch.cuda.synchronize()
     assert torch.cuda.memory_stats()["allocation.all.allocated"] == before
+
+
+@pytest.mark.parametrize("state_dtype,rows,nslots", [(BF16, 1024, 1024), (F32, 384, 1024)],
+                         ids=["1024-rows-bf16", "384-rows-f32-1024-slots"])
+def test_decode_largest_batches_sampled(state_dtype, rows, nslots):
+    """The largest decode batches of the workloads: 1024 concurrent sequences on a full
+    1024-slot bf16 pool (the 48-layer stack's top concurrency, per layer) and the mixed batch's
+    384 rows on a 1024-slot fp32 pool; 16 sampled rows checked against the oracle, every
+    untouched slot bit-identical."""
+    d = NEMOTRON_H_8B.with_(state_dtype=state_dtype)
+    print(f"[decode parity] {rows} rows, {nslots}-slot {state_dtype} pool (sampled)", flush=True)
+    w = synth.decode_batch(d, seed=9, rows=rows, num_slots=nslots, with_z=True)
+    y, post, ssm, conv = run_decode(d, w)
+    pick = np.sort(np.random.default_rng(9).choice(rows, size=16, replace=False))
+    sl = w["slots"][pick]
+    cp, sp = compact_pools(w, sl)
+    y_ref, post_ref = oracle.decode(w["xbc"][pick], w["dt_raw"][pick], w["params"], np.arange(16), cp, sp,
+                                    z=w["z"][pick], **oracle_kw(d))
+    ii = torch.from_numpy(pick.astype(np.int64)).cuda()
+    assert_close(host(post[ii]), post_ref, d.post_dtype, "post-conv xBC")
+    assert_close(host(y[ii]), y_ref, d.out_dtype, "y")
+    s = torch.from_numpy(sl.astype(np.int64)).cuda()
+    assert_close(host(ssm[s]), sp, state_dtype, "ssm state")
+    assert np.array_equal(host(conv[s]), cp)
+    untouched = np.setdiff1d(np.arange(nslots), w["slots"])
+    if len(untouched):
+        u = torch.from_numpy(untouched).cuda()
+        assert torch.all(ssm[u].float() == synth.SENTINEL).item()

@@ -234,6 +234,24 @@ def test_fused_full_size_sampled():
         assert np.array_equal(host(conv[int(w["slots"][seq])]), w["xbc"][e - 3:e].astype(np.float64))
 
 
+def test_fused_long_sequence_resumed_sampled():
+    """One 32,768-token sequence resuming from a saved conv and SSM state (1,024 blocks of
+    carried state in one workgroup per head), checked on sampled heads and the conv cache."""
+    d = NEMOTRON_H_8B.with_(state_dtype=F32)
+    print("[fused prefill] one 32768-token sequence, resumed", flush=True)
+    w = synth.prefill_batch(d, seed=29, seqlens=[32768], num_slots=2, with_z=False, initial_state=True)
+    y, ssm, conv = run_fused(d, w, has_init=np.array([1], np.uint8))
+    yh = y.float().cpu().numpy()
+    sl = int(w["slots"][0])
+    cs0 = w["conv_pool"][sl].astype(np.float64)
+    hs0 = w["ssm_pool"][sl].astype(np.float64)
+    for head in (3, 66, 125):
+        yr, hr = oracle_head_seq(d, w["params"], w["xbc"], w["dt_raw"], head, conv_state=cs0, ssm_state=hs0)
+        assert_close(yh[:, head * 64:(head + 1) * 64], yr, BF16, f"y head {head}")
+        assert_close(host(ssm[sl, head]), hr, F32, f"state head {head}")
+    assert np.array_equal(host(conv[sl]), w["xbc"][-3:].astype(np.float64))
+
+
 def test_mixed_batch_through_fused_prefill():
     """mamba2_mixed_fwd with a prefill workspace: the prefill segment runs mamba2_prefill_fwd
     (fused for bf16 y), the decode rows conv1d_update + state_update, against the oracle."""
