@@ -187,6 +187,29 @@ __device__ __forceinline__ int find_seq(const int32_t *cu, int nseq, int64_t t) 
     return lo;
 }
 
+// Sequence taken by the workgroups in grid row r of a (…, nseq) grid whose workgroups
+// each carry one sequence from start to end: with 2..kRankMax sequences, the r-th
+// longest (ties by index), so long sequences are dispatched first and do not leave a
+// tail of few busy CUs after the short ones finish; otherwise sequence r. The result
+// does not depend on which workgroup takes which sequence. Every thread of the
+// workgroup calls it (it synchronises the workgroup once when it reorders).
+constexpr int kRankMax = 256;
+__device__ __forceinline__ int seq_longest_first(const int32_t *cu, int nseq, int r, int tid, int nthreads,
+                                                 int *shared_seq) {
+    if (nseq <= 1 || nseq > kRankMax) return r;
+    for (int i = tid; i < nseq; i += nthreads) {
+        const int li = cu[i + 1] - cu[i];
+        int rank = 0;
+        for (int j = 0; j < nseq; ++j) {
+            const int lj = cu[j + 1] - cu[j];
+            rank += (lj > li) | ((lj == li) & (j < i));
+        }
+        if (rank == r) *shared_seq = i;  // ranks are a permutation: one writer
+    }
+    __syncthreads();
+    return *shared_seq;
+}
+
 __device__ __forceinline__ float softplus_f(float v) { return fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v))); }
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + expf(-v)); }
 // softplus(v) = max(v, 0) + log1p(exp(-|v|)) from the hardware exp2/log2, with

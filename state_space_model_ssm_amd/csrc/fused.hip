@@ -386,7 +386,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
     const int col = lane & 15, q = lane >> 4;
-    const int head = xcd_head(blockIdx.x, H), seq = blockIdx.y;
+    __shared__ int sSeq;
+    const int head = xcd_head(blockIdx.x, H), seq = seq_longest_first(a.cu, a.nseq, blockIdx.y, tid, NT, &sSeq);
     const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N, cdim = HP + 2 * GN;
     const int g = head / (H / G);
     const int64_t start = a.cu[seq], end = a.cu[seq + 1];

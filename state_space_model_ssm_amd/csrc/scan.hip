@@ -73,7 +73,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, q = lane >> 4;
-    const int head = xcd_head(blockIdx.x, H), seq = blockIdx.y;
+    __shared__ int sSeq;
+    const int head = xcd_head(blockIdx.x, H), seq = seq_longest_first(a.cu, a.nseq, blockIdx.y, tid, NT, &sSeq);
     const int64_t HP = (int64_t)H * P;
     const int64_t cdim = HP + 2LL * G * N;
     const int g = head / (H / G);
@@ -456,7 +457,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, q = lane >> 4;
-    const int head = xcd_head(blockIdx.x, H), seq = blockIdx.y;
+    __shared__ int sSeq;
+    const int head = xcd_head(blockIdx.x, H), seq = seq_longest_first(a.cu, a.nseq, blockIdx.y, tid, NT, &sSeq);
     const int64_t HP = (int64_t)H * P;
     const int64_t cdim = HP + 2LL * G * N;
     const int g = head / (H / G);

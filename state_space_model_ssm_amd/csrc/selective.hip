@@ -62,7 +62,8 @@ __global__ __launch_bounds__(256) void selective_scan_kernel(SelScanArgs a, int 
     __shared__ __attribute__((aligned(16))) float sC[TT][N];
 
     const int tid = threadIdx.x;
-    const int cblk = blockIdx.x, seq = blockIdx.y;
+    __shared__ int sSeq;
+    const int cblk = blockIdx.x, seq = seq_longest_first(a.cu, a.nseq, blockIdx.y, tid, 256, &sSeq);
     const int c0 = cblk * CH;                 // first channel of the workgroup
     const int g = c0 / (Dc / G);              // its group (CH divides Dc / G)
     const int64_t start = a.cu[seq], end = a.cu[seq + 1];
