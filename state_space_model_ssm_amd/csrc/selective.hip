@@ -191,8 +191,9 @@ __global__ __launch_bounds__(256) void selective_scan_kernel(SelScanArgs a, int 
                 float acc = 0.0f;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    h[j] = __builtin_amdgcn_exp2f(dl4[u] * A2[j]) * h[j] + du4[u] * b4[j];
-                    acc += c4[j] * h[j];
+                    // explicit FMAs: the one-token kernel below rounds exactly alike
+                    h[j] = fmaf(__builtin_amdgcn_exp2f(dl4[u] * A2[j]), h[j], du4[u] * b4[j]);
+                    acc = fmaf(c4[j], h[j], acc);
                 }
                 ys[u] = lane_group_sum<LPC>(acc);  // every lane of the channel holds the sum
             }
@@ -253,8 +254,8 @@ __global__ __launch_bounds__(256) void selective_update_kernel(SelUpdateArgs a, 
     float acc = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        h[j] = __builtin_amdgcn_exp2f(dl * (A2[j] * LOG2E)) * h[j] + du * b4[j];
-        acc += c4[j] * h[j];
+        h[j] = fmaf(__builtin_amdgcn_exp2f(dl * (A2[j] * LOG2E)), h[j], du * b4[j]);
+        acc = fmaf(c4[j], h[j], acc);
     }
     acc = lane_group_sum<LPC>(acc);
     store_k<ST, 4>(hp, h);
