@@ -32,14 +32,17 @@
 //      * each lane computes the conv + SiLU of its own channel for eight
 //        consecutive tokens per 32-token block: exactly the k-slots of the
 //        x operands (x dt for the output, x dt exp(lam_end - lam) as hi/lo
-//        for the state), so x never goes through LDS either;
+//        for the state), so post-conv x is never shared or stored; its raw
+//        rows reach the lanes through a small wave-private LDS tile;
 //      * D x is one more MFMA per t-tile, against a selector operand that
 //        holds D (hi and lo) on the diagonal;
-//      * LDS holds only what all waves share: B^T hi/lo, C and the decayed
-//        C.B^T tiles (each wave computes those of one t-tile), 64 KB, so two
-//        workgroups share a CU and overlap each other's phases;
-//      * the next block's tiles, dt and raw x are loaded into registers while
-//        the current block computes.
+//      * the shared LDS tiles are B^T hi/lo, C and the decayed C.B^T operands
+//        (each wave forms half of one t-tile's), double-buffered: about 70 KB
+//        per workgroup with the wave-private tiles, so two workgroups share a
+//        CU and overlap each other's phases;
+//      * block b computes from tiles staged one iteration earlier while block
+//        b + 1 is staged into the other buffer and block b + 2's tiles, dt
+//        and raw x are loaded into registers.
 //
 // With conv width W = 1 both kernels take post-conv xBC as it is (no conv, no
 // SiLU, no context rows): that instantiation is mamba2_chunk_scan_fwd's form

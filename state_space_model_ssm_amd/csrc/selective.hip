@@ -46,7 +46,7 @@ template <int N, typename AT, typename ST, typename OT>
 __global__ __launch_bounds__(256) void selective_scan_kernel(SelScanArgs a, int Dc, int G) {
     constexpr int LPC = N / 4;          // lanes per channel (4 states each)
     constexpr int CH = 256 / LPC;       // channels per workgroup
-    constexpr int TT = 16 * LPC;        // tokens per chunk (LDS stays ~70 KB for every N)
+    constexpr int TT = 16 * LPC;        // tokens per chunk (LDS stays below 80 KB for every N: two workgroups per CU)
     constexpr int CS = CH + 4;          // row stride of the per-token channel arrays (floats)
     constexpr float LOG2E = 1.4426950408889634f;
     static_assert(N % 4 == 0 && LPC >= 1 && LPC <= 16, "dstate must be a multiple of 4, at most 64");
