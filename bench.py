@@ -371,7 +371,7 @@ def main():
 
         for _ in range(args.prefill_warmup):  # untimed; brings the clocks to their sustained state
             prefill_step()
-        for _ in range(2):
+        for _ in range(max(2, args.prefill_warmup // 2)):
             unfused_step()
         torch.cuda.synchronize()
         log(f"timing {args.prefill_steps} prefill steps")
@@ -452,7 +452,7 @@ def main():
         def sel_step():
             B.mamba1_selective_scan_fwd(d1, u1, dl1, A1, B1, C1, D1, None, db1, y1, pool1, cu1, idx1, None, True)
 
-        for _ in range(2):
+        for _ in range(args.prefill_warmup):  # untimed, as for the prefill
             sel_step()
         ms_sel = time_region(sel_step, max(3, args.prefill_steps), torch)
         elems = T1 * d1.dim * d1.dstate
@@ -529,7 +529,7 @@ def main():
             B.mamba2_mixed_fwd(d3, xbc3, dt3, None, cw3, None, A3, dtb3, D3, post3, y3, ssm3, conv3, cu3, pidx3, hi3,
                                didx3, ws3)
 
-        for _ in range(2):
+        for _ in range(args.prefill_warmup):  # untimed, as for the prefill
             mixed_step()
         ms_mix = time_region(mixed_step, max(3, args.prefill_steps), torch)
         dec_b = 384 * decode_bytes_per_row(d3, 4)[2]
