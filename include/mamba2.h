@@ -218,8 +218,14 @@ int mamba2_mixed_fwd(const mamba2_dims *dims, const void *xbc, const void *dt_ra
  * For the fused shape (headdim 64, dstate 128, out_dtype bf16) it holds the
  * post-conv B/C operands of each 32-token block of the packed batch: C
  * (G*N bf16 per token), B^T as hi/lo bf16 (2*G*N per token) and C.B^T
- * (G*32 fp32 per token), each region rounded up to 256 bytes; otherwise the
- * post-conv xBC, Cdim elements of xbc_dtype per token. */
+ * (G*32 fp32 per token), each region rounded up to 256 bytes; from 2048
+ * tokens on it also holds what the segment mode needs, used when few
+ * sequences (nseq*H <= 256) would leave most of the GPU idle: each long
+ * sequence is then cut into up to 8 segments scanned in parallel from zero
+ * state and joined afterwards by linearity (512/H segment records, their
+ * final states in fp32 and as bf16 MFMA operands, H*P*N*6 bytes per record
+ * with the per-head decays, and one fp32 log-decay per block and head);
+ * otherwise the post-conv xBC, Cdim elements of xbc_dtype per token. */
 int mamba2_prefill_workspace_bytes(const mamba2_dims *dims, int64_t total_tokens, size_t *bytes);
 
 /* Whole prefill of the mixer's SSM core over packed sequences: conv1d + SiLU,

@@ -47,6 +47,8 @@
 // With conv width W = 1 both kernels take post-conv xBC as it is (no conv, no
 // SiLU, no context rows): that instantiation is mamba2_chunk_scan_fwd's form
 // when the caller passes a workspace.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma.hpp"
@@ -74,6 +76,10 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
     v += dpp_add_src<0x143, 0xC>(v);        // row_bcast:31 into rows 2 and 3
     return v;
 }
+
+// segment flags (segment mode): the sequence's first segment; its only one
+constexpr int kSegFirst = 1, kSegOnly = 2;
+constexpr int kMinSeg = 1024;  // tokens per segment at least
 
 }  // namespace
 
@@ -390,10 +396,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
     const int col = lane & 15, q = lane >> 4;
     __shared__ int sSeq;
-    const int head = xcd_head(blockIdx.x, H), seq = seq_longest_first(a.cu, a.nseq, blockIdx.y, tid, NT, &sSeq);
+    const int head = xcd_head(blockIdx.x, H);
+    // the workgroup's tokens: a whole sequence, or in segment mode one segment of one
+    int seq, sflags;
+    int64_t start, end;
+    if (a.seg) {
+        const int32_t *sg = a.seg + 4 * blockIdx.y;
+        start = sg[0];
+        end = sg[1];
+        seq = sg[2];
+        sflags = sg[3];
+    } else {
+        seq = seq_longest_first(a.cu, a.nseq, blockIdx.y, tid, NT, &sSeq);
+        start = a.cu[seq];
+        end = a.cu[seq + 1];
+        sflags = kSegFirst | kSegOnly;
+    }
+    // a later segment starts from zero state and reads its conv context from the tokens before it
+    const bool first = sflags & kSegFirst, only = sflags & kSegOnly;
     const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N, cdim = HP + 2 * GN;
     const int g = head / (H / G);
-    const int64_t start = a.cu[seq], end = a.cu[seq + 1];
     const int slot = a.idx[seq];
     bf16 *y = static_cast<bf16 *>(a.y);
 
@@ -407,7 +429,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     const float Dh = a.D[head];
     const int p = 16 * wv + col;  // this lane's channel inside the head (x operands, state column)
     const int64_t chx = (int64_t)head * P + p;
-    const bool init = a.has_init && a.has_init[seq];
+    const bool init = first && a.has_init && a.has_init[seq];
 
     float cw[W], ctx[CONV ? W - 1 : 1];
     float cbias = 0.0f;
@@ -481,11 +503,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             cr[i] = *reinterpret_cast<const u32x4 *>(cpb + min(clane + (uint32_t)(i * (NT / (N / 8))) * crow, cmax));
         const int lo = (int)(start - bL > -W ? start - bL : -W);           // first valid row, block-relative
         const int hi = (int)(end - 1 - bL < L + 8 ? end - 1 - bL : L + 8);  // last valid row
+        // first x row that holds data: a later segment's context rows are tokens of its sequence
+        const int xl = first ? lo : (int)(start - (W - 1) - bL > -W ? start - (W - 1) - bL : -W);
         const char *dtc = static_cast<const char *>(a.dt_raw) + (bL * H + head) * AS;
         dtr = ld_bits(reinterpret_cast<const AT *>(dtc + min(max(dtlane, (uint32_t)max(lo, 0) * H * AS), (uint32_t)hi * H * AS)));
         // raw x rows bL - (W-1) + rho, rho in [0, L + W - 1), of this wave's 16 channels
         const char *xc = static_cast<const char *>(a.xbc) + ((bL - (W - 1)) * cdim + (int64_t)head * P + 16 * wv) * XS;
-        const uint32_t xlo = (uint32_t)(lo + (W - 1) > 0 ? lo + (W - 1) : 0) * xrow, xhi = (uint32_t)(hi + (W - 1)) * xrow;
+        const uint32_t xlo = (uint32_t)(xl + (W - 1) > 0 ? xl + (W - 1) : 0) * xrow, xhi = (uint32_t)(hi + (W - 1)) * xrow;
 #pragma unroll
         for (int k = 0; k < XP; ++k)
             xq[k] = *reinterpret_cast<const u32x4 *>(xc + (min(max(xq_off[k], xlo), xhi) + xq_part[k]));
@@ -499,7 +523,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 
     // ---- staging of a block (from the prefetch registers) for the next iteration
     bf16x8 X[KL], XD[KL], XSh[KL], XSl[KL];  // x, x dt, (x w) hi / lo: k-slots 32m + 8q + j of channel p
-    float el[TL], dec = 1.0f;                // exp(lam_t) for t = 16 tt + col; exp(lam_end)
+    float el[TL], dec = 1.0f, l2e = 0.0f;    // exp(lam_t) for t = 16 tt + col; exp(lam_end); lam_end (log2)
+    float lsum = 0.0f;                       // log2 of the decay over the blocks computed so far
     // tiles of block b into LDS buffer buf: B^T and C (shared), raw x rows (this wave's)
     auto stage_tiles = [&](int64_t b, int buf) {
         const int64_t bL = b * L;
@@ -531,7 +556,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
         const int64_t bL = b * L;
         const int lo = (int)(start - bL > 0 ? start - bL : 0);
         const int hi = (int)(end - bL < L ? end - bL : L);
-        const int ctxlo = (int)(start - bL > -W ? start - bL : -W);  // sequence start, block-relative
+        // sequence start, block-relative (a later segment has none: its context rows are real tokens)
+        const int ctxlo = first ? (int)(start - bL > -W ? start - bL : -W) : -W;
         // token arrays, every wave its own copy: dt, inclusive lam, dt exp(lam_end - lam)
         {
             // (softplus for every lane, then a multiply by 0 / 1: no branch around it)
@@ -542,6 +568,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             sTok[wv][1][lane] = v;
             sTok[wv][2][lane] = dt * __builtin_amdgcn_exp2f(l2end - v);
             dec = __builtin_amdgcn_exp2f(l2end);
+            l2e = l2end;
         }
         const char *xt = sXr[wv];  // (rows written by this wave in the tile pass)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -639,6 +666,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
         bf16x8 Xc[KL], XDc[KL], XShc[KL], XSlc[KL];
         float elc[TL];
         const float decc = dec;
+        lsum += l2e;
+        if (a.seg && tid == 0 && bL >= start && bL + L <= end) a.seg_lam[b * H + head] = lsum;
 #pragma unroll
         for (int m = 0; m < KL; ++m) { Xc[m] = X[m]; XDc[m] = XD[m]; XShc[m] = XSh[m]; XSlc[m] = XSl[m]; }
 #pragma unroll
@@ -732,10 +761,259 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
         __syncthreads();
     }
 
+    if (!only) {
+        // a segment of a longer sequence: its local final state and total decay, for the fix-up pass
+        float *gs = a.seg_state + (((int64_t)blockIdx.y * H + head) * P + p) * N;
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt) *reinterpret_cast<f32x4 *>(gs + 16 * nt + 4 * q) = Hacc[nt];
+        if (tid == 0) a.seg_dec[(int64_t)blockIdx.y * H + head] = lsum;
+        return;
+    }
 #pragma unroll
     for (int nt = 0; nt < NTL; ++nt) {
         const float v[4] = {Hacc[nt][0], Hacc[nt][1], Hacc[nt][2], Hacc[nt][3]};
         store_k<ST, 4>(pool_h + 16 * nt + 4 * q, v);
+    }
+}
+
+// ---------------------------------------------------------------- segment mode
+// With few sequences (nseq * H well under the two workgroups per CU the scan fits),
+// a long sequence is cut into up to smax segments of whole 32-token blocks, each at
+// least kMinSeg tokens, scanned in parallel: the first from the sequence's initial
+// state, the others from zero. The exact result follows from the linearity of the
+// recurrence in the state: the true state entering segment v is
+//   H_in(v) = sum_{u < v} exp2(lam_u) ... H_u,  built as H <- exp2(lam_u) H + H_u over u,
+// (H_u: segment u's local final state, lam_u: its total log2 decay), and the tokens
+// of segment v miss exactly exp2(lam_t) C_t . H_in(v) in y (lam_t: log2 decay from
+// the segment's start through t), the carried-state output term of the scan.
+
+// seg[v] for v = r * smax + k: segment k of sequence r (empty past its last one)
+__global__ __launch_bounds__(256) void fused_seg_plan_kernel(const int32_t *cu, int nseq, int smax, int32_t *seg) {
+    const int v = blockIdx.x * 256 + threadIdx.x;
+    if (v >= nseq * smax) return;
+    const int r = v / smax, k = v % smax;
+    const int s0 = cu[r], s1 = cu[r + 1], len = s1 - s0;
+    const int S = max(1, min(smax, len / kMinSeg));
+    const int step = (len + S - 1) / S;
+    auto bound = [&](int i) {  // segment boundaries at multiples of 32 of the packed position
+        if (i <= 0) return s0;
+        if (i >= S) return s1;
+        return min((s0 + i * step + 31) / 32 * 32, s1);
+    };
+    int32_t *o = seg + 4 * v;
+    o[0] = k < S ? bound(k) : s1;
+    o[1] = k < S ? bound(k + 1) : s1;
+    o[2] = r;
+    o[3] = k < S ? ((k == 0 ? kSegFirst : 0) | (S == 1 ? kSegOnly : 0)) : 0;
+}
+
+// True initial state of each later segment (one workgroup of four waves per (head,
+// segment), the scan's lane layout: wave w, lane (col, q) holds H[16 w + col][16 nt +
+// 4 q + r]), kept as the bf16 A operand of the fix-up MFMAs; for the sequence's last
+// segment, the true final state into the pool.
+template <typename ST>
+__global__ __launch_bounds__(256) void fused_seg_combine_kernel(FusedArgs a, int H, int smax) {
+    constexpr int P = 64, N = 128, KN = 4, NTL = 8;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, q = lane >> 4;
+    const int head = blockIdx.x, v = blockIdx.y, k = v % smax;
+    const int32_t *sg = a.seg + 4 * v;
+    if (k == 0 || sg[0] >= sg[1]) return;  // first segments are exact; empty ones hold no tokens
+    const int slot = a.idx[sg[2]];
+    if (slot < 0) return;
+    const bool last = k + 1 == smax || a.seg[4 * (v + 1)] >= a.seg[4 * (v + 1) + 1];
+    const int p = 16 * wv + col;
+    // H <- exp2(lam_u) H + H_u over the earlier segments u of the sequence
+    f32x4 Hin[NTL];
+#pragma unroll
+    for (int nt = 0; nt < NTL; ++nt) Hin[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int u = v - k; u < v; ++u) {
+        const float d = __builtin_amdgcn_exp2f(a.seg_dec[(int64_t)u * H + head]);
+        const float *gs = a.seg_state + (((int64_t)u * H + head) * P + p) * N;
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt) Hin[nt] = Hin[nt] * d + *reinterpret_cast<const f32x4 *>(gs + 16 * nt + 4 * q);
+    }
+    // the A operand of the carried-state output (k-slots in the permuted n order of the C plane)
+    bf16x8 *hb = static_cast<bf16x8 *>(a.seg_hin) + (((int64_t)v * H + head) * 4 + wv) * 64 * KN + lane * KN;
+#pragma unroll
+    for (int kn = 0; kn < KN; ++kn) {
+        bf16x8 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            o[r] = f32_to_bf16(Hin[2 * kn][r]);
+            o[4 + r] = f32_to_bf16(Hin[2 * kn + 1][r]);
+        }
+        hb[kn] = o;
+    }
+    if (last) {
+        const float d = __builtin_amdgcn_exp2f(a.seg_dec[(int64_t)v * H + head]);
+        const float *gs = a.seg_state + (((int64_t)v * H + head) * P + p) * N;
+        ST *pool_h = static_cast<ST *>(a.pool) + ((int64_t)slot * H + head) * (int64_t)P * N + (int64_t)p * N;
+#pragma unroll
+        for (int nt = 0; nt < NTL; ++nt) {
+            const f32x4 hf = Hin[nt] * d + *reinterpret_cast<const f32x4 *>(gs + 16 * nt + 4 * q);
+            const float o[4] = {hf[0], hf[1], hf[2], hf[3]};
+            store_k<ST, 4>(pool_h + 16 * nt + 4 * q, o);
+        }
+    }
+}
+
+// y += exp2(lam_t) C_t . H_in (times SiLU(z)) for the tokens of later segments; one
+// workgroup per (head, kFixBlocks consecutive 32-token blocks). A block holds tokens of
+// at most one later segment: those start at block boundaries and span many blocks.
+// Every block's loads are issued the same way (addresses clamped, stores masked), one
+// block ahead of the block being applied, and values are widened only where used, so
+// the compiler's waits count just the loads of the block being applied. The block's C
+// rows are read from HBM/L2 once per workgroup and shared by its 4 waves through LDS
+// (two buffers, one barrier per block; every wave passes every barrier). lam_t only
+// falls along a segment, so once exp2 of it is exactly 0 in fp32 every later token of
+// the segment would add exactly 0, and the workgroup stops there.
+constexpr int kFixBlocks = 16;
+template <typename AT, bool HasZ>
+__global__ __launch_bounds__(256) void fused_seg_fix_kernel(FusedArgs a, int H, int G, int nseg, int smax) {
+    constexpr int P = 64, N = 128, L = 32, TL = 2, KN = 4;
+    constexpr int CS = N + 8;  // LDS row stride (bf16): 16-byte reads of 8 rows hit distinct banks
+    __shared__ __align__(16) bf16 sC[2][L * CS];
+    constexpr float LOG2E = 1.4426950408889634f;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, q = lane >> 4;
+    const int head = xcd_head(blockIdx.x, H);
+    const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N;
+    const int g = head / (H / G);
+    const int64_t nblk = (a.T + L - 1) / L;
+    const int64_t b0 = (int64_t)blockIdx.y * kFixBlocks, b1 = b0 + kFixBlocks < nblk ? b0 + kFixBlocks : nblk;
+    const AT *dtr = static_cast<const AT *>(a.dt_raw);
+    const AT *zr = static_cast<const AT *>(a.z);
+    const bf16 *cp = static_cast<const bf16 *>(a.cp);
+    bf16 *y = static_cast<bf16 *>(a.y);
+
+    // The later segment holding position pos, [sstart, send), with sv its record (-1 if
+    // there is none or it is a padding row's); where there is none, send is the start
+    // of the next later segment. A scalar search of the few records, run again only
+    // once the blocks reach send.
+    int sv = -1;
+    int64_t sstart = 0, send = -1;
+    auto locate = [&](int64_t pos) {
+        if (pos < send) return;
+        bool found = false;
+        int64_t next = INT64_MAX;
+        sv = -1;
+        for (int u = 0; u < nseg; ++u) {
+            const int32_t *sg = a.seg + 4 * u;
+            const int64_t s0 = sg[0], s1 = sg[1];
+            if (u % smax == 0 || s0 >= s1) continue;  // first segments need no fix; empty records
+            if (s0 <= pos && pos < s1) {
+                found = true;
+                sstart = s0;
+                send = s1;
+                sv = a.idx[sg[2]] < 0 ? -1 : u;
+            } else if (s0 > pos && s0 < next) {
+                next = s0;
+            }
+        }
+        if (!found) {
+            sstart = pos;
+            send = next;
+        }
+    };
+    if (b0 >= b1) return;
+    locate(b0 * L);
+    if (sv < 0 && send >= b1 * L) return;  // nothing to fix in these blocks
+
+    struct Blk {
+        int64_t bL, send;
+        int v, hi;
+        bool first;
+        float carry;
+        AT dtraw;
+        u32x4 c[2];  // this thread's 32 bytes of the block's C rows
+        bf16x4 yo[TL];
+        Raw<AT, 4> zv[TL];
+    };
+    auto fetch = [&](Blk &k, int64_t b) {
+        const int64_t bc = b < b1 ? b : b1 - 1;
+        k.bL = bc * L;
+        locate(k.bL);
+        k.v = b < b1 ? sv : -1;
+        const int64_t lim = sv >= 0 ? send : a.T;
+        k.hi = (int)(lim - k.bL < L ? lim - k.bL : L);  // >= 1: the block starts inside
+        k.first = k.bL == sstart;
+        k.send = send;
+        k.carry = a.seg_lam[(bc > 0 ? bc - 1 : 0) * H + head];
+        k.dtraw = dtr[(k.bL + (lane < k.hi ? lane : k.hi - 1)) * H + head];
+        {
+            const int row = tid >> 3, rc = row < k.hi ? row : k.hi - 1;  // rows past the segment repeat its last one
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(cp + (k.bL + rc) * GN + (int64_t)g * N + (tid & 7) * 16);
+            k.c[0] = src[0];
+            k.c[1] = src[1];
+        }
+#pragma unroll
+        for (int tt = 0; tt < TL; ++tt) {
+            const int t = 16 * tt + col, tc = t < k.hi ? t : k.hi - 1;
+            const int64_t off = (k.bL + tc) * HP + (int64_t)head * P + 16 * wv + 4 * q;
+            k.yo[tt] = *reinterpret_cast<const bf16x4 *>(y + off);
+            if constexpr (HasZ) k.zv[tt].load(zr + off);
+        }
+    };
+    const float A2 = -expf(a.A_log[head]) * LOG2E;
+    const float dtb = a.dt_bias[head];
+    bf16x8 Hb[KN];
+    int hv = -1;
+    constexpr float kDead = -160.0f;  // exp2 of anything below is 0 in fp32
+    // true: this block and the rest of the workgroup's blocks add nothing (one segment)
+    auto done = [&](const Blk &k) {
+        const float c = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(k.carry)));
+        return k.v >= 0 && !k.first && c < kDead && k.send >= b1 * L;
+    };
+    auto apply = [&](const Blk &k, bf16 *sc) {
+        u32x4 *dst = reinterpret_cast<u32x4 *>(sc + (tid >> 3) * CS + (tid & 7) * 16);
+        dst[0] = k.c[0];
+        dst[1] = k.c[1];
+        __syncthreads();
+        if (k.v < 0) return;
+        if (k.v != hv) {  // a new segment: its H_in (rare, so waiting for it here is fine)
+            hv = k.v;
+            const bf16x8 *hb = static_cast<const bf16x8 *>(a.seg_hin) + (((int64_t)hv * H + head) * 4 + wv) * 64 * KN + lane * KN;
+#pragma unroll
+            for (int kn = 0; kn < KN; ++kn) Hb[kn] = hb[kn];
+            // used here, so the wait for these loads stays on this path
+            asm volatile("" ::"v"(Hb[0]), "v"(Hb[1]), "v"(Hb[2]), "v"(Hb[3]));
+        }
+        // lam_t: log2 decay from the segment's start through token t
+        const float dt = lane < k.hi ? softplus_fast((float)k.dtraw + dtb) : 0.0f;
+        const float lam = wave_prefix_sum(dt * A2) + (k.first ? 0.0f : k.carry);
+#pragma unroll
+        for (int tt = 0; tt < TL; ++tt) {
+            const int t = 16 * tt + col;
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kn = 0; kn < KN; ++kn)
+                acc = mma(Hb[kn], *reinterpret_cast<const bf16x8 *>(sc + (16 * tt + col) * CS + 32 * kn + 8 * q), acc);
+            const float el = __builtin_amdgcn_exp2f(__shfl(lam, t));
+            if (t < k.hi) {
+                bf16x4 o = k.yo[tt];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float gate = 1.0f;
+                    if constexpr (HasZ) gate = silu_fast(k.zv[tt][r]);
+                    o[r] = f32_to_bf16((float)o[r] + acc[r] * el * gate);
+                }
+                *reinterpret_cast<bf16x4 *>(y + (k.bL + t) * HP + (int64_t)head * P + 16 * wv + 4 * q) = o;
+            }
+        }
+    };
+    // Two buffers in turn: a copy of one into the other would wait for its loads.
+    Blk k0, k1;
+    fetch(k0, b0);
+    for (int64_t b = b0; b < b1; b += 2) {
+        fetch(k1, b + 1);
+        if (done(k0)) break;
+        apply(k0, sC[0]);
+        fetch(k0, b + 2);
+        if (done(k1)) break;
+        apply(k1, sC[1]);
     }
 }
 
@@ -747,51 +1025,96 @@ constexpr int kFusedL = 32;
 int64_t up256(int64_t v) { return (v + 255) / 256 * 256; }
 
 struct FusedLayout {
-    int64_t nblk, cp, bt, cb, bytes;  // block count and byte offsets / total
+    int64_t nblk, cp, bt, cb, seg, segdec, segstate, seglam, seghin, bytes;  // block count and byte offsets / total
 };
+
+// Segments the segment mode may use: nseq * smax <= 512 / H (see seg_max), and only
+// from 2 * kMinSeg tokens; their states take at most 512 * P * N * 4 bytes (16 MiB at
+// P = 64, N = 128).
+int64_t max_segments(const LayerShape &s, int64_t T) { return T >= 2 * kMinSeg ? 512 / s.H : 0; }
 
 FusedLayout fused_layout(const LayerShape &s, int64_t T) {
     FusedLayout f;
     const int64_t L = kFusedL;
+    const int64_t nv = max_segments(s, T);
     f.nblk = (T + L - 1) / L;
     f.cp = 0;
     f.bt = up256(T * s.G * s.N * 2);
     f.cb = f.bt + up256(f.nblk * s.G * 2 * s.N * L * 2);
-    f.bytes = f.cb + up256(f.nblk * s.G * L * L * 4);
+    f.seg = f.cb + up256(f.nblk * s.G * L * L * 4);
+    f.segdec = f.seg + up256(nv * 4 * 4);
+    f.segstate = f.segdec + up256(nv * s.H * 4);
+    f.seglam = f.segstate + up256(nv * s.H * s.P * s.N * 4);
+    f.seghin = f.seglam + up256(nv ? f.nblk * s.H * 4 : 0);
+    f.bytes = f.seghin + up256(nv * s.H * s.P * s.N * 2);
     return f;
+}
+
+// Segments per sequence for a batch of few sequences (0: one workgroup per sequence): while
+// nseq * H streams leave at least half the 512 workgroup slots (two per CU) empty.
+int seg_max(const LayerShape &s, const FusedArgs &a) {
+    if (a.T < 2 * kMinSeg || (int64_t)a.nseq * s.H > 256) return 0;
+    const int smax = (int)std::min<int64_t>(8, 512 / ((int64_t)a.nseq * s.H));
+    return smax >= 2 ? smax : 0;
 }
 
 // W == 1: post-conv xbc of type XT (chunk scan alone); W >= 2: raw xbc of type AT
 template <int W, typename ST, typename AT, typename XT>
-hipError_t launch_fw(const LayerShape &s, const FusedArgs &a, int64_t nblk, hipStream_t stream) {
+hipError_t launch_fw(const LayerShape &s, const FusedArgs &a, int64_t nblk, int smax, hipStream_t stream) {
+    hipError_t e;
+    if (smax) {
+        const int nv = a.nseq * smax;
+        hipLaunchKernelGGL(fused_seg_plan_kernel, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, stream, a.cu, a.nseq,
+                           smax, const_cast<int32_t *>(a.seg));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (nblk > 0) {  // no tokens (only empty sequences): the scan alone writes their states
         hipLaunchKernelGGL((fused_prep_kernel<XT, ST, W, kFusedL>), dim3((unsigned)nblk, s.G), dim3(256), 0, stream, a,
                            s.H, s.G);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((fused_scan_kernel<kFusedL, W, ST, AT, XT>), dim3(s.H, a.nseq), dim3(256), 0, stream, a,
-                       s.H, s.G);
-    return hipGetLastError();
+    hipLaunchKernelGGL((fused_scan_kernel<kFusedL, W, ST, AT, XT>), dim3(s.H, smax ? a.nseq * smax : a.nseq), dim3(256),
+                       0, stream, a, s.H, s.G);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (smax && nblk > 0) {
+        const int nv = a.nseq * smax;
+        hipLaunchKernelGGL((fused_seg_combine_kernel<ST>), dim3(s.H, nv), dim3(256), 0, stream, a, s.H, smax);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const dim3 fg(s.H, (unsigned)((nblk + kFixBlocks - 1) / kFixBlocks));
+        if (a.z)
+            hipLaunchKernelGGL((fused_seg_fix_kernel<AT, true>), fg, dim3(256), 0, stream, a, s.H, s.G, nv, smax);
+        else
+            hipLaunchKernelGGL((fused_seg_fix_kernel<AT, false>), fg, dim3(256), 0, stream, a, s.H, s.G, nv, smax);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 template <typename ST, typename AT>
-hipError_t launch_fa(const LayerShape &s, const FusedArgs &a, int64_t nblk, hipStream_t stream) {
+hipError_t launch_fa(const LayerShape &s, const FusedArgs &a, int64_t nblk, int smax, hipStream_t stream) {
     switch (s.W) {
-        case 2: return launch_fw<2, ST, AT, AT>(s, a, nblk, stream);
-        case 3: return launch_fw<3, ST, AT, AT>(s, a, nblk, stream);
-        case 4: return launch_fw<4, ST, AT, AT>(s, a, nblk, stream);
+        case 2: return launch_fw<2, ST, AT, AT>(s, a, nblk, smax, stream);
+        case 3: return launch_fw<3, ST, AT, AT>(s, a, nblk, smax, stream);
+        case 4: return launch_fw<4, ST, AT, AT>(s, a, nblk, smax, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-void set_workspace(const LayerShape &s, FusedArgs &a, void *workspace, int64_t *nblk) {
+// Workspace planes, and the segment arrays when the batch runs in segment mode
+// (*smax > 0; a.seg stays null otherwise).
+void set_workspace(const LayerShape &s, FusedArgs &a, void *workspace, int64_t *nblk, int *smax) {
     const FusedLayout f = fused_layout(s, a.T);
     char *ws = static_cast<char *>(workspace);
     a.cp = ws ? ws + f.cp : nullptr;
     a.bt = ws ? ws + f.bt : nullptr;
     a.cb = ws ? ws + f.cb : nullptr;
     *nblk = f.nblk;
+    *smax = ws ? seg_max(s, a) : 0;
+    a.seg = *smax ? reinterpret_cast<const int32_t *>(ws + f.seg) : nullptr;
+    a.seg_dec = *smax ? reinterpret_cast<float *>(ws + f.segdec) : nullptr;
+    a.seg_state = *smax ? reinterpret_cast<float *>(ws + f.segstate) : nullptr;
+    a.seg_lam = *smax ? reinterpret_cast<float *>(ws + f.seglam) : nullptr;
+    a.seg_hin = *smax ? static_cast<void *>(ws + f.seghin) : nullptr;
 }
 
 }  // namespace
@@ -809,21 +1132,25 @@ int64_t fused_workspace_bytes(const LayerShape &s, int64_t T) { return fused_lay
 hipError_t launch_fused_prefill(const LayerShape &s, FusedArgs a, void *workspace, hipStream_t stream) {
     if (a.nseq == 0) return hipSuccess;
     int64_t nblk = 0;
-    set_workspace(s, a, workspace, &nblk);
+    int smax = 0;
+    set_workspace(s, a, workspace, &nblk, &smax);
     if (s.state_dt == DT_BF16)
-        return s.act_dt == DT_BF16 ? launch_fa<bf16, bf16>(s, a, nblk, stream) : launch_fa<bf16, float>(s, a, nblk, stream);
-    return s.act_dt == DT_BF16 ? launch_fa<float, bf16>(s, a, nblk, stream) : launch_fa<float, float>(s, a, nblk, stream);
+        return s.act_dt == DT_BF16 ? launch_fa<bf16, bf16>(s, a, nblk, smax, stream)
+                                   : launch_fa<bf16, float>(s, a, nblk, smax, stream);
+    return s.act_dt == DT_BF16 ? launch_fa<float, bf16>(s, a, nblk, smax, stream)
+                               : launch_fa<float, float>(s, a, nblk, smax, stream);
 }
 
 hipError_t launch_block_scan(const LayerShape &s, FusedArgs a, void *workspace, hipStream_t stream) {
     if (a.nseq == 0) return hipSuccess;
     int64_t nblk = 0;
-    set_workspace(s, a, workspace, &nblk);
+    int smax = 0;
+    set_workspace(s, a, workspace, &nblk, &smax);
     if (s.state_dt == DT_BF16)
-        return s.xbc_dt == DT_BF16 ? launch_fw<1, bf16, bf16, bf16>(s, a, nblk, stream)
-                                   : launch_fw<1, bf16, bf16, float>(s, a, nblk, stream);
-    return s.xbc_dt == DT_BF16 ? launch_fw<1, float, bf16, bf16>(s, a, nblk, stream)
-                               : launch_fw<1, float, bf16, float>(s, a, nblk, stream);
+        return s.xbc_dt == DT_BF16 ? launch_fw<1, bf16, bf16, bf16>(s, a, nblk, smax, stream)
+                                   : launch_fw<1, bf16, bf16, float>(s, a, nblk, smax, stream);
+    return s.xbc_dt == DT_BF16 ? launch_fw<1, float, bf16, bf16>(s, a, nblk, smax, stream)
+                               : launch_fw<1, float, bf16, float>(s, a, nblk, smax, stream);
 }
 
 }  // namespace m2

@@ -96,6 +96,15 @@ struct FusedArgs {
     int nseq;
     int64_t T;
     void *cp, *bt, *cb;
+    // segment mode (small batches; set by the launcher): workgroup row v takes segment v
+    // of seg [nseg][4] = {start, end, sequence, flags} and, unless it is its sequence's
+    // only segment, leaves its local final state and total log2 decay in seg_state /
+    // seg_dec for the fix-up pass
+    const int32_t *seg;
+    float *seg_state;  // [nseg][H][P][N]
+    float *seg_dec;    // [nseg][H]
+    float *seg_lam;    // [block][H]: log2 decay from the segment's start through the block (blocks inside a segment)
+    void *seg_hin;     // [nseg][H][4 waves][64 lanes][4] bf16x8: a later segment's true initial state, as MFMA operand
 };
 
 struct NormArgs {

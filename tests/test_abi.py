@@ -51,7 +51,8 @@ def test_slot_sizes_match_page_arithmetic(lib):
     assert B.mamba2_ssm_slot_bytes(d.with_(state_dtype=F32)) == 2 * g["ssm_bytes_per_layer_per_seq"]
     assert B.mamba2_conv_slot_bytes(d) == 3 * (128 * 64 + 2 * 8 * 128) * 2
     # the chunk scan's optional workspace: the prefill's B/C planes for P=64, N=128, bf16 act/y; none elsewhere
-    assert B.mamba2_chunk_scan_workspace_bytes(NEMOTRON_H_8B, 32768, 4) == 32768 * (3 * 8 * 128 * 2 + 8 * 32 * 4)
+    assert (B.mamba2_chunk_scan_workspace_bytes(NEMOTRON_H_8B, 32768, 4)
+            == B.mamba2_prefill_workspace_bytes(NEMOTRON_H_8B.with_(state_dtype=F32), 32768))
     assert (B.mamba2_chunk_scan_workspace_bytes(NEMOTRON_H_8B, 1000, 3)
             == B.mamba2_prefill_workspace_bytes(NEMOTRON_H_8B.with_(state_dtype=F32), 1000))
     assert B.mamba2_chunk_scan_workspace_bytes(NEMOTRON_H_8B.with_(out_dtype=F32), 32768, 4) == 0
@@ -144,9 +145,16 @@ def test_prefill_workspace_and_validation_without_gpu(lib):
     P = ctypes.c_void_p
     good = P(0x10000)
     d8 = NEMOTRON_H_8B.with_(state_dtype=F32)  # bf16 y: fused shape
-    # C, B^T hi/lo (bf16) and C.B^T (fp32 per 32-token block), each region padded to 256 bytes
-    assert B.mamba2_prefill_workspace_bytes(d8, 32768) == 32768 * (3 * 8 * 128 * 2 + 8 * 32 * 4)
+    # C, B^T hi/lo (bf16) and C.B^T (fp32 per 32-token block), each region padded to 256 bytes; from
+    # 2048 tokens also the small-batch mode's segment records, decays, local states (at most 512 / H
+    # segments: 16 MiB of fp32 states at P = 64, N = 128), per-block decays and bf16 initial states
     pad = lambda v: -(-v // 256) * 256
+    seg = lambda nv, H, nblk: (pad(nv * 16) + pad(nv * H * 4) + pad(nv * H * 64 * 128 * 4) + pad(nblk * H * 4)
+                               + pad(nv * H * 64 * 128 * 2))
+    assert (B.mamba2_prefill_workspace_bytes(d8, 32768)
+            == 32768 * (3 * 8 * 128 * 2 + 8 * 32 * 4) + seg(4, 128, 1024))
+    assert B.mamba2_prefill_workspace_bytes(d8, 2047) == (pad(2047 * 8 * 128 * 2) + pad(64 * 8 * 2 * 128 * 32 * 2)
+                                                          + pad(64 * 8 * 32 * 32 * 4))
     assert B.mamba2_prefill_workspace_bytes(d8, 33) == (pad(33 * 8 * 128 * 2) + pad(2 * 8 * 2 * 128 * 32 * 2)
                                                         + pad(2 * 8 * 32 * 32 * 4))
     d8f = d8.with_(out_dtype=F32)  # fp32 y: conv1d_fwd + chunk_scan_fwd through the workspace

@@ -235,8 +235,9 @@ def test_fused_full_size_sampled():
 
 
 def test_fused_long_sequence_resumed_sampled():
-    """One 32,768-token sequence resuming from a saved conv and SSM state (1,024 blocks of
-    carried state in one workgroup per head), checked on sampled heads and the conv cache."""
+    """One 32,768-token sequence resuming from a saved conv and SSM state (a single
+    sequence: cut into 4 segments of 8,192 tokens scanned in parallel and joined by the
+    fix-up pass), checked on sampled heads and the conv cache."""
     d = NEMOTRON_H_8B.with_(state_dtype=F32)
     print("[fused prefill] one 32768-token sequence, resumed", flush=True)
     w = synth.prefill_batch(d, seed=29, seqlens=[32768], num_slots=2, with_z=False, initial_state=True)
@@ -250,6 +251,48 @@ def test_fused_long_sequence_resumed_sampled():
         assert_close(yh[:, head * 64:(head + 1) * 64], yr, BF16, f"y head {head}")
         assert_close(host(ssm[sl, head]), hr, F32, f"state head {head}")
     assert np.array_equal(host(conv[sl]), w["xbc"][-3:].astype(np.float64))
+
+
+@pytest.mark.parametrize("state_dtype", [F32, BF16])
+def test_fused_segment_mode_matches_oracle(state_dtype):
+    """Few long sequences (3 sequences x 16 heads leave most workgroup slots empty): each
+    sequence of 2048 tokens or more is cut into segments of at least 1024 tokens scanned in
+    parallel and joined by the fix-up pass. Resumed and fresh sequences, z gate, against the
+    oracle (y, final states, conv cache)."""
+    d = D16B.with_(state_dtype=state_dtype)
+    print(f"[fused prefill] segment mode, state={state_dtype}", flush=True)
+    w = synth.prefill_batch(d, seed=41, seqlens=[5000, 37, 2500], num_slots=5, initial_state=True)
+    check_fused(d, w, has_init=np.array([1, 0, 1], np.uint8))
+
+
+@pytest.mark.parametrize("use_z", [False, True])
+def test_fused_segment_mode_strong_and_weak_decay(use_z):
+    """Segment mode where half of the heads decay by about 2^-10 per token (their
+    correction from earlier segments underflows to exactly 0 in fp32 after a few
+    tokens, so the fix-up pass stops early for them) and half barely decay (the
+    correction spans whole segments), with and without the z gate, against the oracle."""
+    d = D16B
+    w = synth.prefill_batch(d, seed=44, seqlens=[6000, 2600], num_slots=3, initial_state=True)
+    H = d.nheads
+    strong = np.arange(H) < H // 2
+    w["params"]["A_log"] = np.where(strong, np.log(16.0), 0.0).astype(np.float32)
+    w["params"]["dt_bias"] = np.where(strong, np.log(np.expm1(1.0)), np.log(np.expm1(1e-3))).astype(np.float32)
+    print(f"[fused prefill] segment mode, strong and weak decay, z={use_z}", flush=True)
+    check_fused(d, w, has_init=np.array([1, 1], np.uint8), use_z=use_z)
+
+
+def test_fused_segment_mode_padding_and_empty():
+    d = D16B
+    w = synth.prefill_batch(d, seed=42, seqlens=[3000, 0, 2200, 4100], num_slots=6, initial_state=True)
+    slots = w["slots"].copy()
+    slots[0] = -1  # a padding sequence cut into segments: y = 0, no slot touched
+    has_init = np.array([1, 1, 0, 1], np.uint8)
+    y, ssm, conv = run_fused(d, w, has_init=has_init, slots=slots)
+    cu = w["cu_seqlens"]
+    assert torch.all(y[int(cu[0]):int(cu[1])] == 0).item()
+    pad = int(w["slots"][0])
+    assert np.array_equal(host(ssm[pad]), w["ssm_pool"][pad].astype(np.float64))
+    check_fused(d, w, has_init=has_init, slots=slots)
 
 
 def test_mixed_batch_through_fused_prefill():

@@ -159,6 +159,15 @@ def test_block_scan_packing_invariance():
             assert_close(host(ssmi[sl]), host(ssm_all[sl]), d.state_dtype, f"state of sequence {i}")
 
 
+def test_block_scan_segment_mode_matches_oracle():
+    """chunk_scan_fwd with a workspace and few long sequences: the segment mode of the block
+    scan (segments scanned in parallel, then the fix-up pass), against the oracle."""
+    d = D16.with_(out_dtype=BF16)
+    print("[prefill parity] block scan, segment mode", flush=True)
+    w = synth.prefill_batch(d, seed=43, seqlens=[4100, 2048, 1], num_slots=4, initial_state=True)
+    check_prefill(d, w, has_init=np.array([0, 1, 1], np.uint8), ws=True)
+
+
 def test_block_scan_equals_chunk_scan():
     """The two forms of chunk_scan_fwd (32-token blocks with a workspace, chunks of 64
     without) agree within the bf16 y / fp32 state tolerances on the same post-conv input."""
