@@ -172,6 +172,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--prefill-warmup", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-fewer-seqs", action="store_true",
+                    help="skip the 1- and 2-sequence prefill timings (keeps per-kernel profiles to one workload)")
     ap.add_argument("--no-multi", action="store_true", help="skip the multi-token decode section")
     ap.add_argument("--no-mamba1", action="store_true", help="skip the Mamba-1 selective scan section")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -382,6 +384,20 @@ def main():
             scan_chunks()
         ms_chunks = time_region(scan_chunks, args.prefill_steps, torch)
         ms_cf = time_region(conv_fwd, args.prefill_steps, torch)
+        # the same call on the first 1 and 2 of the sequences: too few (sequence, head) workgroups to
+        # fill the GPU, so each sequence is cut into segments scanned in parallel (segment mode)
+        few = {}
+        for nb in (() if args.no_fewer_seqs else (1, 2)):
+            Tb = 8192 * nb
+
+            def few_step(Tb=Tb, nb=nb):
+                B.mamba2_prefill_fwd(d2, xbc2[:Tb], dt2[:Tb], None, cw2, None, A2, dtb2, D2, y2[:Tb], pool2, convp2,
+                                     cu2[:nb + 1], idx2[:nb], hi2[:nb], ws2)
+            for _ in range(3):
+                few_step()
+            ms_b = time_region(few_step, args.prefill_steps, torch)
+            few[f"{nb}x8192"] = {"ms_per_step": round(ms_b, 4), "tok_s": round(Tb / (ms_b * 1e-3), 1)}
+            log(f"prefill {nb} x 8192: {ms_b * 1e3:.1f} us/step ({Tb / (ms_b * 1e-3) / 1e6:.2f} M tok/s)")
         # algorithmic minimum of the whole prefill: raw bf16 xBC + dt in, bf16 y out, final fp32 states
         pb, pf = scan_algorithmic(d2, T, 4, 2, 2, 4)
         pre_gbs = pb / (ms_pre * 1e-3) / 1e9
@@ -409,6 +425,7 @@ def main():
                          "algorithmic_bytes_per_launch": pb, "algorithmic_flops_per_launch": pf,
                          "mfma_achieved_tflops": round(pre_tfs, 2),
                          "mfma_frac": round(pre_tfs / MFMA_BF16_PEAK_TFLOPS, 4)},
+            "fewer_sequences": few,
             "unfused": {
                 "ms_per_step": round(ms_unf, 4), "tok_s": round(T / (ms_unf * 1e-3), 1),
                 "step": "conv1d_fwd (fp32 post-conv xBC) + chunk_scan_fwd with a workspace",
