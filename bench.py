@@ -89,6 +89,19 @@ def time_region(fn, iters, torch):
     return s.elapsed_time(e) / iters
 
 
+def settle(fn, torch, ms=50.0):
+    """Run fn() untimed for about ms of wall time. The GPU's clocks ramp up under load: a
+    decode step timed right after a handful of warmup steps measured 4 % slower than after
+    this (198.7 against 191.2 us)."""
+    import time
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+
+
 def bench_stack(args, torch, np, B, synth, d, dev, bf, time_region):
     """48 Mamba-2 layers x 32 decode steps at several concurrencies, eager and as one
     captured HIP graph per run. Layer l has its own seeded parameters and an input
@@ -232,6 +245,7 @@ def main():
         conv_step()
         su_step()
 
+    settle(decode_step, torch)  # the first GPU work of the run: brings the clocks up
     for _ in range(args.warmup):
         decode_step()
     torch.cuda.synchronize()
