@@ -281,6 +281,15 @@ def test_fused_segment_mode_strong_and_weak_decay(use_z):
     check_fused(d, w, has_init=np.array([1, 1], np.uint8), use_z=use_z)
 
 
+def test_fused_segment_mode_with_gated_norm():
+    """Segment mode under the gated norm: the scan and the fix-up pass write ungated y,
+    the norm applies SiLU(z) afterwards, against the oracle."""
+    d = D16B
+    print("[fused prefill] segment mode + gated norm", flush=True)
+    w = synth.prefill_batch(d, seed=45, seqlens=[3000, 2100], num_slots=3, initial_state=True)
+    check_fused(d, w, has_init=np.array([1, 0], np.uint8), norm_w=synth.norm_weight(d, 45), eps=1e-5, group=64)
+
+
 def test_fused_segment_mode_padding_and_empty():
     d = D16B
     w = synth.prefill_batch(d, seed=42, seqlens=[3000, 0, 2200, 4100], num_slots=6, initial_state=True)
