@@ -862,14 +862,16 @@ __global__ __launch_bounds__(256) void fused_seg_combine_kernel(FusedArgs a, int
 // y += exp2(lam_t) C_t . H_in (times SiLU(z)) for the tokens of later segments; one
 // workgroup per (head, kFixBlocks consecutive 32-token blocks). A block holds tokens of
 // at most one later segment: those start at block boundaries and span many blocks.
-// Every block's loads are issued the same way (addresses clamped, stores masked), one
-// block ahead of the block being applied, and values are widened only where used, so
-// the compiler's waits count just the loads of the block being applied. The block's C
+// Every block's loads are issued the same way (addresses clamped, stores masked, every
+// loaded value used on every path), kFixNB - 1 blocks ahead of the block being applied,
+// and values are widened only where used, so the compiler's waits count just the loads
+// of the block being applied. The block's C
 // rows are read from HBM/L2 once per workgroup and shared by its 4 waves through LDS
 // (two buffers, one barrier per block; every wave passes every barrier). lam_t only
 // falls along a segment, so once exp2 of it is exactly 0 in fp32 every later token of
 // the segment would add exactly 0, and the workgroup stops there.
 constexpr int kFixBlocks = 16;
+constexpr int kFixNB = 3;  // register buffers of the fix-up pass
 template <typename AT, bool HasZ>
 __global__ __launch_bounds__(256) void fused_seg_fix_kernel(FusedArgs a, int H, int G, int nseg, int smax) {
     constexpr int P = 64, N = 128, L = 32, TL = 2, KN = 4;
@@ -972,8 +974,9 @@ __global__ __launch_bounds__(256) void fused_seg_fix_kernel(FusedArgs a, int H, 
         dst[0] = k.c[0];
         dst[1] = k.c[1];
         __syncthreads();
-        if (k.v < 0) return;
-        if (k.v != hv) {  // a new segment: its H_in (rare, so waiting for it here is fine)
+        // a block with nothing to fix (v < 0) still runs the arithmetic on its loaded values
+        // (every load is then used on every path) and only its stores are masked
+        if (k.v >= 0 && k.v != hv) {  // a new segment: its H_in (rare, so waiting for it here is fine)
             hv = k.v;
             const bf16x8 *hb = static_cast<const bf16x8 *>(a.seg_hin) + (((int64_t)hv * H + head) * 4 + wv) * 64 * KN + lane * KN;
 #pragma unroll
@@ -992,7 +995,7 @@ __global__ __launch_bounds__(256) void fused_seg_fix_kernel(FusedArgs a, int H, 
             for (int kn = 0; kn < KN; ++kn)
                 acc = mma(Hb[kn], *reinterpret_cast<const bf16x8 *>(sc + (16 * tt + col) * CS + 32 * kn + 8 * q), acc);
             const float el = __builtin_amdgcn_exp2f(__shfl(lam, t));
-            if (t < k.hi) {
+            if (k.v >= 0 && t < k.hi) {
                 bf16x4 o = k.yo[tt];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -1004,16 +1007,19 @@ __global__ __launch_bounds__(256) void fused_seg_fix_kernel(FusedArgs a, int H, 
             }
         }
     };
-    // Two buffers in turn: a copy of one into the other would wait for its loads.
-    Blk k0, k1;
-    fetch(k0, b0);
-    for (int64_t b = b0; b < b1; b += 2) {
-        fetch(k1, b + 1);
-        if (done(k0)) break;
-        apply(k0, sC[0]);
-        fetch(k0, b + 2);
-        if (done(k1)) break;
-        apply(k1, sC[1]);
+    // kFixNB register buffers in turn (a copy of one into another would wait for its loads):
+    // block b + kFixNB - 1 is fetched into the buffer block b - 1 has just left, so kFixNB - 1
+    // blocks' loads are in flight while one is applied; LDS buffers alternate by block.
+    Blk kb[kFixNB];
+#pragma unroll
+    for (int i = 0; i < kFixNB - 1; ++i) fetch(kb[i], b0 + i);
+    // straight-line over the workgroup's blocks (blocks past b1 are clamped and masked), so
+    // the compiler's wait counts follow the buffers exactly
+#pragma unroll
+    for (int j = 0; j < kFixBlocks; ++j) {
+        fetch(kb[(j + kFixNB - 1) % kFixNB], b0 + j + kFixNB - 1);
+        if (done(kb[j % kFixNB])) return;  // the rest of the blocks add exactly 0 (uniform: every wave returns)
+        apply(kb[j % kFixNB], sC[j & 1]);
     }
 }
 
