@@ -81,13 +81,33 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
 constexpr int kSegFirst = 1, kSegOnly = 2;
 constexpr int kMinSeg = 1024;  // tokens per segment at least
 
+// Segment mode's plan, seg[v] for v = r * smax + k: segment k of sequence r (empty
+// past its last one) as {start, end, sequence, first/only flags}; written by the
+// first workgroup of the prep kernel, read by the scan and the passes after it.
+__device__ __forceinline__ void seg_plan(const int32_t *cu, int smax, int v, int32_t *seg) {
+    const int r = v / smax, k = v % smax;
+    const int s0 = cu[r], s1 = cu[r + 1], len = s1 - s0;
+    const int S = max(1, min(smax, len / kMinSeg));
+    const int step = (len + S - 1) / S;
+    auto bound = [&](int i) {  // segment boundaries at multiples of 32 of the packed position
+        if (i <= 0) return s0;
+        if (i >= S) return s1;
+        return min((s0 + i * step + 31) / 32 * 32, s1);
+    };
+    int32_t *o = seg + 4 * v;
+    o[0] = k < S ? bound(k) : s1;
+    o[1] = k < S ? bound(k + 1) : s1;
+    o[2] = r;
+    o[3] = k < S ? ((k == 0 ? kSegFirst : 0) | (S == 1 ? kSegOnly : 0)) : 0;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- prep
 // XT: xbc element type. W == 1: xbc is already conv + SiLU output and its B/C
 // rows are taken as they are.
 template <typename XT, typename ST, int W, int L>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(XT) == 2 ? 4 : 1))) void fused_prep_kernel(FusedArgs a, int H, int G) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(XT) == 2 ? 4 : 1))) void fused_prep_kernel(FusedArgs a, int H, int G, int smax) {
     constexpr bool CONV = W > 1;
     constexpr int P = 64, N = 128;
     constexpr int RL = L / 8;   // tokens per thread
@@ -105,6 +125,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(XT) 
     const int blk = blockIdx.x, g = blockIdx.y;
     // one coalesced load of cu_seqlens per workgroup, then searches in LDS (global
     // binary search, one dependent load per step, past kCu sequences)
+    if (smax && blockIdx.x == 0 && blockIdx.y == 0)  // segment mode: the plan (the scan runs after this kernel)
+        for (int v = threadIdx.x; v < a.nseq * smax; v += 256) seg_plan(a.cu, smax, v, const_cast<int32_t *>(a.seg));
     const bool cu_lds = CONV && a.nseq <= kCu;
     if (cu_lds)
         for (int i = tid; i <= a.nseq; i += 256) sCu[i] = a.cu[i];
@@ -787,26 +809,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 // of segment v miss exactly exp2(lam_t) C_t . H_in(v) in y (lam_t: log2 decay from
 // the segment's start through t), the carried-state output term of the scan.
 
-// seg[v] for v = r * smax + k: segment k of sequence r (empty past its last one)
-__global__ __launch_bounds__(256) void fused_seg_plan_kernel(const int32_t *cu, int nseq, int smax, int32_t *seg) {
-    const int v = blockIdx.x * 256 + threadIdx.x;
-    if (v >= nseq * smax) return;
-    const int r = v / smax, k = v % smax;
-    const int s0 = cu[r], s1 = cu[r + 1], len = s1 - s0;
-    const int S = max(1, min(smax, len / kMinSeg));
-    const int step = (len + S - 1) / S;
-    auto bound = [&](int i) {  // segment boundaries at multiples of 32 of the packed position
-        if (i <= 0) return s0;
-        if (i >= S) return s1;
-        return min((s0 + i * step + 31) / 32 * 32, s1);
-    };
-    int32_t *o = seg + 4 * v;
-    o[0] = k < S ? bound(k) : s1;
-    o[1] = k < S ? bound(k + 1) : s1;
-    o[2] = r;
-    o[3] = k < S ? ((k == 0 ? kSegFirst : 0) | (S == 1 ? kSegOnly : 0)) : 0;
-}
-
 // True initial state of each later segment (one workgroup of four waves per (head,
 // segment), the scan's lane layout: wave w, lane (col, q) holds H[16 w + col][16 nt +
 // 4 q + r]), kept as the bf16 A operand of the fix-up MFMAs; for the sequence's last
@@ -1068,15 +1070,10 @@ int seg_max(const LayerShape &s, const FusedArgs &a) {
 template <int W, typename ST, typename AT, typename XT>
 hipError_t launch_fw(const LayerShape &s, const FusedArgs &a, int64_t nblk, int smax, hipStream_t stream) {
     hipError_t e;
-    if (smax) {
-        const int nv = a.nseq * smax;
-        hipLaunchKernelGGL(fused_seg_plan_kernel, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, stream, a.cu, a.nseq,
-                           smax, const_cast<int32_t *>(a.seg));
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    // (segment mode needs tokens, so the prep kernel, which writes its plan, always runs then)
     if (nblk > 0) {  // no tokens (only empty sequences): the scan alone writes their states
         hipLaunchKernelGGL((fused_prep_kernel<XT, ST, W, kFusedL>), dim3((unsigned)nblk, s.G), dim3(256), 0, stream, a,
-                           s.H, s.G);
+                           s.H, s.G, smax);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL((fused_scan_kernel<kFusedL, W, ST, AT, XT>), dim3(s.H, smax ? a.nseq * smax : a.nseq), dim3(256),
