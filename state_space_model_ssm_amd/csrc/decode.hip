@@ -214,9 +214,14 @@ template <int K> __device__ __forceinline__ void store_row(void *p, int dt, int6
 //   otherwise (a snapshot after every token): rows base + g + it * kGrp, so one
 //     store instruction of a wave writes consecutive rows (1 KiB contiguous at
 //     N = 128 bf16); measured faster for the snapshot stream, slower without it.
-template <typename ST, typename XT, typename AT, int N, int ITERS, bool CONSEC>
-__global__ __launch_bounds__(256) void state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt,
-                                                                 int psplit) {
+// z is a template parameter (its registers only where it is used). The final-state
+// form without z on bf16 state and post-conv input asks for four waves per SIMD: six
+// spilled registers, measured 3 % faster than three waves without; the other forms
+// would spill more.
+template <typename ST, typename XT, typename AT, int N, int ITERS, bool CONSEC, bool HasZ>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    CONSEC && !HasZ && sizeof(ST) == 2 && sizeof(XT) == 2 ? 4 : 1))) void
+state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int psplit) {
     constexpr int kVec = Io<ST>::kVec;
     constexpr int kLpr = N / kVec;
     constexpr int kGrp = 256 / kLpr;  // row groups per workgroup
@@ -281,17 +286,17 @@ __global__ __launch_bounds__(256) void state_update_multi_kernel(MultiStepArgs a
     __shared__ __attribute__((aligned(16))) float sBC[TB][2][N];
     Raw<XT, 4> bcr;
     RawRow<XT, XK> xr[TB][XI];
-    RawRow<AT, XK> zr[TB][XI];
+    RawRow<AT, XK> zr[HasZ ? TB : 1][HasZ ? XI : 1];
     float dr = 0.0f;
     const XT *xh = static_cast<const XT *>(a.xbc) + (int64_t)row * T * cdim + (int64_t)head * P;
-    // (without z the pointer is formed over dt_raw and never read)
-    const AT *zh = static_cast<const AT *>(a.z ? a.z : a.dt_raw) + (a.z ? ybase : 0);
+    const AT *zh = static_cast<const AT *>(a.z) + ybase;
     auto xval = [&](int u, int it) {
         if constexpr (CONSEC) return xr[u][0][it];
         else return xr[u][it][0];
     };
     auto zval = [&](int u, int it) {
-        if constexpr (CONSEC) return zr[u][0][it];
+        if constexpr (!HasZ) return 1.0f;
+        else if constexpr (CONSEC) return zr[u][0][it];
         else return zr[u][it][0];
     };
     auto load_block = [&](int t0) {
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(256) void state_update_multi_kernel(MultiStepArgs a
         for (int u = 0; u < TB; ++u)
 #pragma unroll
             for (int i = 0; i < XI; ++i) xr[u][i].load(xh + (int64_t)min(t0 + u, T - 1) * cdim + pr[i]);
-        if (a.z)
+        if constexpr (HasZ)
 #pragma unroll
             for (int u = 0; u < TB; ++u)
 #pragma unroll
@@ -337,7 +342,9 @@ __global__ __launch_bounds__(256) void state_update_multi_kernel(MultiStepArgs a
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
             const int t = t0 + u;
-            if (t >= T) break;
+            // (skipped, not left with a break: a break makes the compiler keep a second copy
+            // of the state registers for the loop's exit)
+            if (t >= T) continue;
             float Bv[kVec], Cv[kVec];
 #pragma unroll
             for (int j = 0; j < kVec; j += 4) {
@@ -363,7 +370,7 @@ __global__ __launch_bounds__(256) void state_update_multi_kernel(MultiStepArgs a
                 if (d >= 0 && prow(it) < P) nt_store16<ST>(pool + (int64_t)d * H * P * N + tile0 + (int64_t)prow(it) * N, h[it]);
                 acc = group_sum_last<kLpr>(acc);
                 yv[it] = fmaf(Dh, x, acc);
-                if (a.z) yv[it] *= silu_f(zval(u, it));
+                if constexpr (HasZ) yv[it] *= silu_f(zval(u, it));
                 if constexpr (!CONSEC)  // (stored at once: holding them costs registers here)
                     if (ylane && prow(it) < P)
                         st(a.y, out_dt, ((int64_t)row * T + t) * HP + (int64_t)head * P + prow(it), yv[it]);
@@ -377,24 +384,26 @@ __global__ __launch_bounds__(256) void state_update_multi_kernel(MultiStepArgs a
             if (prow(it) < P) nt_store16<ST>(pool + (int64_t)src * H * P * N + tile0 + (int64_t)prow(it) * N, h[it]);
 }
 
+template <typename ST, typename XT, typename AT, int N, int ITERS, bool CONSEC>
+static void launch_sum_k(const LayerShape &s, const MultiStepArgs &a, hipStream_t stream, dim3 grid, int psplit) {
+    if (a.z)
+        hipLaunchKernelGGL((state_update_multi_kernel<ST, XT, AT, N, ITERS, CONSEC, true>), grid, dim3(256), 0, stream, a,
+                           s.H, s.P, s.G, s.out_dt, psplit);
+    else
+        hipLaunchKernelGGL((state_update_multi_kernel<ST, XT, AT, N, ITERS, CONSEC, false>), grid, dim3(256), 0, stream,
+                           a, s.H, s.P, s.G, s.out_dt, psplit);
+}
+
 template <typename ST, typename XT, int N, int ITERS>
 static hipError_t launch_sum(const LayerShape &s, const MultiStepArgs &a, hipStream_t stream, int rows_needed) {
     const int psplit = (rows_needed + ITERS - 1) / ITERS;
     dim3 grid(s.H * psplit, a.batch);
     if (s.act_dt == DT_BF16) {
-        if (a.dst)
-            hipLaunchKernelGGL((state_update_multi_kernel<ST, XT, bf16, N, ITERS, false>), grid, dim3(256), 0, stream, a,
-                               s.H, s.P, s.G, s.out_dt, psplit);
-        else
-            hipLaunchKernelGGL((state_update_multi_kernel<ST, XT, bf16, N, ITERS, true>), grid, dim3(256), 0, stream, a,
-                               s.H, s.P, s.G, s.out_dt, psplit);
+        if (a.dst) launch_sum_k<ST, XT, bf16, N, ITERS, false>(s, a, stream, grid, psplit);
+        else launch_sum_k<ST, XT, bf16, N, ITERS, true>(s, a, stream, grid, psplit);
     } else {
-        if (a.dst)
-            hipLaunchKernelGGL((state_update_multi_kernel<ST, XT, float, N, ITERS, false>), grid, dim3(256), 0, stream, a,
-                               s.H, s.P, s.G, s.out_dt, psplit);
-        else
-            hipLaunchKernelGGL((state_update_multi_kernel<ST, XT, float, N, ITERS, true>), grid, dim3(256), 0, stream, a,
-                               s.H, s.P, s.G, s.out_dt, psplit);
+        if (a.dst) launch_sum_k<ST, XT, float, N, ITERS, false>(s, a, stream, grid, psplit);
+        else launch_sum_k<ST, XT, float, N, ITERS, true>(s, a, stream, grid, psplit);
     }
     return hipGetLastError();
 }
