@@ -70,6 +70,29 @@ def test_multi_token_decode_matches_oracle(state_dtype, out_dtype, with_z):
     assert np.array_equal(host(ssm[untouched]), pl["ssm_pool"][untouched].astype(np.float64))
 
 
+@pytest.mark.parametrize("T", [3, 6])
+@pytest.mark.parametrize("with_z", [False, True])
+def test_multi_token_snapshots_partial_token_block(T, with_z):
+    """Snapshot form with T not a multiple of the 4-token block the kernel stages (a block
+    with skipped tokens), bf16 pool, against the oracle."""
+    d = D16.with_(state_dtype=BF16, out_dtype=BF16)
+    print(f"[multi decode] snapshots, T={T} z={with_z}", flush=True)
+    rows = 3
+    slots = rows * (T + 1)
+    params, x, dt, z, pl = make_inputs(d, 45, rows, T, slots, with_z)
+    src = np.arange(rows, dtype=np.int32)
+    dst = (rows + np.arange(rows * T, dtype=np.int32)).reshape(rows, T)
+    y, conv, ssm = run_multi(d, params, x, dt, z, pl, src, dst)
+    cp = pl["conv_pool"].astype(np.float64)
+    sp = pl["ssm_pool"].astype(np.float64)
+    y_ref, _ = oracle.decode_multi(x, dt, params, src, dst, cp, sp, z=z, **oracle_kw(d))
+    assert_close(host(y), y_ref, BF16, "y")
+    written = sorted(int(v) for v in dst.ravel())
+    u = torch.tensor(written, dtype=torch.long, device="cuda")
+    assert_close(host(ssm[u]), sp[written], BF16, "state snapshots")
+    assert np.array_equal(host(conv[u]), cp[written]), "conv snapshots hold the exact raw inputs"
+
+
 def test_multi_token_equals_single_steps_bitwise_fp32():
     """Without snapshots the final state goes back to the source slot; with an fp32 pool the
     T-token pass performs exactly the arithmetic of T one-token calls."""
