@@ -198,7 +198,7 @@ def main():
                     help="also run a 1 GiB device-to-device copy (known bytes) for counter calibration")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build's hot path runs on a single MI355X "
+        print(f"bench.py measures one GPU: the hot path runs on a single MI355X "
               f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
