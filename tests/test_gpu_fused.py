@@ -234,6 +234,27 @@ def test_fused_full_size_sampled():
         assert np.array_equal(host(conv[int(w["slots"][seq])]), w["xbc"][e - 3:e].astype(np.float64))
 
 
+@pytest.mark.parametrize("nseq", [1, 2])
+def test_fused_fewer_sequences_full_size_sampled(nseq):
+    """The prefill the benchmark times on 1 and 2 sequences of 8,192 tokens (segment mode:
+    4 and 2 segments per sequence), 128 heads, bf16 inputs and y, fp32 state, checked on
+    sampled (sequence, head) pairs and the conv cache."""
+    d = NEMOTRON_H_8B.with_(state_dtype=F32)
+    print(f"[fused prefill] full size {nseq}x8192 (segment mode)", flush=True)
+    w = synth.prefill_batch(d, seed=2, seqlens=[8192] * nseq, num_slots=8, with_z=False)
+    y, ssm, conv = run_fused(d, w)
+    yh = y.float().cpu().numpy()
+    cu = w["cu_seqlens"]
+    for seq, head in [(0, 5), (nseq - 1, 70), (0, 127)]:
+        s, e = int(cu[seq]), int(cu[seq + 1])
+        yr, hr = oracle_head_seq(d, w["params"], w["xbc"][s:e], w["dt_raw"][s:e], head)
+        assert_close(yh[s:e, head * 64:(head + 1) * 64], yr, BF16, f"y seq {seq} head {head}")
+        assert_close(host(ssm[int(w["slots"][seq]), head]), hr, F32, f"state seq {seq} head {head}")
+    for seq in range(nseq):
+        e = int(cu[seq + 1])
+        assert np.array_equal(host(conv[int(w["slots"][seq])]), w["xbc"][e - 3:e].astype(np.float64))
+
+
 def test_fused_long_sequence_resumed_sampled():
     """One 32,768-token sequence resuming from a saved conv and SSM state (a single
     sequence: cut into 4 segments of 8,192 tokens scanned in parallel and joined by the
