@@ -867,11 +867,11 @@ __global__ __launch_bounds__(256) void fused_seg_combine_kernel(FusedArgs a, int
 // Every block's loads are issued the same way (addresses clamped, stores masked, every
 // loaded value used on every path), kFixNB - 1 blocks ahead of the block being applied,
 // and values are widened only where used, so the compiler's waits count just the loads
-// of the block being applied. The block's C
-// rows are read from HBM/L2 once per workgroup and shared by its 4 waves through LDS
-// (two buffers, one barrier per block; every wave passes every barrier). lam_t only
-// falls along a segment, so once exp2 of it is exactly 0 in fp32 every later token of
-// the segment would add exactly 0, and the workgroup stops there.
+// of the block being applied. The block's C rows are read from HBM/L2 once per workgroup
+// and shared by its 4 waves through LDS (two buffers, one barrier per block; every wave
+// passes every barrier). lam_t only falls along a segment, so once exp2 of it is exactly
+// 0 in fp32 every later token of the segment would add exactly 0, and the workgroup
+// stops there.
 constexpr int kFixBlocks = 16;
 constexpr int kFixNB = 3;  // register buffers of the fix-up pass
 template <typename AT, bool HasZ>
