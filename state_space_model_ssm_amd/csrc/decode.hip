@@ -277,13 +277,15 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
     // Per block of TB tokens: B and C are loaded once per workgroup into LDS (every
     // p-row of the head uses the same vectors: re-reading them per row would move
     // TB * 2 * N values per row through L1/L2 against N state values); lane u of
-    // each wave takes dt of token t0 + u (read back with readlane). The first
-    // block's loads are issued before the state's, so its staging and dt overlap
-    // the state's latency.
+    // wave 0 forms dt and the decay of token t0 + u (library softplus and exp, as the
+    // one-token kernel: once per workgroup, not once per wave), read by every wave
+    // from LDS. The first block's loads are issued before the state's, so its
+    // staging and dt overlap the state's latency.
     constexpr int TB = 4;
     constexpr int NT4 = TB * 2 * N / 4;  // 4-element pieces of the block's B|C
     static_assert(NT4 <= 256, "one B|C piece per thread");
     __shared__ __attribute__((aligned(16))) float sBC[TB][2][N];
+    __shared__ float sDt[2][TB];  // dt and decay of the block's tokens, formed by wave 0 alone
     Raw<XT, 4> bcr;
     RawRow<XT, XK> xr[TB][XI];
     RawRow<AT, XK> zr[HasZ ? TB : 1][HasZ ? XI : 1];
@@ -317,13 +319,20 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
         const int u = (tid & 63) & (TB - 1);
         dr = (float)static_cast<const AT *>(a.dt_raw)[((int64_t)row * T + min(t0 + u, T - 1)) * H + head];
     };
-    auto stage_block = [&](float &dt_l, float &dec_l) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    auto stage_block = [&]() {
         if (tid < NT4) {
             const int u = tid / (N / 2), rem = tid % (N / 2), which = rem / (N / 4), n4 = rem % (N / 4);
             *reinterpret_cast<f32x4 *>(&sBC[u][which][4 * n4]) = f32x4{bcr[0], bcr[1], bcr[2], bcr[3]};
         }
-        dt_l = softplus_f(dr + dtb);
-        dec_l = expf(dt_l * A);
+        if (wave == 0) {  // the scalars of the block's tokens once per workgroup, not once per wave
+            const float dt_l = softplus_f(dr + dtb);
+            const float dec_l = expf(dt_l * A);
+            if ((tid & 63) < TB) {
+                sDt[0][tid & 63] = dt_l;
+                sDt[1][tid & 63] = dec_l;
+            }
+        }
     };
 
     load_block(0);
@@ -336,8 +345,7 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
             __syncthreads();  // previous block's B/C fully read
             load_block(t0);
         }
-        float dt_l, dec_l;
-        stage_block(dt_l, dec_l);
+        stage_block();
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
@@ -353,8 +361,8 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) { Bv[j + e] = bq[e]; Cv[j + e] = cq[e]; }
             }
-            const float dt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dt_l), u));
-            const float decay = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dec_l), u));
+            const float dt = sDt[0][u];
+            const float decay = sDt[1][u];
             const int d = a.dst ? a.dst[(int64_t)row * T + t] : -1;
             float yv[ITERS];
 #pragma unroll
