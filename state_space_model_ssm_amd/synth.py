@@ -168,12 +168,27 @@ def mixed_batch(dims: Dims, seed: int, num_prefill: int = 8, len_lo: int = 256, 
 
 def stack_layer(dims: Dims, seed: int, layer: int, concurrency: int, steps: int):
     """Inputs of one layer of the decode stack: per-layer seeded params and an input
-    buffer of ``concurrency + steps - 1`` rows; step s uses rows [s, s + concurrency)."""
+    buffer of ``concurrency + steps - 1`` rows; step s uses rows [s, s + concurrency).
+    Parameters, xBC rows and dt rows come from separate streams of the layer's seed, so
+    the first k rows are the same whatever ``concurrency`` and ``steps`` are."""
     ss = np.random.SeedSequence(seed).spawn(layer + 1)[layer]
-    rng = np.random.Generator(np.random.PCG64(ss))
-    params = layer_params(dims, rng)
-    tok = tokens(dims, rng, concurrency + steps - 1, with_z=False)
-    return {"params": params, **tok}
+    s_par, s_x, s_dt = (np.random.Generator(np.random.PCG64(c)) for c in ss.spawn(3))
+    params = layer_params(dims, s_par)
+    rows = concurrency + steps - 1
+    xbc = round_to_dtype(xbc_values(dims, s_x, rows), dims.act_dtype)
+    dt_raw = round_to_dtype(_normal(s_dt, (rows, dims.nheads), std=math.sqrt(0.5)), dims.act_dtype)
+    return {"params": params, "xbc": xbc, "dt_raw": dt_raw, "z": None}
+
+
+def stack_slot(dims: Dims, seed: int, layer: int, slot: int):
+    """Initial contents of one slot of one layer's pools in the decode stack (state ~
+    N(0, 0.1), conv cache ~ the xBC distribution), from a stream of its own so any subset
+    of slots can be drawn alone. Returns (ssm [H, P, N], conv [W-1, Cdim]) float32."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, layer, slot, 0x5107])))
+    H, P, N, K = dims.nheads, dims.headdim, dims.dstate, dims.conv_width - 1
+    ssm = round_to_dtype(_normal(rng, (H, P, N), std=math.sqrt(0.1)), dims.state_dtype)
+    conv = round_to_dtype(xbc_values(dims, rng, K), dims.state_dtype)
+    return ssm, conv
 
 
 def mamba1_batch(d, seed: int, seqlens, num_slots: int, with_z: bool = True, initial_state: bool = False):

@@ -38,9 +38,52 @@ def max_rel(got, ref):
     return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
 
 
-def assert_close(got, ref, dtype, what):
+def max_rel_slices(got, ref):
+    """Worst slice of max_rel over the leading axis: got/ref [S, ...], each slice normalised by
+    its own max |ref| (so an error confined to one small-valued head or row is not hidden by
+    larger values elsewhere in the tensor)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if got.size == 0:
+        return 0.0, -1
+    g = got.reshape(got.shape[0], -1)
+    r = ref.reshape(ref.shape[0], -1)
+    assert np.all(np.isfinite(g)), "non-finite values in GPU output"
+    den = np.max(np.abs(r), axis=1)
+    den = np.where(den > 0, den, 1.0)
+    errs = np.max(np.abs(g - r), axis=1) / den
+    worst = int(np.argmax(errs))
+    return float(errs[worst]), worst
+
+
+def by_head(a, H):
+    """[T, H*P] outputs of one sequence -> [H, T, P]: one slice per head."""
+    a = np.asarray(a)
+    return a.reshape(a.shape[0], H, -1).transpose(1, 0, 2)
+
+
+def by_row_head(a, H):
+    """[rows, H*P] -> [rows*H, P]: one slice per (row, head)."""
+    a = np.asarray(a)
+    return a.reshape(a.shape[0] * H, -1)
+
+
+def by_slot_head(a):
+    """[n, H, P, N] states -> [n*H, P*N]: one slice per (slot, head)."""
+    a = np.asarray(a)
+    return a.reshape(a.shape[0] * a.shape[1], -1)
+
+
+def assert_close(got, ref, dtype, what, slices=None):
+    """R16 bound on the whole tensor; with ``slices`` (a function mapping an array to
+    [S, ...]) the same bound also holds for every slice against its own max |ref|."""
     err = max_rel(got, ref)
     assert err <= TOL[dtype], f"{what}: max relative error {err:.3e} > {TOL[dtype]:.0e} ({dtype})"
+    if slices is not None:
+        es, worst = max_rel_slices(slices(got), slices(ref))
+        assert es <= TOL[dtype], (f"{what}: slice {worst} has relative error {es:.3e} against its own "
+                                  f"max > {TOL[dtype]:.0e} ({dtype})")
     return err
 
 

@@ -1,0 +1,237 @@
+"""Full-size oracle parity of the benchmarked workloads, in the launch configurations the
+benchmark times:
+
+* the prefill of 4 x 8192 tokens (and of the first 1 and 2 of those sequences, and of one
+  resumed 32,768-token sequence): every token of every head of every sequence, every final
+  state and conv cache, through mamba2_prefill_fwd and both forms of chunk_scan_fwd;
+* the mixed batch (8 varlen prefill sequences + 384 decode rows on a 1024-slot fp32 pool, one
+  mamba2_mixed_fwd with a workspace): every token, row and slot, untouched slots bit-identical;
+* the 48-layer decode stack replayed from one captured HIP graph: every row at concurrency 16,
+  8 sampled rows at concurrency 64, per layer and step.
+
+The oracle is the fp64 C loop (OpenMP across heads), fast enough to cover whole workloads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _helpers import (assert_close, by_head, by_row_head, by_slot_head, dev, dev_i32, dev_u8, host, oracle_kw,
+                      params_dev)
+from state_space_model_ssm_amd import binding as B
+from state_space_model_ssm_amd import synth
+from state_space_model_ssm_amd.configs import BF16, F32, NEMOTRON_H_8B, NEMOTRON_H_8B_MAMBA_LAYERS
+
+pytestmark = pytest.mark.gpu
+
+D2 = NEMOTRON_H_8B.with_(state_dtype=F32)   # prefill-8b and mixed-8b: bf16 inputs and y, fp32 state
+
+
+def check_sequence(d, params, xbc, dt, y_rows, ssm_slot, conv_slot, what, cs0=None, hs0=None):
+    """One sequence, all heads: y rows [T, H*P] (device), final state [H, P, N] and conv
+    cache [W-1, Cdim] (device) against oracle.layer_seq from (cs0, hs0) (zeros if None)."""
+    H, P, N = d.nheads, d.headdim, d.dstate
+    cs = np.zeros((d.conv_width - 1, d.conv_dim)) if cs0 is None else cs0
+    hs = np.zeros((H, P, N)) if hs0 is None else hs0
+    yr, _, cr, hr = oracle.layer_seq(xbc, dt, params, cs, hs, **oracle_kw(d))
+    assert_close(host(y_rows), yr, d.out_dtype, f"{what}: y", slices=lambda a: by_head(a, H))
+    assert_close(host(ssm_slot)[None], hr[None], d.state_dtype, f"{what}: final state", slices=by_slot_head)
+    assert np.array_equal(host(conv_slot), cr), f"{what}: conv cache"
+
+
+def run_prefill_8b(w, mode, nseq=None, has_init=None):
+    """The benchmark's prefill calls on the first `nseq` sequences of `w`: 'fused' =
+    mamba2_prefill_fwd; 'blocks' / 'chunks' = conv1d_fwd to fp32 then chunk_scan_fwd with / without
+    a workspace."""
+    d = D2
+    cu = w["cu_seqlens"]
+    nseq = len(cu) - 1 if nseq is None else nseq
+    T = int(cu[nseq])
+    pd = params_dev(w["params"])
+    xbc, dt = dev(w["xbc"][:T], BF16), dev(w["dt_raw"][:T], BF16)
+    ssm = dev(w["ssm_pool"], F32)
+    conv = dev(w["conv_pool"], F32)
+    cud, idx = dev_i32(cu[:nseq + 1]), dev_i32(w["slots"][:nseq])
+    hi = dev_u8(np.zeros(nseq, np.uint8) if has_init is None else has_init)
+    y = torch.empty(T, d.d_inner, dtype=torch.bfloat16, device="cuda")
+    ws = B.prefill_workspace(d, T)
+    if mode == "fused":
+        B.mamba2_prefill_fwd(d, xbc, dt, None, pd["conv_w"], None, pd["A_log"], pd["dt_bias"], pd["D"], y, ssm, conv,
+                             cud, idx, hi, ws)
+    else:
+        post = torch.empty(T, d.conv_dim, dtype=torch.float32, device="cuda")
+        B.mamba2_conv1d_fwd(d, xbc, pd["conv_w"], None, post, conv, cud, idx, hi)
+        B.mamba2_chunk_scan_fwd(d, post, dt, pd["A_log"], pd["dt_bias"], pd["D"], None, y, ssm, cud, idx, hi,
+                                ws if mode == "blocks" else None)
+    torch.cuda.synchronize()
+    return y, ssm, conv
+
+
+@pytest.mark.parametrize("mode", ["fused", "blocks", "chunks"])
+def test_prefill_8b_every_head(mode):
+    """4 x 8192 tokens, 128 heads, chunk 128, bf16 inputs and y, fp32 state, zero initial
+    state: every head of every sequence against the oracle."""
+    print(f"[full size] prefill 4x8192 {mode}", flush=True)
+    w = synth.prefill_batch(D2, seed=2, seqlens=[8192] * 4, num_slots=8, with_z=False)
+    y, ssm, conv = run_prefill_8b(w, mode)
+    cu = w["cu_seqlens"]
+    for i in range(4):
+        s, e, sl = int(cu[i]), int(cu[i + 1]), int(w["slots"][i])
+        check_sequence(D2, w["params"], w["xbc"][s:e], w["dt_raw"][s:e], y[s:e], ssm[sl], conv[sl],
+                       f"{mode} sequence {i}")
+    untouched = np.setdiff1d(np.arange(8), w["slots"])
+    assert torch.all(ssm[torch.from_numpy(untouched).cuda()] == synth.SENTINEL).item()
+
+
+@pytest.mark.parametrize("nseq", [1, 2])
+def test_prefill_8b_fewer_sequences_every_head(nseq):
+    """The benchmark's prefill of the first 1 and 2 sequences (segment mode: 4 and 2 segments
+    per sequence scanned in parallel, then joined): every head against the oracle."""
+    print(f"[full size] prefill {nseq}x8192 (segment mode)", flush=True)
+    w = synth.prefill_batch(D2, seed=2, seqlens=[8192] * nseq, num_slots=8, with_z=False)
+    y, ssm, conv = run_prefill_8b(w, "fused")
+    cu = w["cu_seqlens"]
+    for i in range(nseq):
+        s, e, sl = int(cu[i]), int(cu[i + 1]), int(w["slots"][i])
+        check_sequence(D2, w["params"], w["xbc"][s:e], w["dt_raw"][s:e], y[s:e], ssm[sl], conv[sl],
+                       f"sequence {i}")
+
+
+def test_prefill_8b_long_resumed_every_head():
+    """One 32,768-token sequence resuming from a saved conv and SSM state (4 segments of
+    8,192 tokens joined by the fix-up pass): every head against the oracle."""
+    print("[full size] one 32768-token sequence, resumed", flush=True)
+    w = synth.prefill_batch(D2, seed=29, seqlens=[32768], num_slots=2, with_z=False, initial_state=True)
+    y, ssm, conv = run_prefill_8b(w, "fused", has_init=np.array([1], np.uint8))
+    sl = int(w["slots"][0])
+    check_sequence(D2, w["params"], w["xbc"], w["dt_raw"], y, ssm[sl], conv[sl], "resumed sequence",
+                   cs0=w["conv_pool"][sl].astype(np.float64), hs0=w["ssm_pool"][sl].astype(np.float64))
+
+
+# ------------------------------------------------------------------ mixed batch
+
+def mixed_8b_inputs():
+    """The benchmark's mixed batch: 8 prefill sequences of U[256, 4096] tokens (zero initial
+    state) + 384 decode rows (random initial state) on a 1024-slot fp32 pool, bf16 activations
+    and y, no z."""
+    w = synth.mixed_batch(D2, seed=3, num_prefill=8, len_lo=256, len_hi=4096, decode_rows=384, num_slots=1024)
+    T = int(w["cu_seqlens"][-1])
+    dv = {"xbc": dev(np.concatenate([w["prefill"]["xbc"], w["decode"]["xbc"]]), BF16),
+          "dt": dev(np.concatenate([w["prefill"]["dt_raw"], w["decode"]["dt_raw"]]), BF16),
+          "ssm0": dev(w["ssm_pool"], F32), "conv0": dev(w["conv_pool"], F32),
+          "cu": dev_i32(w["cu_seqlens"]), "pidx": dev_i32(w["prefill_slots"]), "didx": dev_i32(w["decode_slots"]),
+          "hi": dev_u8(w["has_initial_state"]), **params_dev(w["params"])}
+    return w, T, dv
+
+
+def check_mixed(w, T, y, ssm, conv, what):
+    d = D2
+    H = d.nheads
+    cu = w["cu_seqlens"]
+    for i in range(len(cu) - 1):
+        s, e, sl = int(cu[i]), int(cu[i + 1]), int(w["prefill_slots"][i])
+        check_sequence(d, w["params"], w["prefill"]["xbc"][s:e], w["prefill"]["dt_raw"][s:e], y[s:e], ssm[sl],
+                       conv[sl], f"{what} prefill sequence {i}")
+    rows = len(w["decode_slots"])
+    for r0 in range(0, rows, 64):  # decode rows in batches of 64 (fp64 pools of 64 slots on the host)
+        r1 = min(rows, r0 + 64)
+        sl = w["decode_slots"][r0:r1].astype(np.int64)
+        cp = w["conv_pool"][sl].astype(np.float64)
+        sp = w["ssm_pool"][sl].astype(np.float64)
+        yr, _ = oracle.decode(w["decode"]["xbc"][r0:r1], w["decode"]["dt_raw"][r0:r1], w["params"],
+                              np.arange(r1 - r0), cp, sp, **oracle_kw(d))
+        assert_close(host(y[T + r0:T + r1]), yr, d.out_dtype, f"{what} decode y rows {r0}..{r1}",
+                     slices=lambda a: by_row_head(a, H))
+        u = torch.from_numpy(sl).cuda()
+        assert_close(host(ssm[u]), sp, d.state_dtype, f"{what} decode states rows {r0}..{r1}", slices=by_slot_head)
+        assert np.array_equal(host(conv[u]), cp), f"{what} decode conv caches rows {r0}..{r1}"
+    used = np.concatenate([w["prefill_slots"], w["decode_slots"]])
+    u = torch.from_numpy(np.setdiff1d(np.arange(1024), used)).cuda()
+    assert torch.all(ssm[u] == synth.SENTINEL).item() and torch.all(conv[u] == synth.SENTINEL).item(), \
+        f"{what}: a slot no row uses was written"
+
+
+def test_mixed_8b_every_row():
+    """One mamba2_mixed_fwd with a prefill workspace on the benchmark's mixed batch: every
+    prefill token and head, every decode row, every used slot against the oracle; the 632 slots
+    no row uses stay bit-identical."""
+    print("[full size] mixed batch: 8 varlen sequences + 384 decode rows, 1024-slot fp32 pool", flush=True)
+    w, T, dv = mixed_8b_inputs()
+    d = D2
+    rows = T + 384
+    ssm, conv = dv["ssm0"].clone(), dv["conv0"].clone()
+    post = torch.empty(rows, d.conv_dim, dtype=torch.float32, device="cuda")
+    y = torch.empty(rows, d.d_inner, dtype=torch.bfloat16, device="cuda")
+    ws = B.prefill_workspace(d, T)
+    B.mamba2_mixed_fwd(d, dv["xbc"], dv["dt"], None, dv["conv_w"], None, dv["A_log"], dv["dt_bias"], dv["D"], post, y,
+                       ssm, conv, dv["cu"], dv["pidx"], dv["hi"], dv["didx"], ws)
+    torch.cuda.synchronize()
+    check_mixed(w, T, y, ssm, conv, "mixed")
+
+
+# ------------------------------------------------------------------ 48-layer decode stack
+
+@pytest.mark.parametrize("c,sample", [(16, 0), (64, 8)], ids=["c16-all-rows", "c64-8-rows"])
+def test_stack_graph_every_layer(c, sample):
+    """48 layers x 4 steps of one token per row, captured once as a HIP graph and replayed:
+    per-layer seeded parameters and inputs (step s reads rows [s, s + c) of the layer's
+    buffer), bf16 pools of c slots per layer. Every layer's y at every step and the final
+    state and conv cache of the checked rows (all at c = 16, 8 sampled at c = 64) against the
+    oracle."""
+    d = NEMOTRON_H_8B
+    NL, steps = NEMOTRON_H_8B_MAMBA_LAYERS, 4
+    H = d.nheads
+    print(f"[full size] decode stack {NL} layers x {steps} steps, c={c}", flush=True)
+    checked = np.arange(c) if sample == 0 else np.sort(np.random.default_rng(c).choice(c, sample, replace=False))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    layers, pools, init = [], [], []
+    for l in range(NL):
+        w = synth.stack_layer(d, seed=4, layer=l, concurrency=c, steps=steps)
+        layers.append({"w": w, "xbc": dev(w["xbc"], BF16), "dt": dev(w["dt_raw"], BF16), **params_dev(w["params"])})
+        ssm = torch.empty(c, H, d.headdim, d.dstate, dtype=torch.bfloat16, device="cuda").normal_(0, 0.3, generator=gen)
+        conv = torch.empty(c, d.conv_width - 1, d.conv_dim, dtype=torch.bfloat16, device="cuda").normal_(
+            generator=gen)
+        hs, cs = [], []
+        for r in checked:  # checked rows start from host-generated states
+            s_, c_ = synth.stack_slot(d, seed=4, layer=l, slot=int(r))
+            ssm[int(r)] = torch.from_numpy(s_).to(torch.bfloat16).cuda()
+            conv[int(r)] = torch.from_numpy(c_).to(torch.bfloat16).cuda()
+            hs.append(s_)
+            cs.append(c_)
+        pools.append((ssm, conv))
+        init.append((np.stack(cs).astype(np.float64), np.stack(hs).astype(np.float64)))
+    idx = torch.arange(c, dtype=torch.int32, device="cuda")
+    post = torch.empty(c, d.conv_dim, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(NL, steps, c, d.d_inner, dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        for s_ in range(steps):
+            for l, (L, (ssm, conv)) in enumerate(zip(layers, pools)):
+                B.mamba2_conv1d_update(d, L["xbc"][s_:s_ + c], L["conv_w"], None, post, conv, idx)
+                B.mamba2_state_update(d, post, L["dt"][s_:s_ + c], L["A_log"], L["dt_bias"], L["D"], None,
+                                      y[l, s_], ssm, idx)
+
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        graph.capture_begin()
+        run()
+        graph.capture_end()
+    torch.cuda.current_stream().wait_stream(stream)
+    graph.replay()
+    torch.cuda.synchronize()
+    ck = torch.from_numpy(checked.astype(np.int64)).cuda()
+    kw = oracle_kw(d)
+    for l, L in enumerate(layers):
+        cp, sp = init[l]
+        w = L["w"]
+        for s_ in range(steps):
+            rows = s_ + checked
+            yr, _ = oracle.decode(w["xbc"][rows], w["dt_raw"][rows], w["params"], np.arange(len(checked)), cp, sp,
+                                  **kw)
+            assert_close(host(y[l, s_][ck]), yr, BF16, f"layer {l} step {s_} y", slices=lambda a: by_row_head(a, H))
+        ssm, conv = pools[l]
+        assert_close(host(ssm[ck]), sp, BF16, f"layer {l} final states", slices=by_slot_head)
+        assert np.array_equal(host(conv[ck]), cp), f"layer {l} conv caches"

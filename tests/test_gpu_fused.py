@@ -6,8 +6,8 @@ import pytest
 import torch
 
 import oracle
-from _helpers import (assert_close, compact_pools, dev, dev_i32, dev_u8, host, oracle_head_seq, oracle_kw,
-                      params_dev)
+from _helpers import (assert_close, by_head, by_slot_head, compact_pools, dev, dev_i32, dev_u8, host,
+                      oracle_kw, params_dev)
 from state_space_model_ssm_amd import binding as B
 from state_space_model_ssm_amd import synth
 from state_space_model_ssm_amd.configs import BF16, F32, NEMOTRON_H_8B, TINY
@@ -60,9 +60,9 @@ def oracle_fused(d, w, has_init=None, slots=None, norm_w=None, eps=1e-5, group=0
 def check_fused(d, w, **kw):
     y, ssm, conv = run_fused(d, w, **kw)
     y_ref, cp, sp, used = oracle_fused(d, w, **kw)
-    e_y = assert_close(host(y), y_ref, d.out_dtype, "y")
+    e_y = assert_close(host(y), y_ref, d.out_dtype, "y", slices=lambda a: by_head(a, d.nheads))
     u = torch.tensor(used, dtype=torch.long, device="cuda")
-    e_h = assert_close(host(ssm[u]), sp, d.state_dtype, "final ssm state")
+    e_h = assert_close(host(ssm[u]), sp, d.state_dtype, "final ssm state", slices=by_slot_head)
     assert np.array_equal(host(conv[u]), cp), "conv cache must hold the exact raw inputs"
     print(f"  y err {e_y:.2e}  state err {e_h:.2e}", flush=True)
     return y, ssm, conv
@@ -212,66 +212,6 @@ def test_fused_prefill_equals_repeated_steps():
     assert_close(host(y_scan), host(ys), BF16, "y: fused prefill vs steps")
     assert_close(host(ssm_scan), host(ssm), F32, "state: fused prefill vs steps")
     assert torch.equal(conv_scan, conv)
-
-
-def test_fused_full_size_sampled():
-    """The timed prefill workload (4 x 8192 tokens, 128 heads, chunk 128, bf16 inputs and y,
-    fp32 state) through mamba2_prefill_fwd in the benchmark's launch configuration, checked
-    on sampled (sequence, head) pairs, plus the whole conv cache."""
-    d = NEMOTRON_H_8B.with_(state_dtype=F32)
-    print("[fused prefill] full size 4x8192", flush=True)
-    w = synth.prefill_batch(d, seed=2, seqlens=[8192] * 4, num_slots=8, with_z=False)
-    y, ssm, conv = run_fused(d, w)
-    yh = y.float().cpu().numpy()
-    cu = w["cu_seqlens"]
-    for seq, head in [(0, 0), (1, 37), (2, 77), (3, 127), (0, 64), (3, 15)]:
-        s, e = int(cu[seq]), int(cu[seq + 1])
-        yr, hr = oracle_head_seq(d, w["params"], w["xbc"][s:e], w["dt_raw"][s:e], head)
-        assert_close(yh[s:e, head * 64:(head + 1) * 64], yr, BF16, f"y seq {seq} head {head}")
-        assert_close(host(ssm[int(w["slots"][seq]), head]), hr, F32, f"state seq {seq} head {head}")
-    for seq in range(4):
-        e = int(cu[seq + 1])
-        assert np.array_equal(host(conv[int(w["slots"][seq])]), w["xbc"][e - 3:e].astype(np.float64))
-
-
-@pytest.mark.parametrize("nseq", [1, 2])
-def test_fused_fewer_sequences_full_size_sampled(nseq):
-    """The prefill the benchmark times on 1 and 2 sequences of 8,192 tokens (segment mode:
-    4 and 2 segments per sequence), 128 heads, bf16 inputs and y, fp32 state, checked on
-    sampled (sequence, head) pairs and the conv cache."""
-    d = NEMOTRON_H_8B.with_(state_dtype=F32)
-    print(f"[fused prefill] full size {nseq}x8192 (segment mode)", flush=True)
-    w = synth.prefill_batch(d, seed=2, seqlens=[8192] * nseq, num_slots=8, with_z=False)
-    y, ssm, conv = run_fused(d, w)
-    yh = y.float().cpu().numpy()
-    cu = w["cu_seqlens"]
-    for seq, head in [(0, 5), (nseq - 1, 70), (0, 127)]:
-        s, e = int(cu[seq]), int(cu[seq + 1])
-        yr, hr = oracle_head_seq(d, w["params"], w["xbc"][s:e], w["dt_raw"][s:e], head)
-        assert_close(yh[s:e, head * 64:(head + 1) * 64], yr, BF16, f"y seq {seq} head {head}")
-        assert_close(host(ssm[int(w["slots"][seq]), head]), hr, F32, f"state seq {seq} head {head}")
-    for seq in range(nseq):
-        e = int(cu[seq + 1])
-        assert np.array_equal(host(conv[int(w["slots"][seq])]), w["xbc"][e - 3:e].astype(np.float64))
-
-
-def test_fused_long_sequence_resumed_sampled():
-    """One 32,768-token sequence resuming from a saved conv and SSM state (a single
-    sequence: cut into 4 segments of 8,192 tokens scanned in parallel and joined by the
-    fix-up pass), checked on sampled heads and the conv cache."""
-    d = NEMOTRON_H_8B.with_(state_dtype=F32)
-    print("[fused prefill] one 32768-token sequence, resumed", flush=True)
-    w = synth.prefill_batch(d, seed=29, seqlens=[32768], num_slots=2, with_z=False, initial_state=True)
-    y, ssm, conv = run_fused(d, w, has_init=np.array([1], np.uint8))
-    yh = y.float().cpu().numpy()
-    sl = int(w["slots"][0])
-    cs0 = w["conv_pool"][sl].astype(np.float64)
-    hs0 = w["ssm_pool"][sl].astype(np.float64)
-    for head in (3, 66, 125):
-        yr, hr = oracle_head_seq(d, w["params"], w["xbc"], w["dt_raw"], head, conv_state=cs0, ssm_state=hs0)
-        assert_close(yh[:, head * 64:(head + 1) * 64], yr, BF16, f"y head {head}")
-        assert_close(host(ssm[sl, head]), hr, F32, f"state head {head}")
-    assert np.array_equal(host(conv[sl]), w["xbc"][-3:].astype(np.float64))
 
 
 @pytest.mark.parametrize("state_dtype", [F32, BF16])

@@ -5,8 +5,8 @@ import pytest
 import torch
 
 import oracle
-from _helpers import (assert_close, compact_pools, dev, dev_i32, dev_u8, host, oracle_head_seq, oracle_kw,
-                      params_dev)
+from _helpers import (assert_close, by_head, by_slot_head, compact_pools, dev, dev_i32, dev_u8, host,
+                      oracle_kw, params_dev)
 from state_space_model_ssm_amd import binding as B
 from state_space_model_ssm_amd import synth
 from state_space_model_ssm_amd.configs import BF16, F32, NEMOTRON_H_8B, TINY
@@ -58,9 +58,9 @@ def check_prefill(d, w, has_init=None, slots=None, ws=False):
     y, post, ssm, conv = run_prefill(d, w, has_init, slots, ws)
     y_ref, post_ref, cp, sp, used = oracle_prefill(d, w, has_init, slots)
     e_post = assert_close(host(post), post_ref, d.post_dtype, "post-conv xBC")
-    e_y = assert_close(host(y), y_ref, d.out_dtype, "y")
+    e_y = assert_close(host(y), y_ref, d.out_dtype, "y", slices=lambda a: by_head(a, d.nheads))
     u = torch.tensor(used, dtype=torch.long, device="cuda")
-    e_h = assert_close(host(ssm[u]), sp, d.state_dtype, "final ssm state")
+    e_h = assert_close(host(ssm[u]), sp, d.state_dtype, "final ssm state", slices=by_slot_head)
     assert np.array_equal(host(conv[u]), cp), "conv cache must hold the exact raw inputs"
     return y, ssm, conv, (e_post, e_y, e_h)
 
@@ -229,24 +229,6 @@ def test_padding_and_empty_sequences(out_dtype, ws):
     assert np.array_equal(host(ssm[int(slots[1])]), w["ssm_pool"][slots[1]].astype(np.float64))
     assert torch.all(ssm[int(slots[3])] == 0).item()
     check_prefill(d, w, has_init=has_init, slots=slots, ws=ws)
-
-
-@pytest.mark.parametrize("ws", [False, True], ids=["chunks", "blocks"])
-def test_full_size_prefill_sampled(ws):
-    """The timed prefill workload (4 x 8192 tokens, 128 heads, chunk 128, bf16 y, fp32 state)
-    in the benchmark's launch configurations (chunk_scan_fwd without and with a workspace),
-    checked on sampled (sequence, head) pairs."""
-    d = NEMOTRON_H_8B.with_(state_dtype=F32)
-    print(f"[prefill parity] full size 4x8192 ws={ws}", flush=True)
-    w = synth.prefill_batch(d, seed=2, seqlens=[8192] * 4, num_slots=8, with_z=False)
-    y, _, ssm, _ = run_prefill(d, w, ws=ws)
-    yh = y.float().cpu().numpy()
-    cu = w["cu_seqlens"]
-    for seq, head in [(0, 0), (1, 37), (2, 77), (3, 127), (0, 64), (3, 15)]:
-        s, e = int(cu[seq]), int(cu[seq + 1])
-        yr, hr = oracle_head_seq(d, w["params"], w["xbc"][s:e], w["dt_raw"][s:e], head)
-        assert_close(yh[s:e, head * 64:(head + 1) * 64], yr, BF16, f"y seq {seq} head {head}")
-        assert_close(host(ssm[int(w["slots"][seq]), head]), hr, F32, f"state seq {seq} head {head}")
 
 
 def test_mixed_batch_matches_oracle():
