@@ -45,14 +45,16 @@ size_t mamba1_ssm_slot_bytes(const mamba1_dims *dims);
  * starts from ssm_pool[state_indices[i]] when has_initial_state[i] is 1 (zeros
  * otherwise; has_initial_state may be NULL) and its final state is written to
  * that slot. state_indices[i] < 0 marks a padding sequence (y = 0, no slot
- * access). Requires dstate in {4, 8, 16} and Dc/G a multiple of the
+ * access); num_slots is the pool's slot count, and an index >= num_slots is
+ * skipped like padding and counted (see mamba2_slot_errors in mamba2.h).
+ * Requires dstate in {4, 8, 16} and Dc/G a multiple of the
  * workgroup's channel count (64, 128, 256 for N = 16, 8, 4), else
  * MAMBA2_ERR_UNSUPPORTED. */
 int mamba1_selective_scan_fwd(const mamba1_dims *dims, const void *u, const void *delta_raw,
                               const float *A, const void *B, const void *C, const float *D,
                               const void *z, const float *delta_bias, int32_t delta_softplus,
-                              void *y, void *ssm_pool, const int32_t *cu_seqlens, int32_t nseq,
-                              int64_t total_tokens, const int32_t *state_indices,
+                              void *y, void *ssm_pool, int32_t num_slots, const int32_t *cu_seqlens,
+                              int32_t nseq, int64_t total_tokens, const int32_t *state_indices,
                               const uint8_t *has_initial_state, void *stream);
 
 /* One token per row, the state read and written in place at
@@ -60,13 +62,13 @@ int mamba1_selective_scan_fwd(const mamba1_dims *dims, const void *u, const void
  * update is the one the vllm.cpp page, "The divergence", asks for). Same math
  * and the same per-step arithmetic as mamba1_selective_scan_fwd, so T calls equal
  * one T-token scan. u, delta_raw, z, y [batch][Dc]; B, C [batch][G][N].
- * state_indices[i] < 0 marks a padding row (y = 0, no slot access); two rows
- * on one slot race. */
+ * state_indices[i] < 0 marks a padding row (y = 0, no slot access); an index
+ * >= num_slots is skipped and counted the same way; two rows on one slot race. */
 int mamba1_selective_state_update(const mamba1_dims *dims, const void *u, const void *delta_raw,
                                   const float *A, const void *B, const void *C, const float *D,
                                   const void *z, const float *delta_bias, int32_t delta_softplus,
-                                  void *y, void *ssm_pool, const int32_t *state_indices,
-                                  int32_t batch, void *stream);
+                                  void *y, void *ssm_pool, int32_t num_slots,
+                                  const int32_t *state_indices, int32_t batch, void *stream);
 
 #ifdef __cplusplus
 }

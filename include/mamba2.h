@@ -51,9 +51,14 @@
  *       A_log, dt_bias, D  [H] fp32
  *       ssm pool   [slots][H][P][N]   (state_dtype)
  *       conv pool  [slots][W-1][Cdim] (state_dtype; raw pre-conv inputs, oldest first)
- *   - Slot index < 0 marks a padding row/sequence: its outputs are written as
- *     zero and no slot is read or written. Two rows of one call on the same
- *     slot race (undefined result).
+ *   - Every entry point that takes a pool also takes num_slots, the number of
+ *     slots the caller allocated in it (both pools of a call have that many).
+ *     Slot index < 0 marks a padding row/sequence: its outputs are written as
+ *     zero and no slot is read or written. An index >= num_slots is a caller
+ *     error that the kernels treat the same way (outputs zero, no slot access,
+ *     so nothing outside the pool is touched) and count in a per-device word
+ *     that mamba2_slot_errors reads. Two rows of one call on the same slot race
+ *     (undefined result); mamba2_check_slot_indices finds such duplicates.
  *   - Sizes: a call with zero rows / zero tokens is valid and enqueues nothing.
  */
 #ifndef MAMBA2_H
@@ -123,7 +128,7 @@ int mamba2_chunk_scan_workspace_bytes(const mamba2_dims *dims, int64_t total_tok
  * from the old cache for sequences shorter than W-1). Rows of padding
  * sequences (slot < 0) are written as zero. */
 int mamba2_conv1d_fwd(const mamba2_dims *dims, const void *xbc, const float *conv_w,
-                      const float *conv_b, void *xbc_out, void *conv_pool,
+                      const float *conv_b, void *xbc_out, void *conv_pool, int32_t num_slots,
                       const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens,
                       const int32_t *state_indices, const uint8_t *has_initial_state,
                       void *stream);
@@ -133,7 +138,7 @@ int mamba2_conv1d_fwd(const mamba2_dims *dims, const void *xbc, const float *con
  *   xbc [batch][Cdim] act_dtype; xbc_out [batch][Cdim] xbc_dtype (may not alias xbc);
  *   state_indices [batch] int32 device. */
 int mamba2_conv1d_update(const mamba2_dims *dims, const void *xbc, const float *conv_w,
-                         const float *conv_b, void *xbc_out, void *conv_pool,
+                         const float *conv_b, void *xbc_out, void *conv_pool, int32_t num_slots,
                          const int32_t *state_indices, int32_t batch, void *stream);
 
 /* Chunked SSD scan over packed sequences ([record], "REQUIRED KERNEL CLASS").
@@ -152,8 +157,8 @@ int mamba2_conv1d_update(const mamba2_dims *dims, const void *xbc, const float *
  *   to rounding order. */
 int mamba2_chunk_scan_fwd(const mamba2_dims *dims, const void *xbc, const void *dt_raw,
                           const float *A_log, const float *dt_bias, const float *D, const void *z,
-                          void *y, void *ssm_pool, const int32_t *cu_seqlens, int32_t nseq,
-                          int64_t total_tokens, const int32_t *state_indices,
+                          void *y, void *ssm_pool, int32_t num_slots, const int32_t *cu_seqlens,
+                          int32_t nseq, int64_t total_tokens, const int32_t *state_indices,
                           const uint8_t *has_initial_state, void *workspace,
                           size_t workspace_bytes, void *stream);
 
@@ -165,8 +170,8 @@ int mamba2_chunk_scan_fwd(const mamba2_dims *dims, const void *xbc, const void *
  *   z [batch][H*P] act_dtype or NULL; y [batch][H*P] out_dtype. */
 int mamba2_state_update(const mamba2_dims *dims, const void *xbc, const void *dt_raw,
                         const float *A_log, const float *dt_bias, const float *D, const void *z,
-                        void *y, void *ssm_pool, const int32_t *state_indices, int32_t batch,
-                        void *stream);
+                        void *y, void *ssm_pool, int32_t num_slots, const int32_t *state_indices,
+                        int32_t batch, void *stream);
 
 /* Multi-token decode: `tokens` (T) consecutive tokens per row, as when a step
  * verifies drafted tokens ([TRT-LLM]: one-model MTP in the hybrid serving
@@ -185,14 +190,14 @@ int mamba2_state_update(const mamba2_dims *dims, const void *xbc, const void *dt
  * row: a destination that is another row's source (or two rows writing one
  * slot) races. src_indices[i] < 0 marks a padding row (y = 0, no slot access). */
 int mamba2_conv1d_update_multi(const mamba2_dims *dims, const void *xbc, const float *conv_w,
-                               const float *conv_b, void *xbc_out, void *conv_pool,
+                               const float *conv_b, void *xbc_out, void *conv_pool, int32_t num_slots,
                                const int32_t *src_indices, const int32_t *dst_indices,
                                int32_t batch, int32_t tokens, void *stream);
 int mamba2_state_update_multi(const mamba2_dims *dims, const void *xbc, const void *dt_raw,
                               const float *A_log, const float *dt_bias, const float *D,
-                              const void *z, void *y, void *ssm_pool, const int32_t *src_indices,
-                              const int32_t *dst_indices, int32_t batch, int32_t tokens,
-                              void *stream);
+                              const void *z, void *y, void *ssm_pool, int32_t num_slots,
+                              const int32_t *src_indices, const int32_t *dst_indices, int32_t batch,
+                              int32_t tokens, void *stream);
 
 /* Mixed batch ([TRT-LLM] mixed prefill+decode iterations): the prefill
  * segment (packed by cu_seqlens) runs conv1d_fwd + chunk_scan_fwd, or
@@ -208,8 +213,8 @@ int mamba2_state_update_multi(const mamba2_dims *dims, const void *xbc, const vo
 int mamba2_mixed_fwd(const mamba2_dims *dims, const void *xbc, const void *dt_raw, const void *z,
                      const float *conv_w, const float *conv_b, const float *A_log,
                      const float *dt_bias, const float *D, void *xbc_post, void *y,
-                     void *ssm_pool, void *conv_pool, const int32_t *cu_seqlens, int32_t nseq,
-                     int64_t total_tokens, const int32_t *prefill_indices,
+                     void *ssm_pool, void *conv_pool, int32_t num_slots, const int32_t *cu_seqlens,
+                     int32_t nseq, int64_t total_tokens, const int32_t *prefill_indices,
                      const uint8_t *has_initial_state, const int32_t *decode_indices,
                      int32_t decode_batch, void *workspace, size_t workspace_bytes,
                      void *stream);
@@ -248,7 +253,7 @@ int mamba2_prefill_fwd(const mamba2_dims *dims, const void *xbc, const void *dt_
                        const float *conv_w, const float *conv_b, const float *A_log,
                        const float *dt_bias, const float *D, const float *norm_w, float norm_eps,
                        int32_t norm_group, void *y, void *ssm_pool, void *conv_pool,
-                       const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens,
+                       int32_t num_slots, const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens,
                        const int32_t *state_indices, const uint8_t *has_initial_state,
                        void *workspace, size_t workspace_bytes, void *stream);
 
@@ -266,13 +271,36 @@ int mamba2_gated_rmsnorm(const mamba2_dims *dims, const void *y, const void *z, 
  * cost scales with concurrency, not context). Host-only: it hands out slot
  * ids of a caller-owned pool in O(1); it never touches device memory. A new
  * sequence starts from zero state by passing has_initial_state = 0, not by
- * clearing its slot. Not thread-safe; one allocator per pool. */
+ * clearing its slot. Not thread-safe: calls on one allocator from several
+ * threads need the caller's lock; distinct allocators are independent. One
+ * allocator per pool. Host memory for the free list comes from the C++ heap;
+ * if it runs out, mamba2_slots_create returns MAMBA2_ERR_NO_SLOT (no exception
+ * crosses the ABI). */
 typedef struct mamba2_slots mamba2_slots;
 int mamba2_slots_create(int32_t num_slots, mamba2_slots **out);
 int mamba2_slot_alloc(mamba2_slots *s, int32_t *slot);      /* MAMBA2_ERR_NO_SLOT when full */
 int mamba2_slot_free(mamba2_slots *s, int32_t slot);        /* MAMBA2_ERR_NO_SLOT if not allocated */
 int32_t mamba2_slots_in_use(const mamba2_slots *s);
 void mamba2_slots_destroy(mamba2_slots *s);
+
+/* Slot index safety ([vllm.cpp], "The divergence": the ops index the caller's
+ * cache in place at the slot, so the library bounds every index it reads).
+ * mamba2_read_slot_errors: when the stream reaches the call, count[0] (device
+ * memory, one uint32) receives how many times kernels on the current device
+ * skipped a row or sequence because its index was >= num_slots since the last
+ * reset, and reset != 0 then sets that count to 0. A call with one bad row may
+ * count it once per kernel of the call that reads the slot, so any nonzero
+ * value means "a caller passed an index beyond its pool". The count lives in
+ * one device word per GPU that every call on that GPU shares.
+ * mamba2_check_slot_indices: a debug check of one index list on `stream`,
+ * nothing else touched: result[0] = entries >= num_slots, result[1] = entries
+ * in [0, num_slots) equal to an earlier entry (rows that would race); result
+ * is device memory for 2 uint32, written (not accumulated) when the stream
+ * reaches the call. O(n^2) compares in one workgroup: meant for debugging,
+ * not for the hot path. */
+int mamba2_read_slot_errors(uint32_t *count, int32_t reset, void *stream);
+int mamba2_check_slot_indices(const int32_t *indices, int32_t n, int32_t num_slots, uint32_t *result,
+                              void *stream);
 
 const char *mamba2_status_string(int status);
 const char *mamba2_last_error(void);

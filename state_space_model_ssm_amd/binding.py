@@ -60,39 +60,41 @@ _lock = threading.Lock()
 _lib = None
 
 _P = ctypes.c_void_p
+_I32 = ctypes.c_int32
 _SIGS = {
     "mamba2_check_dims": (ctypes.c_int, [ctypes.POINTER(CDims)]),
     "mamba2_ssm_slot_bytes": (ctypes.c_size_t, [ctypes.POINTER(CDims)]),
     "mamba2_conv_slot_bytes": (ctypes.c_size_t, [ctypes.POINTER(CDims)]),
     "mamba2_chunk_scan_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(CDims), ctypes.c_int64, ctypes.c_int32,
                                                           ctypes.POINTER(ctypes.c_size_t)]),
-    "mamba2_conv1d_fwd": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+    "mamba2_conv1d_fwd": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _I32, _P, _I32,
                                          ctypes.c_int64, _P, _P, _P]),
-    "mamba2_conv1d_update": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P]),
-    "mamba2_chunk_scan_fwd": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                             ctypes.c_int32, ctypes.c_int64, _P, _P, _P, ctypes.c_size_t, _P]),
-    "mamba2_state_update": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                           ctypes.c_int32, _P]),
+    "mamba2_conv1d_update": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _I32, _P, _I32, _P]),
+    "mamba2_chunk_scan_fwd": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P,
+                                             _I32, ctypes.c_int64, _P, _P, _P, ctypes.c_size_t, _P]),
+    "mamba2_state_update": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P,
+                                           _I32, _P]),
     "mamba2_mixed_fwd": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                        _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P, ctypes.c_int32, _P,
+                                        _I32, _P, _I32, ctypes.c_int64, _P, _P, _P, _I32, _P,
                                         ctypes.c_size_t, _P]),
-    "mamba2_conv1d_update_multi": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P,
-                                                   ctypes.c_int32, ctypes.c_int32, _P]),
-    "mamba2_state_update_multi": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                                  ctypes.c_int32, ctypes.c_int32, _P]),
+    "mamba2_conv1d_update_multi": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _I32, _P, _P,
+                                                   _I32, _I32, _P]),
+    "mamba2_state_update_multi": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P,
+                                                  _P, _I32, _I32, _P]),
     "mamba2_prefill_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(CDims), ctypes.c_int64,
                                                        ctypes.POINTER(ctypes.c_size_t)]),
     "mamba2_prefill_fwd": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
-                                          ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P,
+                                          _I32, _P, _P, _P, _I32, _P, _I32, ctypes.c_int64, _P, _P, _P,
                                           ctypes.c_size_t, _P]),
     "mamba2_gated_rmsnorm": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, ctypes.c_float, ctypes.c_int32, _P,
                                             ctypes.c_int64, _P]),
     "mamba1_ssm_slot_bytes": (ctypes.c_size_t, [ctypes.POINTER(CDims1)]),
     "mamba1_selective_scan_fwd": (ctypes.c_int, [ctypes.POINTER(CDims1), _P, _P, _P, _P, _P, _P, _P, _P,
-                                                  ctypes.c_int32, _P, _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P,
-                                                  _P]),
+                                                  _I32, _P, _P, _I32, _P, _I32, ctypes.c_int64, _P, _P, _P]),
     "mamba1_selective_state_update": (ctypes.c_int, [ctypes.POINTER(CDims1), _P, _P, _P, _P, _P, _P, _P, _P,
-                                                      ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P]),
+                                                      _I32, _P, _P, _I32, _P, _I32, _P]),
+    "mamba2_read_slot_errors": (ctypes.c_int, [_P, _I32, _P]),
+    "mamba2_check_slot_indices": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "mamba2_slots_create": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(_P)]),
     "mamba2_slot_alloc": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32)]),
     "mamba2_slot_free": (ctypes.c_int, [_P, ctypes.c_int32]),
@@ -164,6 +166,43 @@ def _xdt(d: Dims, xbc_dtype):
     return _TORCH_DT[xbc_dtype or d.post_dtype]
 
 
+def _ssm_slots(d: Dims, pool) -> int:
+    """Slot count of an SSM pool [slots, H, P, N] (checked)."""
+    if pool is None or pool.dim() != 4 or tuple(pool.shape[1:]) != (d.nheads, d.headdim, d.dstate):
+        raise ValueError(f"ssm_pool must be [slots, {d.nheads}, {d.headdim}, {d.dstate}], got "
+                         f"{None if pool is None else tuple(pool.shape)}")
+    _want(pool, "ssm_pool", _TORCH_DT[d.state_dtype])
+    return int(pool.shape[0])
+
+
+def _conv_slots(d: Dims, pool) -> int:
+    """Slot count of a conv pool [slots, W-1, Cdim] (checked)."""
+    if pool is None or pool.dim() != 3 or tuple(pool.shape[1:]) != (d.conv_width - 1, d.conv_dim):
+        raise ValueError(f"conv_pool must be [slots, {d.conv_width - 1}, {d.conv_dim}], got "
+                         f"{None if pool is None else tuple(pool.shape)}")
+    _want(pool, "conv_pool", _TORCH_DT[d.state_dtype])
+    return int(pool.shape[0])
+
+
+def _both_slots(d: Dims, ssm_pool, conv_pool) -> int:
+    n = _ssm_slots(d, ssm_pool)
+    if _conv_slots(d, conv_pool) != n:
+        raise ValueError("ssm_pool and conv_pool must have the same number of slots")
+    return n
+
+
+def _debug_check(num_slots: int, *index_tensors) -> None:
+    """With MAMBA2_CHECK_SLOTS=1 in the environment, every call that indexes a pool first
+    checks its index tables on the device (out-of-range and repeated slots; this waits for
+    the device) and raises on either."""
+    if os.environ.get("MAMBA2_CHECK_SLOTS", "0") in ("", "0"):
+        return
+    idx = torch.cat([t.reshape(-1) for t in index_tensors if t is not None])
+    bad, dup = check_slot_indices(idx, num_slots)
+    if bad or dup:
+        raise ValueError(f"slot indices: {bad} >= num_slots ({num_slots}), {dup} repeated")
+
+
 # ------------------------------------------------------------------ queries
 
 def mamba2_check_dims(d: Dims, xbc_dtype=None) -> None:
@@ -196,13 +235,14 @@ def mamba2_conv1d_fwd(d: Dims, xbc, conv_w, conv_b, xbc_out, conv_pool, cu_seqle
     _want(conv_w, "conv_w", torch.float32, (d.conv_dim, d.conv_width))
     _want(conv_b, "conv_b", torch.float32, (d.conv_dim,), optional=True)
     _want(xbc_out, "xbc_out", _xdt(d, xbc_dtype), (T, d.conv_dim))
-    _want(conv_pool, "conv_pool", _TORCH_DT[d.state_dtype])
+    ns = _conv_slots(d, conv_pool)
     _want(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,))
     _want(state_indices, "state_indices", torch.int32, (nseq,))
     _want(has_initial_state, "has_initial_state", torch.uint8, (nseq,), optional=True)
+    _debug_check(ns, state_indices)
     c = cdims(d, xbc_dtype)
     _check(lib().mamba2_conv1d_fwd(ctypes.byref(c), _ptr(xbc), _ptr(conv_w), _ptr(conv_b), _ptr(xbc_out),
-                                   _ptr(conv_pool), _ptr(cu_seqlens), nseq, T, _ptr(state_indices),
+                                   _ptr(conv_pool), ns, _ptr(cu_seqlens), nseq, T, _ptr(state_indices),
                                    _ptr(has_initial_state), _stream(stream)), "mamba2_conv1d_fwd")
 
 
@@ -213,11 +253,12 @@ def mamba2_conv1d_update(d: Dims, xbc, conv_w, conv_b, xbc_out, conv_pool, state
     _want(conv_w, "conv_w", torch.float32, (d.conv_dim, d.conv_width))
     _want(conv_b, "conv_b", torch.float32, (d.conv_dim,), optional=True)
     _want(xbc_out, "xbc_out", _xdt(d, xbc_dtype), (Bd, d.conv_dim))
-    _want(conv_pool, "conv_pool", _TORCH_DT[d.state_dtype])
+    ns = _conv_slots(d, conv_pool)
     _want(state_indices, "state_indices", torch.int32, (Bd,))
+    _debug_check(ns, state_indices)
     c = cdims(d, xbc_dtype)
     _check(lib().mamba2_conv1d_update(ctypes.byref(c), _ptr(xbc), _ptr(conv_w), _ptr(conv_b), _ptr(xbc_out),
-                                      _ptr(conv_pool), _ptr(state_indices), Bd, _stream(stream)),
+                                      _ptr(conv_pool), ns, _ptr(state_indices), Bd, _stream(stream)),
            "mamba2_conv1d_update")
 
 
@@ -232,16 +273,15 @@ def mamba2_chunk_scan_fwd(d: Dims, xbc, dt_raw, A_log, dt_bias, D, z, y, ssm_poo
         _want(t, n, torch.float32, (H,))
     _want(z, "z", _TORCH_DT[d.act_dtype], (T, d.d_inner), optional=True)
     _want(y, "y", _TORCH_DT[d.out_dtype], (T, d.d_inner))
-    _want(ssm_pool, "ssm_pool", _TORCH_DT[d.state_dtype])
-    if ssm_pool.dim() != 4 or tuple(ssm_pool.shape[1:]) != (H, d.headdim, d.dstate):
-        raise ValueError("ssm_pool must be [slots, H, P, N]")
+    ns = _ssm_slots(d, ssm_pool)
     _want(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,))
     _want(state_indices, "state_indices", torch.int32, (nseq,))
     _want(has_initial_state, "has_initial_state", torch.uint8, (nseq,), optional=True)
+    _debug_check(ns, state_indices)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     c = cdims(d, xbc_dtype)
     _check(lib().mamba2_chunk_scan_fwd(ctypes.byref(c), _ptr(xbc), _ptr(dt_raw), _ptr(A_log), _ptr(dt_bias),
-                                       _ptr(D), _ptr(z), _ptr(y), _ptr(ssm_pool), _ptr(cu_seqlens), nseq, T,
+                                       _ptr(D), _ptr(z), _ptr(y), _ptr(ssm_pool), ns, _ptr(cu_seqlens), nseq, T,
                                        _ptr(state_indices), _ptr(has_initial_state), _ptr(workspace), ws_bytes,
                                        _stream(stream)), "mamba2_chunk_scan_fwd")
 
@@ -256,13 +296,13 @@ def mamba2_state_update(d: Dims, xbc, dt_raw, A_log, dt_bias, D, z, y, ssm_pool,
         _want(t, n, torch.float32, (H,))
     _want(z, "z", _TORCH_DT[d.act_dtype], (Bd, d.d_inner), optional=True)
     _want(y, "y", _TORCH_DT[d.out_dtype], (Bd, d.d_inner))
-    _want(ssm_pool, "ssm_pool", _TORCH_DT[d.state_dtype])
-    if ssm_pool.dim() != 4 or tuple(ssm_pool.shape[1:]) != (H, d.headdim, d.dstate):
-        raise ValueError("ssm_pool must be [slots, H, P, N]")
+    ns = _ssm_slots(d, ssm_pool)
     _want(state_indices, "state_indices", torch.int32, (Bd,))
+    _debug_check(ns, state_indices)
     c = cdims(d, xbc_dtype)
     _check(lib().mamba2_state_update(ctypes.byref(c), _ptr(xbc), _ptr(dt_raw), _ptr(A_log), _ptr(dt_bias), _ptr(D),
-                                     _ptr(z), _ptr(y), _ptr(ssm_pool), _ptr(state_indices), Bd, _stream(stream)),
+                                     _ptr(z), _ptr(y), _ptr(ssm_pool), ns, _ptr(state_indices), Bd,
+                                     _stream(stream)),
            "mamba2_state_update")
 
 
@@ -274,12 +314,13 @@ def mamba2_conv1d_update_multi(d: Dims, xbc, conv_w, conv_b, xbc_out, conv_pool,
     _want(conv_w, "conv_w", torch.float32, (d.conv_dim, d.conv_width))
     _want(conv_b, "conv_b", torch.float32, (d.conv_dim,), optional=True)
     _want(xbc_out, "xbc_out", _xdt(d, xbc_dtype), (Bd, T, d.conv_dim))
-    _want(conv_pool, "conv_pool", _TORCH_DT[d.state_dtype])
+    ns = _conv_slots(d, conv_pool)
     _want(src_indices, "src_indices", torch.int32, (Bd,))
     _want(dst_indices, "dst_indices", torch.int32, (Bd, T), optional=True)
+    _debug_check(ns, src_indices, dst_indices)
     _check(lib().mamba2_conv1d_update_multi(ctypes.byref(cdims(d, xbc_dtype)), _ptr(xbc), _ptr(conv_w), _ptr(conv_b),
-                                            _ptr(xbc_out), _ptr(conv_pool), _ptr(src_indices), _ptr(dst_indices), Bd, T,
-                                            _stream(stream)), "mamba2_conv1d_update_multi")
+                                            _ptr(xbc_out), _ptr(conv_pool), ns, _ptr(src_indices), _ptr(dst_indices),
+                                            Bd, T, _stream(stream)), "mamba2_conv1d_update_multi")
 
 
 def mamba2_state_update_multi(d: Dims, xbc, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, src_indices, dst_indices=None,
@@ -293,14 +334,14 @@ def mamba2_state_update_multi(d: Dims, xbc, dt_raw, A_log, dt_bias, D, z, y, ssm
         _want(t, n, torch.float32, (H,))
     _want(z, "z", _TORCH_DT[d.act_dtype], (Bd, T, d.d_inner), optional=True)
     _want(y, "y", _TORCH_DT[d.out_dtype], (Bd, T, d.d_inner))
-    _want(ssm_pool, "ssm_pool", _TORCH_DT[d.state_dtype])
-    if ssm_pool.dim() != 4 or tuple(ssm_pool.shape[1:]) != (H, d.headdim, d.dstate):
-        raise ValueError("ssm_pool must be [slots, H, P, N]")
+    ns = _ssm_slots(d, ssm_pool)
     _want(src_indices, "src_indices", torch.int32, (Bd,))
     _want(dst_indices, "dst_indices", torch.int32, (Bd, T), optional=True)
+    _debug_check(ns, src_indices, dst_indices)
     _check(lib().mamba2_state_update_multi(ctypes.byref(cdims(d, xbc_dtype)), _ptr(xbc), _ptr(dt_raw), _ptr(A_log),
-                                           _ptr(dt_bias), _ptr(D), _ptr(z), _ptr(y), _ptr(ssm_pool), _ptr(src_indices),
-                                           _ptr(dst_indices), Bd, T, _stream(stream)), "mamba2_state_update_multi")
+                                           _ptr(dt_bias), _ptr(D), _ptr(z), _ptr(y), _ptr(ssm_pool), ns,
+                                           _ptr(src_indices), _ptr(dst_indices), Bd, T, _stream(stream)),
+           "mamba2_state_update_multi")
 
 
 def mamba2_prefill_workspace_bytes(d: Dims, total_tokens: int, *, xbc_dtype=None) -> int:
@@ -331,19 +372,17 @@ def mamba2_prefill_fwd(d: Dims, xbc, dt_raw, z, conv_w, conv_b, A_log, dt_bias, 
         _want(t, n, torch.float32, (H,))
     _want(norm_w, "norm_w", torch.float32, (d.d_inner,), optional=True)
     _want(y, "y", _TORCH_DT[d.out_dtype], (T, d.d_inner))
-    _want(ssm_pool, "ssm_pool", _TORCH_DT[d.state_dtype])
-    if ssm_pool.dim() != 4 or tuple(ssm_pool.shape[1:]) != (H, d.headdim, d.dstate):
-        raise ValueError("ssm_pool must be [slots, H, P, N]")
-    _want(conv_pool, "conv_pool", _TORCH_DT[d.state_dtype])
+    ns = _both_slots(d, ssm_pool, conv_pool)
     _want(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,))
     _want(state_indices, "state_indices", torch.int32, (nseq,))
     _want(has_initial_state, "has_initial_state", torch.uint8, (nseq,), optional=True)
     _want(workspace, "workspace", optional=True)
+    _debug_check(ns, state_indices)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     c = cdims(d, xbc_dtype)
     _check(lib().mamba2_prefill_fwd(ctypes.byref(c), _ptr(xbc), _ptr(dt_raw), _ptr(z), _ptr(conv_w), _ptr(conv_b),
                                     _ptr(A_log), _ptr(dt_bias), _ptr(D), _ptr(norm_w), float(norm_eps),
-                                    int(norm_group), _ptr(y), _ptr(ssm_pool), _ptr(conv_pool), _ptr(cu_seqlens),
+                                    int(norm_group), _ptr(y), _ptr(ssm_pool), _ptr(conv_pool), ns, _ptr(cu_seqlens),
                                     nseq, T, _ptr(state_indices), _ptr(has_initial_state), _ptr(workspace), ws_bytes,
                                     _stream(stream)), "mamba2_prefill_fwd")
 
@@ -381,12 +420,14 @@ def mamba1_selective_scan_fwd(d, u, delta_raw, A, B, C, D, z, delta_bias, y, ssm
     _want(ssm_pool, "ssm_pool", _TORCH_DT[d.state_dtype])
     if ssm_pool.dim() != 3 or tuple(ssm_pool.shape[1:]) != (d.dim, d.dstate):
         raise ValueError("ssm_pool must be [slots, dim, dstate]")
+    ns = int(ssm_pool.shape[0])
     _want(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,))
     _want(state_indices, "state_indices", torch.int32, (nseq,))
     _want(has_initial_state, "has_initial_state", torch.uint8, (nseq,), optional=True)
+    _debug_check(ns, state_indices)
     _check(lib().mamba1_selective_scan_fwd(ctypes.byref(cdims1(d)), _ptr(u), _ptr(delta_raw), _ptr(A), _ptr(B), _ptr(C),
                                            _ptr(D), _ptr(z), _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(y),
-                                           _ptr(ssm_pool), _ptr(cu_seqlens), nseq, T, _ptr(state_indices),
+                                           _ptr(ssm_pool), ns, _ptr(cu_seqlens), nseq, T, _ptr(state_indices),
                                            _ptr(has_initial_state), _stream(stream)), "mamba1_selective_scan_fwd")
 
 
@@ -408,10 +449,12 @@ def mamba1_selective_state_update(d, u, delta_raw, A, B, C, D, z, delta_bias, y,
     _want(ssm_pool, "ssm_pool", _TORCH_DT[d.state_dtype])
     if ssm_pool.dim() != 3 or tuple(ssm_pool.shape[1:]) != (d.dim, d.dstate):
         raise ValueError("ssm_pool must be [slots, dim, dstate]")
+    ns = int(ssm_pool.shape[0])
     _want(state_indices, "state_indices", torch.int32, (Bd,))
+    _debug_check(ns, state_indices)
     _check(lib().mamba1_selective_state_update(ctypes.byref(cdims1(d)), _ptr(u), _ptr(delta_raw), _ptr(A), _ptr(B),
                                                _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-                                               1 if delta_softplus else 0, _ptr(y), _ptr(ssm_pool),
+                                               1 if delta_softplus else 0, _ptr(y), _ptr(ssm_pool), ns,
                                                _ptr(state_indices), Bd, _stream(stream)),
            "mamba1_selective_state_update")
 
@@ -433,19 +476,40 @@ def mamba2_mixed_fwd(d: Dims, xbc, dt_raw, z, conv_w, conv_b, A_log, dt_bias, D,
         _want(t, n, torch.float32, (H,))
     _want(xbc_post, "xbc_post", _xdt(d, xbc_dtype), (rows, d.conv_dim))
     _want(y, "y", _TORCH_DT[d.out_dtype], (rows, d.d_inner))
-    _want(ssm_pool, "ssm_pool", _TORCH_DT[d.state_dtype])
-    _want(conv_pool, "conv_pool", _TORCH_DT[d.state_dtype])
+    ns = _both_slots(d, ssm_pool, conv_pool)
     _want(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,))
     _want(prefill_indices, "prefill_indices", torch.int32, (nseq,))
     _want(has_initial_state, "has_initial_state", torch.uint8, (nseq,), optional=True)
     _want(decode_indices, "decode_indices", torch.int32, (Bd,))
+    _debug_check(ns, prefill_indices, decode_indices)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     c = cdims(d, xbc_dtype)
     _check(lib().mamba2_mixed_fwd(ctypes.byref(c), _ptr(xbc), _ptr(dt_raw), _ptr(z), _ptr(conv_w), _ptr(conv_b),
                                   _ptr(A_log), _ptr(dt_bias), _ptr(D), _ptr(xbc_post), _ptr(y), _ptr(ssm_pool),
-                                  _ptr(conv_pool), _ptr(cu_seqlens), nseq, T, _ptr(prefill_indices),
+                                  _ptr(conv_pool), ns, _ptr(cu_seqlens), nseq, T, _ptr(prefill_indices),
                                   _ptr(has_initial_state), _ptr(decode_indices), Bd, _ptr(workspace), ws_bytes,
                                   _stream(stream)), "mamba2_mixed_fwd")
+
+
+# ------------------------------------------------------------------ slot index safety
+
+def mamba2_read_slot_errors(reset: bool = False, *, stream=None) -> int:
+    """How many times kernels on the current device skipped a row or sequence whose slot
+    index was >= its pool's slot count (since the last reset). Waits for the stream."""
+    out = torch.empty(4, dtype=torch.int32, device="cuda")
+    _check(lib().mamba2_read_slot_errors(_ptr(out), 1 if reset else 0, _stream(stream)), "mamba2_read_slot_errors")
+    return int(out[0].item())
+
+
+def check_slot_indices(indices, num_slots: int, *, stream=None):
+    """Debug check of one int32 index table on the device: returns (entries >= num_slots,
+    entries in [0, num_slots) that repeat an earlier one). Waits for the stream."""
+    _want(indices, "indices", torch.int32)
+    res = torch.empty(2, dtype=torch.int32, device=indices.device)
+    _check(lib().mamba2_check_slot_indices(_ptr(indices), int(indices.numel()), int(num_slots), _ptr(res),
+                                           _stream(stream)), "mamba2_check_slot_indices")
+    r = res.cpu()
+    return int(r[0]), int(r[1])
 
 
 # ------------------------------------------------------------------ slot allocator

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <new>
 #include <cstdio>
 #include <string>
 #include <vector>
@@ -100,6 +101,21 @@ int hip_status(hipError_t e, const char *what) {
     return ok();
 }
 
+// The device word (current device) in which kernels count the pool indices >= num_slots
+// that they skip; looked up right before a launch.
+int slot_word(unsigned **err) {
+    const hipError_t e = m2::slot_error_word(err);
+    if (e != hipSuccess) return fail(MAMBA2_ERR_HIP, "slot error word: %s", hipGetErrorString(e));
+    return MAMBA2_OK;
+}
+
+#define SLOT_WORD(err)             \
+    unsigned *err = nullptr;       \
+    do {                           \
+        int st_ = slot_word(&err); \
+        if (st_) return st_;       \
+    } while (0)
+
 }  // namespace
 
 extern "C" {
@@ -135,10 +151,12 @@ int mamba2_chunk_scan_workspace_bytes(const mamba2_dims *d, int64_t total_tokens
 }
 
 int mamba2_conv1d_fwd(const mamba2_dims *d, const void *xbc, const float *conv_w, const float *conv_b, void *xbc_out,
-                      void *conv_pool, const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens,
-                      const int32_t *state_indices, const uint8_t *has_initial_state, void *stream) {
+                      void *conv_pool, int32_t num_slots, const int32_t *cu_seqlens, int32_t nseq,
+                      int64_t total_tokens, const int32_t *state_indices, const uint8_t *has_initial_state,
+                      void *stream) {
     int st = check_conv(d);
     if (st) return st;
+    if (num_slots < 0) return fail(MAMBA2_ERR_INVALID_ARG, "num_slots must be >= 0 (got %d)", num_slots);
     if (nseq < 0 || total_tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative nseq or total_tokens");
     if (nseq == 0) {
         if (total_tokens != 0) return fail(MAMBA2_ERR_INVALID_ARG, "tokens without sequences");
@@ -148,30 +166,36 @@ int mamba2_conv1d_fwd(const mamba2_dims *d, const void *xbc, const float *conv_w
     REQUIRE_IDX(cu_seqlens); REQUIRE_IDX(state_indices);
     if (total_tokens > 0) { REQUIRE_PTR(xbc); REQUIRE_PTR(xbc_out); }
     if (xbc && xbc == xbc_out) return fail(MAMBA2_ERR_INVALID_ARG, "xbc_out must not alias xbc");
+    SLOT_WORD(err);
     m2::ConvFwdArgs a{xbc, conv_w, conv_b, xbc_out, conv_pool, cu_seqlens, state_indices, has_initial_state, nseq,
-                      total_tokens};
+                      total_tokens, num_slots, err};
     return hip_status(m2::launch_conv_fwd(shape_of(d), a, static_cast<hipStream_t>(stream)), "conv1d_fwd launch");
 }
 
 int mamba2_conv1d_update(const mamba2_dims *d, const void *xbc, const float *conv_w, const float *conv_b,
-                         void *xbc_out, void *conv_pool, const int32_t *state_indices, int32_t batch, void *stream) {
+                         void *xbc_out, void *conv_pool, int32_t num_slots, const int32_t *state_indices,
+                         int32_t batch, void *stream) {
     int st = check_conv(d);
     if (st) return st;
+    if (num_slots < 0) return fail(MAMBA2_ERR_INVALID_ARG, "num_slots must be >= 0 (got %d)", num_slots);
     if (batch < 0) return fail(MAMBA2_ERR_INVALID_ARG, "batch < 0");
     if (batch == 0) return ok();
     REQUIRE_PTR(xbc); REQUIRE_PTR(conv_w); OPT_PTR(conv_b); REQUIRE_PTR(xbc_out); REQUIRE_PTR(conv_pool);
     REQUIRE_IDX(state_indices);
     if (xbc == xbc_out) return fail(MAMBA2_ERR_INVALID_ARG, "xbc_out must not alias xbc");
-    m2::ConvUpdateArgs a{xbc, conv_w, conv_b, xbc_out, conv_pool, state_indices, batch};
+    SLOT_WORD(err);
+    m2::ConvUpdateArgs a{xbc, conv_w, conv_b, xbc_out, conv_pool, state_indices, batch, num_slots, err};
     return hip_status(m2::launch_conv_update(shape_of(d), a, static_cast<hipStream_t>(stream)), "conv1d_update launch");
 }
 
 int mamba2_chunk_scan_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw, const float *A_log,
                           const float *dt_bias, const float *D, const void *z, void *y, void *ssm_pool,
-                          const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens, const int32_t *state_indices,
-                          const uint8_t *has_initial_state, void *workspace, size_t workspace_bytes, void *stream) {
+                          int32_t num_slots, const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens,
+                          const int32_t *state_indices, const uint8_t *has_initial_state, void *workspace,
+                          size_t workspace_bytes, void *stream) {
     int st = check_scan(d);
     if (st) return st;
+    if (num_slots < 0) return fail(MAMBA2_ERR_INVALID_ARG, "num_slots must be >= 0 (got %d)", num_slots);
     if (nseq < 0 || total_tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative nseq or total_tokens");
     if (nseq == 0) {
         if (total_tokens != 0) return fail(MAMBA2_ERR_INVALID_ARG, "tokens without sequences");
@@ -188,34 +212,41 @@ int mamba2_chunk_scan_fwd(const mamba2_dims *d, const void *xbc, const void *dt_
             return fail(MAMBA2_ERR_WORKSPACE, "chunk scan needs %zu workspace bytes, got %zu", need, workspace_bytes);
         OPT_PTR(workspace);
         if (workspace == xbc || workspace == y) return fail(MAMBA2_ERR_INVALID_ARG, "xbc, y and workspace must not alias");
+        SLOT_WORD(err);
         m2::FusedArgs fa{xbc, nullptr, nullptr, nullptr, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, cu_seqlens,
                          state_indices, has_initial_state, nseq, total_tokens, nullptr, nullptr, nullptr};
+        fa.num_slots = num_slots;
+        fa.err = err;
         return hip_status(m2::launch_block_scan(s, fa, workspace, static_cast<hipStream_t>(stream)),
                           "chunk_scan launch");
     }
-    m2::ScanArgs a{xbc, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, cu_seqlens, state_indices, has_initial_state,
-                   nseq, total_tokens};
+    SLOT_WORD(err);
+    m2::ScanArgs a{xbc,   dt_raw, A_log, dt_bias,      D,         z,   y, ssm_pool, cu_seqlens, state_indices,
+                   has_initial_state, nseq, total_tokens, num_slots, err};
     return hip_status(m2::launch_chunk_scan(s, a, static_cast<hipStream_t>(stream)), "chunk_scan launch");
 }
 
 int mamba2_state_update(const mamba2_dims *d, const void *xbc, const void *dt_raw, const float *A_log,
                         const float *dt_bias, const float *D, const void *z, void *y, void *ssm_pool,
-                        const int32_t *state_indices, int32_t batch, void *stream) {
+                        int32_t num_slots, const int32_t *state_indices, int32_t batch, void *stream) {
     int st = check_state_update(d);
     if (st) return st;
+    if (num_slots < 0) return fail(MAMBA2_ERR_INVALID_ARG, "num_slots must be >= 0 (got %d)", num_slots);
     if (batch < 0) return fail(MAMBA2_ERR_INVALID_ARG, "batch < 0");
     if (batch == 0) return ok();
     REQUIRE_PTR(xbc); REQUIRE_PTR(dt_raw); REQUIRE_PTR(A_log); REQUIRE_PTR(dt_bias); REQUIRE_PTR(D);
     OPT_PTR(z); REQUIRE_PTR(y); REQUIRE_PTR(ssm_pool); REQUIRE_IDX(state_indices);
-    m2::StateUpdateArgs a{xbc, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, state_indices, batch};
+    SLOT_WORD(err);
+    m2::StateUpdateArgs a{xbc, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, state_indices, batch, num_slots, err};
     return hip_status(m2::launch_state_update(shape_of(d), a, static_cast<hipStream_t>(stream)), "state_update launch");
 }
 
 int mamba2_conv1d_update_multi(const mamba2_dims *d, const void *xbc, const float *conv_w, const float *conv_b,
-                               void *xbc_out, void *conv_pool, const int32_t *src_indices,
+                               void *xbc_out, void *conv_pool, int32_t num_slots, const int32_t *src_indices,
                                const int32_t *dst_indices, int32_t batch, int32_t tokens, void *stream) {
     int st = check_conv(d);
     if (st) return st;
+    if (num_slots < 0) return fail(MAMBA2_ERR_INVALID_ARG, "num_slots must be >= 0 (got %d)", num_slots);
     if (batch < 0 || tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative batch or tokens");
     if (batch == 0 || tokens == 0) return ok();
     REQUIRE_PTR(xbc); REQUIRE_PTR(conv_w); OPT_PTR(conv_b); REQUIRE_PTR(xbc_out); REQUIRE_PTR(conv_pool);
@@ -223,31 +254,35 @@ int mamba2_conv1d_update_multi(const mamba2_dims *d, const void *xbc, const floa
     if (dst_indices && (reinterpret_cast<uintptr_t>(dst_indices) & 3u))
         return fail(MAMBA2_ERR_INVALID_ARG, "dst_indices is not 4-byte aligned");
     if (xbc == xbc_out) return fail(MAMBA2_ERR_INVALID_ARG, "xbc_out must not alias xbc");
-    m2::ConvMultiArgs a{xbc, conv_w, conv_b, xbc_out, conv_pool, src_indices, dst_indices, batch, tokens};
+    SLOT_WORD(err);
+    m2::ConvMultiArgs a{xbc, conv_w, conv_b, xbc_out, conv_pool, src_indices, dst_indices, batch, tokens, num_slots, err};
     return hip_status(m2::launch_conv_update_multi(shape_of(d), a, static_cast<hipStream_t>(stream)),
                       "conv1d_update_multi launch");
 }
 
 int mamba2_state_update_multi(const mamba2_dims *d, const void *xbc, const void *dt_raw, const float *A_log,
                               const float *dt_bias, const float *D, const void *z, void *y, void *ssm_pool,
-                              const int32_t *src_indices, const int32_t *dst_indices, int32_t batch, int32_t tokens,
-                              void *stream) {
+                              int32_t num_slots, const int32_t *src_indices, const int32_t *dst_indices,
+                              int32_t batch, int32_t tokens, void *stream) {
     int st = check_state_update(d);
     if (st) return st;
+    if (num_slots < 0) return fail(MAMBA2_ERR_INVALID_ARG, "num_slots must be >= 0 (got %d)", num_slots);
     if (batch < 0 || tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative batch or tokens");
     if (batch == 0 || tokens == 0) return ok();
     REQUIRE_PTR(xbc); REQUIRE_PTR(dt_raw); REQUIRE_PTR(A_log); REQUIRE_PTR(dt_bias); REQUIRE_PTR(D);
     OPT_PTR(z); REQUIRE_PTR(y); REQUIRE_PTR(ssm_pool); REQUIRE_IDX(src_indices);
     if (dst_indices && (reinterpret_cast<uintptr_t>(dst_indices) & 3u))
         return fail(MAMBA2_ERR_INVALID_ARG, "dst_indices is not 4-byte aligned");
-    m2::MultiStepArgs a{xbc, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, src_indices, dst_indices, batch, tokens};
+    SLOT_WORD(err);
+    m2::MultiStepArgs a{xbc,         dt_raw,      A_log, dt_bias, D,         z, y, ssm_pool, src_indices,
+                        dst_indices, batch, tokens, num_slots, err};
     return hip_status(m2::launch_state_update_multi(shape_of(d), a, static_cast<hipStream_t>(stream)),
                       "state_update_multi launch");
 }
 
 int mamba2_mixed_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw, const void *z, const float *conv_w,
                      const float *conv_b, const float *A_log, const float *dt_bias, const float *D, void *xbc_post,
-                     void *y, void *ssm_pool, void *conv_pool, const int32_t *cu_seqlens, int32_t nseq,
+                     void *y, void *ssm_pool, void *conv_pool, int32_t num_slots, const int32_t *cu_seqlens, int32_t nseq,
                      int64_t total_tokens, const int32_t *prefill_indices, const uint8_t *has_initial_state,
                      const int32_t *decode_indices, int32_t decode_batch, void *workspace, size_t workspace_bytes,
                      void *stream) {
@@ -265,15 +300,15 @@ int mamba2_mixed_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw, 
             // whole prefill in one call (fused for the Nemotron head shape); xbc_post rows of the
             // prefill segment are not written
             st = mamba2_prefill_fwd(d, xbc, dt_raw, z, conv_w, conv_b, A_log, dt_bias, D, nullptr, 0.0f, 0, y,
-                                    ssm_pool, conv_pool, cu_seqlens, nseq, total_tokens, prefill_indices,
+                                    ssm_pool, conv_pool, num_slots, cu_seqlens, nseq, total_tokens, prefill_indices,
                                     has_initial_state, workspace, workspace_bytes, stream);
             if (st) return st;
         } else {
-            st = mamba2_conv1d_fwd(d, xbc, conv_w, conv_b, xbc_post, conv_pool, cu_seqlens, nseq, total_tokens,
-                                   prefill_indices, has_initial_state, stream);
+            st = mamba2_conv1d_fwd(d, xbc, conv_w, conv_b, xbc_post, conv_pool, num_slots, cu_seqlens, nseq,
+                                   total_tokens, prefill_indices, has_initial_state, stream);
             if (st) return st;
-            st = mamba2_chunk_scan_fwd(d, xbc_post, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, cu_seqlens, nseq,
-                                       total_tokens, prefill_indices, has_initial_state, nullptr, 0, stream);
+            st = mamba2_chunk_scan_fwd(d, xbc_post, dt_raw, A_log, dt_bias, D, z, y, ssm_pool, num_slots, cu_seqlens,
+                                       nseq, total_tokens, prefill_indices, has_initial_state, nullptr, 0, stream);
             if (st) return st;
         }
     }
@@ -284,10 +319,11 @@ int mamba2_mixed_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw, 
         const char *dtd = static_cast<const char *>(dt_raw) + total_tokens * s.H * ab;
         const char *zd = z ? static_cast<const char *>(z) + total_tokens * hp * ab : nullptr;
         char *yd = static_cast<char *>(y) + total_tokens * hp * ob;
-        st = mamba2_conv1d_update(d, xin, conv_w, conv_b, xpost, conv_pool, decode_indices, decode_batch, stream);
+        st = mamba2_conv1d_update(d, xin, conv_w, conv_b, xpost, conv_pool, num_slots, decode_indices, decode_batch,
+                                  stream);
         if (st) return st;
-        st = mamba2_state_update(d, xpost, dtd, A_log, dt_bias, D, zd, yd, ssm_pool, decode_indices, decode_batch,
-                                 stream);
+        st = mamba2_state_update(d, xpost, dtd, A_log, dt_bias, D, zd, yd, ssm_pool, num_slots, decode_indices,
+                                 decode_batch, stream);
         if (st) return st;
     }
     return ok();
@@ -347,13 +383,14 @@ int mamba2_gated_rmsnorm(const mamba2_dims *d, const void *y, const void *z, con
 int mamba2_prefill_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw, const void *z, const float *conv_w,
                        const float *conv_b, const float *A_log, const float *dt_bias, const float *D,
                        const float *norm_w, float norm_eps, int32_t norm_group, void *y, void *ssm_pool,
-                       void *conv_pool, const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens,
-                       const int32_t *state_indices, const uint8_t *has_initial_state, void *workspace,
-                       size_t workspace_bytes, void *stream) {
+                       void *conv_pool, int32_t num_slots, const int32_t *cu_seqlens, int32_t nseq,
+                       int64_t total_tokens, const int32_t *state_indices, const uint8_t *has_initial_state,
+                       void *workspace, size_t workspace_bytes, void *stream) {
     int st = check_conv(d);
     if (st) return st;
     st = check_scan(d);
     if (st) return st;
+    if (num_slots < 0) return fail(MAMBA2_ERR_INVALID_ARG, "num_slots must be >= 0 (got %d)", num_slots);
     if (norm_w) {
         st = check_norm(d, norm_group);
         if (st) return st;
@@ -380,21 +417,24 @@ int mamba2_prefill_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw
     const m2::LayerShape s = shape_of(d);
     // with a norm, the gate is applied by the norm pass (the scan writes ungated y)
     const void *scan_z = norm_w ? nullptr : z;
-    m2::ConvFwdArgs ca{xbc, conv_w, conv_b, workspace, conv_pool, cu_seqlens, state_indices, has_initial_state, nseq,
-                       total_tokens};
+    SLOT_WORD(err);
+    m2::ConvFwdArgs ca{xbc,  conv_w,       conv_b, workspace, conv_pool, cu_seqlens, state_indices, has_initial_state,
+                       nseq, total_tokens, num_slots, err};
     if (fused_path(d)) {
         m2::FusedArgs fa{xbc, conv_w, conv_b, conv_pool, dt_raw, A_log, dt_bias, D, scan_z, y, ssm_pool,
                          cu_seqlens, state_indices, has_initial_state, nseq, total_tokens, nullptr, nullptr, nullptr};
+        fa.num_slots = num_slots;
+        fa.err = err;
         st = hip_status(m2::launch_fused_prefill(s, fa, total_tokens > 0 ? workspace : nullptr, strm), "prefill launch");
         if (st) return st;
         st = hip_status(m2::launch_conv_state(s, ca, strm), "prefill conv state launch");
         if (st) return st;
     } else {
-        st = mamba2_conv1d_fwd(d, xbc, conv_w, conv_b, workspace, conv_pool, cu_seqlens, nseq, total_tokens,
-                               state_indices, has_initial_state, stream);
+        st = mamba2_conv1d_fwd(d, xbc, conv_w, conv_b, workspace, conv_pool, num_slots, cu_seqlens, nseq,
+                               total_tokens, state_indices, has_initial_state, stream);
         if (st) return st;
-        st = mamba2_chunk_scan_fwd(d, workspace, dt_raw, A_log, dt_bias, D, scan_z, y, ssm_pool, cu_seqlens, nseq,
-                                   total_tokens, state_indices, has_initial_state, nullptr, 0, stream);
+        st = mamba2_chunk_scan_fwd(d, workspace, dt_raw, A_log, dt_bias, D, scan_z, y, ssm_pool, num_slots,
+                                   cu_seqlens, nseq, total_tokens, state_indices, has_initial_state, nullptr, 0, stream);
         if (st) return st;
     }
     if (norm_w && total_tokens > 0)
@@ -430,11 +470,12 @@ size_t mamba1_ssm_slot_bytes(const mamba1_dims *d) {
 
 int mamba1_selective_scan_fwd(const mamba1_dims *d, const void *u, const void *delta_raw, const float *A,
                               const void *B, const void *C, const float *D, const void *z, const float *delta_bias,
-                              int32_t delta_softplus, void *y, void *ssm_pool, const int32_t *cu_seqlens,
-                              int32_t nseq, int64_t total_tokens, const int32_t *state_indices,
-                              const uint8_t *has_initial_state, void *stream) {
+                              int32_t delta_softplus, void *y, void *ssm_pool, int32_t num_slots,
+                              const int32_t *cu_seqlens, int32_t nseq, int64_t total_tokens,
+                              const int32_t *state_indices, const uint8_t *has_initial_state, void *stream) {
     int st = check_sel(d);
     if (st) return st;
+    if (num_slots < 0) return fail(MAMBA2_ERR_INVALID_ARG, "num_slots must be >= 0 (got %d)", num_slots);
     if (nseq < 0 || total_tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative nseq or total_tokens");
     if (nseq == 0) {
         if (total_tokens != 0) return fail(MAMBA2_ERR_INVALID_ARG, "tokens without sequences");
@@ -447,25 +488,28 @@ int mamba1_selective_scan_fwd(const mamba1_dims *d, const void *u, const void *d
         if (y == u || y == delta_raw || (z && y == z)) return fail(MAMBA2_ERR_INVALID_ARG, "y must not alias inputs");
     }
     m2::SelShape s{d->dim, d->dstate, d->ngroups, d->act_dtype, d->state_dtype, d->out_dtype};
+    SLOT_WORD(err);
     m2::SelScanArgs a{u, delta_raw, A, B, C, D, z, delta_bias, delta_softplus ? 1 : 0, y, ssm_pool, cu_seqlens,
-                      state_indices, has_initial_state, nseq, total_tokens};
+                      state_indices, has_initial_state, nseq, total_tokens, num_slots, err};
     return hip_status(m2::launch_selective_scan(s, a, static_cast<hipStream_t>(stream)), "selective_scan launch");
 }
 
 int mamba1_selective_state_update(const mamba1_dims *d, const void *u, const void *delta_raw, const float *A,
                                   const void *B, const void *C, const float *D, const void *z,
                                   const float *delta_bias, int32_t delta_softplus, void *y, void *ssm_pool,
-                                  const int32_t *state_indices, int32_t batch, void *stream) {
+                                  int32_t num_slots, const int32_t *state_indices, int32_t batch, void *stream) {
     int st = check_sel(d);
     if (st) return st;
+    if (num_slots < 0) return fail(MAMBA2_ERR_INVALID_ARG, "num_slots must be >= 0 (got %d)", num_slots);
     if (batch < 0) return fail(MAMBA2_ERR_INVALID_ARG, "batch < 0");
     if (batch == 0) return ok();
     REQUIRE_PTR(u); REQUIRE_PTR(delta_raw); REQUIRE_PTR(A); REQUIRE_PTR(B); REQUIRE_PTR(C); OPT_PTR(D); OPT_PTR(z);
     OPT_PTR(delta_bias); REQUIRE_PTR(y); REQUIRE_PTR(ssm_pool); REQUIRE_IDX(state_indices);
     if (y == u || y == delta_raw || (z && y == z)) return fail(MAMBA2_ERR_INVALID_ARG, "y must not alias inputs");
     m2::SelShape s{d->dim, d->dstate, d->ngroups, d->act_dtype, d->state_dtype, d->out_dtype};
+    SLOT_WORD(err);
     m2::SelUpdateArgs a{u, delta_raw, A, B, C, D, z, delta_bias, delta_softplus ? 1 : 0, y, ssm_pool, state_indices,
-                        batch};
+                        batch, num_slots, err};
     return hip_status(m2::launch_selective_update(s, a, static_cast<hipStream_t>(stream)),
                       "selective_state_update launch");
 }
@@ -478,11 +522,18 @@ struct mamba2_slots {
 
 int mamba2_slots_create(int32_t num_slots, mamba2_slots **out) {
     if (!out) return fail(MAMBA2_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
     if (num_slots <= 0) return fail(MAMBA2_ERR_INVALID_ARG, "num_slots must be positive");
-    auto *s = new mamba2_slots;
-    s->free_list.reserve(num_slots);
-    for (int32_t i = num_slots - 1; i >= 0; --i) s->free_list.push_back(i);  // slot 0 is handed out first
-    s->in_use.assign(num_slots, 0);
+    auto *s = new (std::nothrow) mamba2_slots;
+    if (!s) return fail(MAMBA2_ERR_NO_SLOT, "out of host memory for %d slots", num_slots);
+    try {  // no exception may cross the C ABI
+        s->free_list.reserve(num_slots);
+        for (int32_t i = num_slots - 1; i >= 0; --i) s->free_list.push_back(i);  // slot 0 is handed out first
+        s->in_use.assign(num_slots, 0);
+    } catch (...) {
+        delete s;
+        return fail(MAMBA2_ERR_NO_SLOT, "out of host memory for %d slots", num_slots);
+    }
     *out = s;
     return ok();
 }
@@ -524,6 +575,20 @@ const char *mamba2_status_string(int status) {
 }
 
 const char *mamba2_last_error(void) { return g_last_error.c_str(); }
+
+int mamba2_read_slot_errors(uint32_t *count, int32_t reset, void *stream) {
+    REQUIRE_IDX(count);
+    return hip_status(m2::launch_read_slot_errors(count, reset ? 1 : 0, static_cast<hipStream_t>(stream)),
+                      "read_slot_errors launch");
+}
+
+int mamba2_check_slot_indices(const int32_t *indices, int32_t n, int32_t num_slots, uint32_t *result, void *stream) {
+    if (n < 0 || num_slots < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative n or num_slots");
+    REQUIRE_PTR(result);
+    if (n > 0) REQUIRE_IDX(indices);
+    return hip_status(m2::launch_check_slots(indices, n, num_slots, result, static_cast<hipStream_t>(stream)),
+                      "check_slot_indices launch");
+}
 
 const char *mamba2_version(void) { return "mamba2-gfx950 0.1"; }
 

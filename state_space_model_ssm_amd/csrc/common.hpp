@@ -13,6 +13,17 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 enum Dt : int { DT_F32 = 0, DT_BF16 = 1 };
 
+// Pool slot for an index read from the caller's table: the index itself when it lies in
+// [0, num_slots) or is negative (padding), -1 when it is >= num_slots (the row or sequence is
+// then skipped like padding and, by the one thread that `reports`, counted in *err).
+__device__ __forceinline__ int pool_slot(int s, int num_slots, unsigned *err, bool reports) {
+    if (s >= num_slots) {
+        if (reports && err) atomicAdd(err, 1u);
+        return -1;
+    }
+    return s;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
 // float -> bf16, round to nearest even (the conversion clang defines for __bf16).

@@ -43,7 +43,8 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(ConvFwdArgs a, int64_t cd
 
     int seq = find_seq(a.cu, a.nseq, t0);
     int64_t seq_start = a.cu[seq], seq_end = a.cu[seq + 1];
-    int slot = a.idx[seq];
+    // (conv_state_kernel, run for every sequence after this one, counts bad indices)
+    int slot = pool_slot(a.idx[seq], a.num_slots, a.err, false);
 
     if (t1 <= seq_end) {
         // The run lies in one sequence (all but the runs that cross a boundary): every
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(ConvFwdArgs a, int64_t cd
             while (seq + 1 < a.nseq && a.cu[seq + 1] <= t) ++seq;
             seq_start = a.cu[seq];
             seq_end = a.cu[seq + 1];
-            slot = a.idx[seq];
+            slot = pool_slot(a.idx[seq], a.num_slots, a.err, false);
             fill_window(t);
         }
         float u[8], o[8];
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(256) void conv_state_kernel(ConvFwdArgs a, int64_t 
     const int seq = blockIdx.y;
     const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (c0 >= cdim) return;
-    const int slot = a.idx[seq];
+    const int slot = pool_slot(a.idx[seq], a.num_slots, a.err, c0 == 0);
     if (slot < 0) return;
     const int64_t start = a.cu[seq];
     const int64_t len = a.cu[seq + 1] - start;

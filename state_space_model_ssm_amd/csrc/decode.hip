@@ -24,6 +24,9 @@
 //     lane (they hit L2: the 16 heads of a group share them);
 //   * a head's tile is split across `psplit` workgroups when rows x heads alone
 //     would not fill the 256 CUs.
+#include <atomic>
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -49,7 +52,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(StateUpdateArgs a, in
     const int p_first = pblk * kRpi * ITERS + r;
     const int64_t yrow = (int64_t)row * HP + (int64_t)head * P;
 
-    const int slot = a.idx[row];
+    const int slot = pool_slot(a.idx[row], a.num_slots, a.err, blockIdx.x == 0 && tid == 0);
     if (slot < 0) {  // padding row: y = 0, no state access
         if (lr == 0) {
 #pragma unroll
@@ -259,7 +262,7 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
                 if (prow(it) < P) st(a.y, out_dt, ybase + (int64_t)t * HP + prow(it), yv[it]);
         }
     };
-    const int src = a.src[row];
+    const int src = pool_slot(a.src[row], a.num_slots, a.err, blockIdx.x == 0 && tid == 0);
     if (src < 0) {  // padding row: y = 0, no state access
         if (ylane)
             for (int it = 0; it < ITERS; ++it)
@@ -363,7 +366,8 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
             }
             const float dt = sDt[0][u];
             const float decay = sDt[1][u];
-            const int d = a.dst ? a.dst[(int64_t)row * T + t] : -1;
+            const int d = a.dst ? pool_slot(a.dst[(int64_t)row * T + t], a.num_slots, a.err, blockIdx.x == 0 && tid == 0)
+                                : -1;
             float yv[ITERS];
 #pragma unroll
             for (int it = 0; it < ITERS; ++it) {
@@ -457,7 +461,7 @@ __global__ __launch_bounds__(256) void conv_update_kernel(ConvUpdateArgs a, int6
     const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (c0 >= cdim) return;
     XT *out = static_cast<XT *>(a.out) + (int64_t)row * cdim + c0;
-    const int slot = a.idx[row];
+    const int slot = pool_slot(a.idx[row], a.num_slots, a.err, c0 == 0);
     float o[8];
     if (slot < 0) {
 #pragma unroll
@@ -522,7 +526,7 @@ __global__ __launch_bounds__(256) void conv_update_multi_kernel(ConvMultiArgs a,
     const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (c0 >= cdim) return;
     const int T = a.T;
-    const int src = a.src[row];
+    const int src = pool_slot(a.src[row], a.num_slots, a.err, c0 == 0);
     float o[8];
     if (src < 0) {
 #pragma unroll
@@ -554,7 +558,7 @@ __global__ __launch_bounds__(256) void conv_update_multi_kernel(ConvMultiArgs a,
 #pragma unroll
         for (int j = 0; j < 8; ++j) win[W - 2][j] = u[j];
         if (a.dst) {
-            const int d = a.dst[(int64_t)row * T + t];
+            const int d = pool_slot(a.dst[(int64_t)row * T + t], a.num_slots, a.err, c0 == 0);
             if (d >= 0)
 #pragma unroll
                 for (int k = 0; k < W - 1; ++k) store_k<ST, 8>(pool + ((int64_t)d * (W - 1) + k) * cdim + c0, win[k]);
@@ -591,6 +595,95 @@ static hipError_t launch_cum_s(const LayerShape &s, const ConvMultiArgs &a, hipS
 hipError_t launch_conv_update_multi(const LayerShape &s, const ConvMultiArgs &a, hipStream_t stream) {
     if (a.batch == 0 || a.T == 0) return hipSuccess;
     return s.act_dt == DT_BF16 ? launch_cum_s<bf16>(s, a, stream) : launch_cum_s<float>(s, a, stream);
+}
+
+}  // namespace m2
+
+// ----------------------------------------------------------------- slot index checks
+namespace m2 {
+
+// Count of pool indices >= the caller's slot count that kernels skipped, on this device:
+// a file-scope device word, one copy per device for the life of the process. Host code
+// never passes the name itself to a kernel; it passes the address that slot_error_word
+// looks up (once per device) with hipGetSymbolAddress.
+static __device__ __align__(16) unsigned g_slot_errors[4];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<unsigned *> g_err_addr[kMaxDevices];
+std::mutex g_err_mu;
+}  // namespace
+
+hipError_t slot_error_word(unsigned **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    unsigned *p = g_err_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_err_mu);
+        p = g_err_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            void *sym = nullptr;
+            e = hipGetSymbolAddress(&sym, HIP_SYMBOL(g_slot_errors));
+            if (e != hipSuccess) return e;
+            p = static_cast<unsigned *>(sym);
+            g_err_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+// One workgroup: indices >= num_slots, and indices in [0, num_slots) that repeat an earlier
+// entry of the list (O(n^2) compares: a debug check).
+__global__ __launch_bounds__(1024) void check_slots_kernel(const int32_t *idx, int n, int num_slots,
+                                                          unsigned *result) {
+    __shared__ unsigned s_bad, s_dup;
+    if (threadIdx.x == 0) {
+        s_bad = 0;
+        s_dup = 0;
+    }
+    __syncthreads();
+    unsigned bad = 0, dup = 0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int v = idx[i];
+        if (v >= num_slots) {
+            ++bad;
+        } else if (v >= 0) {
+            for (int j = 0; j < i; ++j)
+                if (idx[j] == v) {
+                    ++dup;
+                    break;
+                }
+        }
+    }
+    atomicAdd(&s_bad, bad);
+    atomicAdd(&s_dup, dup);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        result[0] = s_bad;
+        result[1] = s_dup;
+    }
+}
+
+// Copies the count into the caller's memory and, if asked, clears it (one thread).
+__global__ void read_slot_errors_kernel(unsigned *word, unsigned *dst, int reset) {
+    dst[0] = word[0];
+    if (reset) word[0] = 0;
+}
+
+hipError_t launch_read_slot_errors(unsigned *dst, int reset, hipStream_t stream) {
+    unsigned *word = nullptr;
+    hipError_t e = slot_error_word(&word);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(read_slot_errors_kernel, dim3(1), dim3(1), 0, stream, word, dst, reset);
+    return hipGetLastError();
+}
+
+hipError_t launch_check_slots(const int32_t *idx, int n, int num_slots, unsigned *result, hipStream_t stream) {
+    hipLaunchKernelGGL(check_slots_kernel, dim3(1), dim3(1024), 0, stream, idx, n, num_slots, result);
+    return hipGetLastError();
 }
 
 }  // namespace m2

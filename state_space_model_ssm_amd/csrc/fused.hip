@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(XT) 
             // one sequence holds the whole run: every row is loaded up front, clamped into it
             constexpr int NR = RL + W - 1;
             const int64_t ss = cus[sa], se = cus[sa + 1];
-            const int slot = a.idx[sa];
+            const int slot = pool_slot(a.idx[sa], a.num_slots, a.err, false);
             // rows as raw bits (widened where used) at 32-bit offsets from the window's
             // first row: fewer registers, so more workgroups share a CU
             const int64_t r0 = t0 - (W - 1);
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(XT) 
             // a sequence boundary inside the run: token by token, restarting the window
             int seq = sa;
             int64_t seq_start = cus[seq], seq_end = cus[seq + 1];
-            int slot = a.idx[seq];
+            int slot = pool_slot(a.idx[seq], a.num_slots, a.err, false);
             float win[W - 1][8];
             auto fill_window = [&](int64_t t) {
                 const bool init = slot >= 0 && a.has_init && a.has_init[seq];
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(XT) 
                     while (seq + 1 < a.nseq && cus[seq + 1] <= t) ++seq;
                     seq_start = cus[seq];
                     seq_end = cus[seq + 1];
-                    slot = a.idx[seq];
+                    slot = pool_slot(a.idx[seq], a.num_slots, a.err, false);
                     fill_window(t);
                 }
                 float u[8], o[8];
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     const bool first = sflags & kSegFirst, only = sflags & kSegOnly;
     const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N, cdim = HP + 2 * GN;
     const int g = head / (H / G);
-    const int slot = a.idx[seq];
+    const int slot = pool_slot(a.idx[seq], a.num_slots, a.err, head == 0 && tid == 0 && first);
     bf16 *y = static_cast<bf16 *>(a.y);
 
     if (slot < 0) {
@@ -822,7 +822,7 @@ __global__ __launch_bounds__(256) void fused_seg_combine_kernel(FusedArgs a, int
     const int head = blockIdx.x, v = blockIdx.y, k = v % smax;
     const int32_t *sg = a.seg + 4 * v;
     if (k == 0 || sg[0] >= sg[1]) return;  // first segments are exact; empty ones hold no tokens
-    const int slot = a.idx[sg[2]];
+    const int slot = pool_slot(a.idx[sg[2]], a.num_slots, a.err, false);
     if (slot < 0) return;
     const bool last = k + 1 == smax || a.seg[4 * (v + 1)] >= a.seg[4 * (v + 1) + 1];
     const int p = 16 * wv + col;
@@ -912,7 +912,7 @@ __global__ __launch_bounds__(256) void fused_seg_fix_kernel(FusedArgs a, int H, 
                 found = true;
                 sstart = s0;
                 send = s1;
-                sv = a.idx[sg[2]] < 0 ? -1 : u;
+                sv = pool_slot(a.idx[sg[2]], a.num_slots, a.err, false) < 0 ? -1 : u;
             } else if (s0 > pos && s0 < next) {
                 next = s0;
             }

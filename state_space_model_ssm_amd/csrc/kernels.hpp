@@ -20,6 +20,8 @@ struct StateUpdateArgs {
     void *pool;           // [slots][H][P][N]
     const int32_t *idx;   // [batch]
     int batch;
+    int num_slots = 0;    // pool slots: indices >= num_slots are skipped like padding and counted in *err
+    unsigned *err = nullptr;  // the library's per-device count of such indices
 };
 
 struct ConvUpdateArgs {
@@ -29,6 +31,8 @@ struct ConvUpdateArgs {
     void *pool;           // [slots][W-1][Cdim]
     const int32_t *idx;
     int batch;
+    int num_slots = 0;    // pool slots: indices >= num_slots are skipped like padding and counted in *err
+    unsigned *err = nullptr;  // the library's per-device count of such indices
 };
 
 struct ConvFwdArgs {
@@ -41,6 +45,8 @@ struct ConvFwdArgs {
     const uint8_t *has_init;  // [nseq] or null
     int nseq;
     int64_t T;
+    int num_slots = 0;    // pool slots: indices >= num_slots are skipped like padding and counted in *err
+    unsigned *err = nullptr;  // the library's per-device count of such indices
 };
 
 struct ScanArgs {
@@ -54,6 +60,8 @@ struct ScanArgs {
     const uint8_t *has_init;
     int nseq;
     int64_t T;
+    int num_slots = 0;    // pool slots: indices >= num_slots are skipped like padding and counted in *err
+    unsigned *err = nullptr;  // the library's per-device count of such indices
 };
 
 // T tokens per row: activations [batch][T][...]; src [batch] (slot read before the
@@ -68,6 +76,8 @@ struct MultiStepArgs {
     void *pool;           // [slots][H][P][N]
     const int32_t *src, *dst;
     int batch, T;
+    int num_slots = 0;    // pool slots: indices >= num_slots are skipped like padding and counted in *err
+    unsigned *err = nullptr;  // the library's per-device count of such indices
 };
 
 struct ConvMultiArgs {
@@ -77,6 +87,8 @@ struct ConvMultiArgs {
     void *pool;           // [slots][W-1][Cdim]
     const int32_t *src, *dst;
     int batch, T;
+    int num_slots = 0;    // pool slots: indices >= num_slots are skipped like padding and counted in *err
+    unsigned *err = nullptr;  // the library's per-device count of such indices
 };
 
 // Fused prefill (fused.hip); cp / bt / cb are the workspace planes, set by
@@ -105,6 +117,8 @@ struct FusedArgs {
     float *seg_dec;    // [nseg][H]
     float *seg_lam;    // [block][H]: log2 decay from the segment's start through the block (blocks inside a segment)
     void *seg_hin;     // [nseg][H][4 waves][64 lanes][4] bf16x8: a later segment's true initial state, as MFMA operand
+    int num_slots = 0;    // pool slots: indices >= num_slots are skipped like padding and counted in *err
+    unsigned *err = nullptr;  // the library's per-device count of such indices
 };
 
 struct NormArgs {
@@ -136,6 +150,8 @@ struct SelScanArgs {
     const uint8_t *has_init;
     int nseq;
     int64_t T;
+    int num_slots = 0;    // pool slots: indices >= num_slots are skipped like padding and counted in *err
+    unsigned *err = nullptr;  // the library's per-device count of such indices
 };
 
 struct SelUpdateArgs {
@@ -150,7 +166,18 @@ struct SelUpdateArgs {
     void *pool;                  // [slots][Dc][N]
     const int32_t *idx;          // [batch]
     int batch;
+    int num_slots = 0;    // pool slots: indices >= num_slots are skipped like padding and counted in *err
+    unsigned *err = nullptr;  // the library's per-device count of such indices
 };
+
+// Device address of this library's count of out-of-range slot indices on the current
+// device (a file-scope device word, looked up once per device).
+hipError_t slot_error_word(unsigned **out);
+// Copies that count to dst (device memory) on the stream and clears it when reset != 0.
+hipError_t launch_read_slot_errors(unsigned *dst, int reset, hipStream_t st);
+// Debug check of one index list: result[0] = indices >= num_slots, result[1] = indices
+// (>= 0) equal to an earlier one; one workgroup, result written without a prior clear.
+hipError_t launch_check_slots(const int32_t *idx, int n, int num_slots, unsigned *result, hipStream_t st);
 
 // Each returns hipSuccess or the launch error. `supported` queries return
 // false for shapes outside the compiled set (no launch happens).

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int64_t cdim = HP + 2LL * G * N;
     const int g = head / (H / G);
     const int64_t start = a.cu[seq], end = a.cu[seq + 1];
-    const int slot = a.idx[seq];
+    const int slot = pool_slot(a.idx[seq], a.num_slots, a.err, head == 0 && tid == 0);
     const int64_t offX = (int64_t)head * P;
     const int64_t offB = HP + (int64_t)g * N;
     const int64_t offC = HP + (int64_t)G * N + (int64_t)g * N;
@@ -463,7 +463,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int64_t cdim = HP + 2LL * G * N;
     const int g = head / (H / G);
     const int64_t start = a.cu[seq], end = a.cu[seq + 1];
-    const int slot = a.idx[seq];
+    const int slot = pool_slot(a.idx[seq], a.num_slots, a.err, head == 0 && tid == 0);
     const int64_t offX = (int64_t)head * P;
     const int64_t offB = HP + (int64_t)g * N;
     const int64_t offC = HP + (int64_t)G * N + (int64_t)g * N;

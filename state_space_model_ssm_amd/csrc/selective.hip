@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void selective_scan_kernel(SelScanArgs a, int 
     const int c0 = cblk * CH;                 // first channel of the workgroup
     const int g = c0 / (Dc / G);              // its group (CH divides Dc / G)
     const int64_t start = a.cu[seq], end = a.cu[seq + 1];
-    const int slot = a.idx[seq];
+    const int slot = pool_slot(a.idx[seq], a.num_slots, a.err, cblk == 0 && tid == 0);
     OT *y = static_cast<OT *>(a.y);
 
     if (slot < 0) {
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) void selective_update_kernel(SelUpdateArgs a, 
     const int cl = tid / LPC, sg = tid % LPC, n0 = 4 * sg;
     const int ch = blockIdx.x * CH + cl;
     const int g = (blockIdx.x * CH) / (Dc / G);
-    const int slot = a.idx[row];
+    const int slot = pool_slot(a.idx[row], a.num_slots, a.err, blockIdx.x == 0 && tid == 0);
     OT *y = static_cast<OT *>(a.y);
     if (slot < 0) {
         if (sg == 0) Io<OT>::put(y, (int64_t)row * Dc + ch, 0.0f);

@@ -83,33 +83,42 @@ def test_invalid_arguments_rejected_without_gpu(lib):
     good = P(0x10000)
     mis = P(0x10004)
     # NULL required pointer
-    st = lib.mamba2_state_update(_cd(), None, good, good, good, good, None, good, good, good, 4, None)
+    st = lib.mamba2_state_update(_cd(), None, good, good, good, good, None, good, good, 8, good, 4, None)
     assert st == B.ERR_INVALID_ARG and b"xbc" in lib.mamba2_last_error()
     # misaligned pointer
-    st = lib.mamba2_state_update(_cd(), mis, good, good, good, good, None, good, good, good, 4, None)
+    st = lib.mamba2_state_update(_cd(), mis, good, good, good, good, None, good, good, 8, good, 4, None)
     assert st == B.ERR_INVALID_ARG and b"aligned" in lib.mamba2_last_error()
     # negative batch
-    st = lib.mamba2_state_update(_cd(), good, good, good, good, good, None, good, good, good, -1, None)
+    st = lib.mamba2_state_update(_cd(), good, good, good, good, good, None, good, good, 8, good, -1, None)
     assert st == B.ERR_INVALID_ARG
+    # negative pool slot count
+    st = lib.mamba2_state_update(_cd(), good, good, good, good, good, None, good, good, -1, good, 4, None)
+    assert st == B.ERR_INVALID_ARG and b"num_slots" in lib.mamba2_last_error()
+    st = lib.mamba2_conv1d_update(_cd(), good, good, None, good, good, -3, good, 2, None)
+    assert st == B.ERR_INVALID_ARG and b"num_slots" in lib.mamba2_last_error()
     # zero rows: valid, nothing enqueued
-    assert lib.mamba2_state_update(_cd(), None, None, None, None, None, None, None, None, None, 0, None) == B.OK
-    assert lib.mamba2_conv1d_update(_cd(), None, None, None, None, None, None, 0, None) == B.OK
-    assert lib.mamba2_conv1d_fwd(_cd(), None, None, None, None, None, None, 0, 0, None, None, None) == B.OK
+    assert lib.mamba2_state_update(_cd(), None, None, None, None, None, None, None, None, 0, None, 0, None) == B.OK
+    assert lib.mamba2_conv1d_update(_cd(), None, None, None, None, None, 0, None, 0, None) == B.OK
+    assert lib.mamba2_conv1d_fwd(_cd(), None, None, None, None, None, 0, None, 0, 0, None, None, None) == B.OK
     # aliasing conv output
-    st = lib.mamba2_conv1d_update(_cd(), good, good, None, good, good, good, 2, None)
+    st = lib.mamba2_conv1d_update(_cd(), good, good, None, good, good, 8, good, 2, None)
     assert st == B.ERR_INVALID_ARG and b"alias" in lib.mamba2_last_error()
     # tokens without sequences
-    st = lib.mamba2_chunk_scan_fwd(_cd(), good, good, good, good, good, None, good, good, good, 0, 5, good, None,
+    st = lib.mamba2_chunk_scan_fwd(_cd(), good, good, good, good, good, None, good, good, 8, good, 0, 5, good, None,
                                    None, 0, None)
     assert st == B.ERR_INVALID_ARG
     # a workspace smaller than the block form needs
-    st = lib.mamba2_chunk_scan_fwd(_cd(), good, good, good, good, good, None, good, good, good, 1, 64, good, None,
+    st = lib.mamba2_chunk_scan_fwd(_cd(), good, good, good, good, good, None, good, good, 8, good, 1, 64, good, None,
                                    good, 1024, None)
     assert st == B.ERR_WORKSPACE and b"workspace" in lib.mamba2_last_error()
     # unsupported chunk
     st = lib.mamba2_chunk_scan_fwd(_cd(NEMOTRON_H_8B.with_(chunk_size=96)), good, good, good, good, good, None, good,
-                                   good, good, 1, 5, good, None, None, 0, None)
+                                   good, 8, good, 1, 5, good, None, None, 0, None)
     assert st == B.ERR_UNSUPPORTED
+    # the slot checks reject bad arguments before any launch
+    assert lib.mamba2_check_slot_indices(good, -1, 4, good, None) == B.ERR_INVALID_ARG
+    assert lib.mamba2_check_slot_indices(good, 3, 4, None, None) == B.ERR_INVALID_ARG
+    assert lib.mamba2_read_slot_errors(None, 0, None) == B.ERR_INVALID_ARG
     assert lib.mamba2_status_string(B.ERR_UNSUPPORTED) == b"unsupported dims or dtype"
 
 
@@ -139,6 +148,20 @@ def test_binding_rejects_host_tensors(lib):
                                torch.zeros(2, dtype=torch.int32))
 
 
+def test_binding_checks_pool_shapes(lib):
+    """The binding derives num_slots from the pools and refuses pools of the wrong shape
+    (a pool that is not [slots, H, P, N] / [slots, W-1, Cdim] would let an index address
+    memory outside it)."""
+    import torch
+    d = TINY
+    with pytest.raises(ValueError, match="ssm_pool must be"):
+        B._ssm_slots(d, torch.zeros(4, d.nheads * d.headdim, d.dstate))
+    with pytest.raises(ValueError, match="conv_pool must be"):
+        B._conv_slots(d, torch.zeros(4, d.conv_width, d.conv_dim))
+    with pytest.raises(ValueError, match="device tensor"):  # right shape, but host memory
+        B._ssm_slots(d, torch.zeros(5, d.nheads, d.headdim, d.dstate))
+
+
 def test_prefill_workspace_and_validation_without_gpu(lib):
     """Workspace sizing of the fused prefill (B/C operand planes per 32-token block) and of the
     unfused composition (post-conv xBC), and the errors raised before any launch."""
@@ -161,8 +184,8 @@ def test_prefill_workspace_and_validation_without_gpu(lib):
     assert B.mamba2_prefill_workspace_bytes(d8f, 100) == 100 * d8f.conv_dim * 4
     assert B.mamba2_prefill_workspace_bytes(TINY, 64) == 64 * TINY.conv_dim * 4
     args = lambda ws, nbytes, norm=None, group=0: (_cd(d8), good, good, None, good, None, good, good, good, norm,
-                                                   ctypes.c_float(1e-5), group, good, good, good, good, 1, 64, good,
-                                                   None, ws, nbytes, None)
+                                                   ctypes.c_float(1e-5), group, good, good, good, 8, good, 1, 64,
+                                                   good, None, ws, nbytes, None)
     need = B.mamba2_prefill_workspace_bytes(d8, 64)
     st = lib.mamba2_prefill_fwd(*args(good, need - 16))
     assert st == B.ERR_WORKSPACE and b"workspace" in lib.mamba2_last_error()
