@@ -257,6 +257,26 @@ int mamba2_prefill_fwd(const mamba2_dims *dims, const void *xbc, const void *dt_
                        const int32_t *state_indices, const uint8_t *has_initial_state,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): mamba2_prefill_fwd with
+ * the same arguments except the workspace, which is a fixed device array inside
+ * the library, MAMBA2_STATIC_SCRATCH_BYTES per GPU, held from the time the
+ * library's code is loaded on that GPU until the process ends. The call allocates
+ * and frees nothing. A batch whose workspace (mamba2_prefill_workspace_bytes)
+ * exceeds the array is refused with MAMBA2_ERR_WORKSPACE before anything is
+ * enqueued (about 5,800 packed tokens at Nemotron-H-8B dims with bf16 y; split
+ * longer prefills into chunks). Every call on one GPU uses the same array, which
+ * keeps the last call's contents: calls that overlap on one GPU (two streams, two
+ * host threads) race and must be serialised by the caller. */
+#define MAMBA2_STATIC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int mamba2_prefill_fwd_noalloc(const mamba2_dims *dims, const void *xbc, const void *dt_raw, const void *z,
+                               const float *conv_w, const float *conv_b, const float *A_log,
+                               const float *dt_bias, const float *D, const float *norm_w, float norm_eps,
+                               int32_t norm_group, void *y, void *ssm_pool, void *conv_pool,
+                               int32_t num_slots, const int32_t *cu_seqlens, int32_t nseq,
+                               int64_t total_tokens, const int32_t *state_indices,
+                               const uint8_t *has_initial_state, void *stream);
+
 /* Gated RMSNorm of mixer outputs ([record], the mixer's "norm" tensor):
  * out = norm_w * g / sqrt(mean_group(g^2) + eps), g = y * SiLU(z) (g = y when z
  * is NULL), over groups of group_size consecutive channels (0 = H*P/G).

@@ -86,6 +86,9 @@ _SIGS = {
     "mamba2_prefill_fwd": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                           _I32, _P, _P, _P, _I32, _P, _I32, ctypes.c_int64, _P, _P, _P,
                                           ctypes.c_size_t, _P]),
+    "mamba2_prefill_fwd_noalloc": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                  ctypes.c_float, _I32, _P, _P, _P, _I32, _P, _I32, ctypes.c_int64,
+                                                  _P, _P, _P]),
     "mamba2_gated_rmsnorm": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _P, _P, ctypes.c_float, ctypes.c_int32, _P,
                                             ctypes.c_int64, _P]),
     "mamba1_ssm_slot_bytes": (ctypes.c_size_t, [ctypes.POINTER(CDims1)]),
@@ -385,6 +388,39 @@ def mamba2_prefill_fwd(d: Dims, xbc, dt_raw, z, conv_w, conv_b, A_log, dt_bias, 
                                     int(norm_group), _ptr(y), _ptr(ssm_pool), _ptr(conv_pool), ns, _ptr(cu_seqlens),
                                     nseq, T, _ptr(state_indices), _ptr(has_initial_state), _ptr(workspace), ws_bytes,
                                     _stream(stream)), "mamba2_prefill_fwd")
+
+
+STATIC_SCRATCH_BYTES = 64 * 1024 * 1024  # MAMBA2_STATIC_SCRATCH_BYTES in include/mamba2.h
+
+
+def mamba2_prefill_fwd_noalloc(d: Dims, xbc, dt_raw, z, conv_w, conv_b, A_log, dt_bias, D, y, ssm_pool, conv_pool,
+                               cu_seqlens, state_indices, has_initial_state=None, norm_w=None, norm_eps: float = 1e-5,
+                               norm_group: int = 0, *, xbc_dtype=None, stream=None):
+    """mamba2_prefill_fwd without a workspace argument: the library's fixed per-GPU scratch array
+    serves as the workspace (nothing is allocated; calls that overlap on one GPU race)."""
+    T = xbc.shape[0]
+    nseq = state_indices.shape[0]
+    H = d.nheads
+    _want(xbc, "xbc", _TORCH_DT[d.act_dtype], (T, d.conv_dim))
+    _want(dt_raw, "dt_raw", _TORCH_DT[d.act_dtype], (T, H))
+    _want(z, "z", _TORCH_DT[d.act_dtype], (T, d.d_inner), optional=True)
+    _want(conv_w, "conv_w", torch.float32, (d.conv_dim, d.conv_width))
+    _want(conv_b, "conv_b", torch.float32, (d.conv_dim,), optional=True)
+    for n, t in (("A_log", A_log), ("dt_bias", dt_bias), ("D", D)):
+        _want(t, n, torch.float32, (H,))
+    _want(norm_w, "norm_w", torch.float32, (d.d_inner,), optional=True)
+    _want(y, "y", _TORCH_DT[d.out_dtype], (T, d.d_inner))
+    ns = _both_slots(d, ssm_pool, conv_pool)
+    _want(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,))
+    _want(state_indices, "state_indices", torch.int32, (nseq,))
+    _want(has_initial_state, "has_initial_state", torch.uint8, (nseq,), optional=True)
+    _debug_check(ns, state_indices)
+    c = cdims(d, xbc_dtype)
+    _check(lib().mamba2_prefill_fwd_noalloc(ctypes.byref(c), _ptr(xbc), _ptr(dt_raw), _ptr(z), _ptr(conv_w),
+                                            _ptr(conv_b), _ptr(A_log), _ptr(dt_bias), _ptr(D), _ptr(norm_w),
+                                            float(norm_eps), int(norm_group), _ptr(y), _ptr(ssm_pool),
+                                            _ptr(conv_pool), ns, _ptr(cu_seqlens), nseq, T, _ptr(state_indices),
+                                            _ptr(has_initial_state), _stream(stream)), "mamba2_prefill_fwd_noalloc")
 
 
 def mamba2_gated_rmsnorm(d: Dims, y, z, norm_w, out, eps: float = 1e-5, group_size: int = 0, *, stream=None):

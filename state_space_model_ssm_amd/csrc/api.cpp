@@ -442,6 +442,31 @@ int mamba2_prefill_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw
     return ok();
 }
 
+int mamba2_prefill_fwd_noalloc(const mamba2_dims *d, const void *xbc, const void *dt_raw, const void *z,
+                               const float *conv_w, const float *conv_b, const float *A_log, const float *dt_bias,
+                               const float *D, const float *norm_w, float norm_eps, int32_t norm_group, void *y,
+                               void *ssm_pool, void *conv_pool, int32_t num_slots, const int32_t *cu_seqlens,
+                               int32_t nseq, int64_t total_tokens, const int32_t *state_indices,
+                               const uint8_t *has_initial_state, void *stream) {
+    size_t need = 0;
+    int st = mamba2_prefill_workspace_bytes(d, total_tokens, &need);
+    if (st) return st;
+    if (need > MAMBA2_STATIC_SCRATCH_BYTES)
+        return fail(MAMBA2_ERR_WORKSPACE,
+                    "prefill of %lld tokens needs %zu workspace bytes, more than the %u-byte static scratch; "
+                    "split it into smaller chunks or use mamba2_prefill_fwd with a workspace",
+                    (long long)total_tokens, need, (unsigned)MAMBA2_STATIC_SCRATCH_BYTES);
+    void *scratch = nullptr;
+    size_t bytes = 0;
+    if (nseq > 0 && total_tokens > 0) {
+        st = hip_status(m2::static_scratch(&scratch, &bytes), "static scratch lookup");
+        if (st) return st;
+    }
+    return mamba2_prefill_fwd(d, xbc, dt_raw, z, conv_w, conv_b, A_log, dt_bias, D, norm_w, norm_eps, norm_group, y,
+                              ssm_pool, conv_pool, num_slots, cu_seqlens, nseq, total_tokens, state_indices,
+                              has_initial_state, scratch, bytes, stream);
+}
+
 // ------------------------------------------------------------ Mamba-1 selective scan
 namespace {
 

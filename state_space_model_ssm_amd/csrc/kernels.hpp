@@ -179,6 +179,10 @@ hipError_t launch_read_slot_errors(unsigned *dst, int reset, hipStream_t st);
 // (>= 0) equal to an earlier one; one workgroup, result written without a prior clear.
 hipError_t launch_check_slots(const int32_t *idx, int n, int num_slots, unsigned *result, hipStream_t st);
 
+// Device address (current device) and size of the library's fixed scratch array, looked up
+// once per device; the workspace of mamba2_prefill_fwd_noalloc.
+hipError_t static_scratch(void **ptr, size_t *bytes);
+
 // Each returns hipSuccess or the launch error. `supported` queries return
 // false for shapes outside the compiled set (no launch happens).
 bool state_update_supported(const LayerShape &s);

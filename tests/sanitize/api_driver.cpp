@@ -85,6 +85,11 @@ int main() {
                               1000, ix, nullptr, arena + 3072, need - 1, nullptr) == MAMBA2_ERR_WORKSPACE);
     EXPECT(mamba2_prefill_fwd(&d32, g, g2, nullptr, f, nullptr, f, f, f, f, 1e-5f, 100, g3, g, g2, 8, ix, 4, 1000,
                               ix, nullptr, arena + 3072, need, nullptr) == MAMBA2_ERR_UNSUPPORTED);
+    EXPECT(mamba2_prefill_fwd_noalloc(&d32, g, g2, nullptr, f, nullptr, f, f, f, nullptr, 1e-5f, 0, g3, g, g2, 8,
+                                      ix, 4, 1000, ix, nullptr, nullptr) == MAMBA2_OK);
+    EXPECT(mamba2_prefill_fwd_noalloc(&d32, g, g2, nullptr, f, nullptr, f, f, f, nullptr, 1e-5f, 0, g3, g, g2, 8,
+                                      ix, 4, 1 << 20, ix, nullptr, nullptr) == MAMBA2_ERR_WORKSPACE);
+    EXPECT(std::strstr(mamba2_last_error(), "static scratch") != nullptr);
     EXPECT(mamba2_mixed_fwd(&d32, g, g2, nullptr, f, nullptr, f, f, f, g3, g3, g, g2, 8, ix, 4, 1000, ix, nullptr,
                             ix, 16, arena + 3072, need, nullptr) == MAMBA2_OK);
     EXPECT(mamba2_gated_rmsnorm(&d, g, g2, f, 1e-5f, 0, g3, 7, nullptr) == MAMBA2_OK);

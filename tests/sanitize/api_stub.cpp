@@ -6,6 +6,7 @@
 
 #include <cstdint>
 
+#include "../../include/mamba2.h"
 #include "../../state_space_model_ssm_amd/csrc/kernels.hpp"
 
 int g_launches = 0;
@@ -27,6 +28,12 @@ hipError_t slot_error_word(unsigned **out) {
     return hipSuccess;
 }
 hipError_t launch_read_slot_errors(unsigned *, int, hipStream_t) { return reached(); }
+hipError_t static_scratch(void **ptr, size_t *bytes) {
+    alignas(256) static unsigned char fake[256];  // never dereferenced by the stubs
+    *ptr = fake;
+    *bytes = MAMBA2_STATIC_SCRATCH_BYTES;
+    return hipSuccess;
+}
 hipError_t launch_check_slots(const int32_t *, int, int, unsigned *, hipStream_t) { return reached(); }
 
 bool state_update_supported(const LayerShape &s) { return s.N == 16 || s.N == 64 || s.N == 128; }
