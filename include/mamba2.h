@@ -286,6 +286,41 @@ int mamba2_prefill_fwd_noalloc(const mamba2_dims *dims, const void *xbc, const v
 int mamba2_gated_rmsnorm(const mamba2_dims *dims, const void *y, const void *z, const float *norm_w,
                          float eps, int32_t group_size, void *out, int64_t rows, void *stream);
 
+/* Captured decode step ([TRT-LLM], "Questions" item 1: run the decode rows of a
+ * mixed iteration as a replay of the captured decode graph and only the context
+ * chunk eagerly; "Corrected measurements": graphed decode replays against the
+ * eager mixed pass). The decode of `nlayers` layer entries -- each
+ * mamba2_conv1d_update then mamba2_state_update of `batch` rows with that
+ * entry's buffers -- is recorded once into a HIP graph and replayed by
+ * mamba2_decode_graph_launch with one launch. An entry is a layer at one step:
+ * several steps of a stack are simply more entries. The graph keeps the
+ * pointers: the caller refills the same buffers (inputs, slot indices) before a
+ * replay and keeps them alive until mamba2_decode_graph_destroy.
+ *   create: records on capture_stream (a created stream, not NULL); on error
+ *           nothing is kept and *out is NULL. It instantiates the graph, which
+ *           may allocate: call it at set-up, not per step.
+ *   launch: enqueues one replay on `stream` (any stream); no allocation.
+ * Messages of the graph calls: mamba2_decode_graph_last_error(). */
+typedef struct {
+    const void *xbc;                 /* [batch][Cdim] act_dtype, raw */
+    const float *conv_w, *conv_b;    /* [Cdim][W]; [Cdim] or NULL */
+    void *xbc_post;                  /* [batch][Cdim] xbc_dtype */
+    void *conv_pool;                 /* [num_slots][W-1][Cdim] */
+    const void *dt_raw;              /* [batch][H] */
+    const float *A_log, *dt_bias, *D;
+    const void *z;                   /* [batch][H*P] or NULL */
+    void *y;                         /* [batch][H*P] out_dtype */
+    void *ssm_pool;                  /* [num_slots][H][P][N] */
+    int32_t num_slots;
+    const int32_t *state_indices;    /* [batch] */
+} mamba2_decode_layer;
+typedef struct mamba2_decode_graph mamba2_decode_graph;
+int mamba2_decode_graph_create(const mamba2_dims *dims, const mamba2_decode_layer *layers, int32_t nlayers,
+                               int32_t batch, void *capture_stream, mamba2_decode_graph **out);
+int mamba2_decode_graph_launch(mamba2_decode_graph *graph, void *stream);
+void mamba2_decode_graph_destroy(mamba2_decode_graph *graph);
+const char *mamba2_decode_graph_last_error(void);
+
 /* Fixed-size recurrent-state slot allocator ([record], "REQUIRED KERNEL
  * CLASS": a fixed-size recurrent state allocator; "Recurrent state": the
  * cost scales with concurrency, not context). Host-only: it hands out slot

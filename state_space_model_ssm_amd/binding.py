@@ -97,6 +97,10 @@ _SIGS = {
     "mamba1_selective_state_update": (ctypes.c_int, [ctypes.POINTER(CDims1), _P, _P, _P, _P, _P, _P, _P, _P,
                                                       _I32, _P, _P, _I32, _P, _I32, _P]),
     "mamba2_read_slot_errors": (ctypes.c_int, [_P, _I32, _P]),
+    "mamba2_decode_graph_create": (ctypes.c_int, [ctypes.POINTER(CDims), _P, _I32, _I32, _P, ctypes.POINTER(_P)]),
+    "mamba2_decode_graph_launch": (ctypes.c_int, [_P, _P]),
+    "mamba2_decode_graph_destroy": (None, [_P]),
+    "mamba2_decode_graph_last_error": (ctypes.c_char_p, []),
     "mamba2_check_slot_indices": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "mamba2_slots_create": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(_P)]),
     "mamba2_slot_alloc": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32)]),
@@ -525,6 +529,75 @@ def mamba2_mixed_fwd(d: Dims, xbc, dt_raw, z, conv_w, conv_b, A_log, dt_bias, D,
                                   _ptr(conv_pool), ns, _ptr(cu_seqlens), nseq, T, _ptr(prefill_indices),
                                   _ptr(has_initial_state), _ptr(decode_indices), Bd, _ptr(workspace), ws_bytes,
                                   _stream(stream)), "mamba2_mixed_fwd")
+
+
+# ------------------------------------------------------------------ captured decode step
+
+class CDecodeLayer(ctypes.Structure):
+    _fields_ = [("xbc", _P), ("conv_w", _P), ("conv_b", _P), ("xbc_post", _P), ("conv_pool", _P), ("dt_raw", _P),
+                ("A_log", _P), ("dt_bias", _P), ("D", _P), ("z", _P), ("y", _P), ("ssm_pool", _P),
+                ("num_slots", _I32), ("state_indices", _P)]
+
+
+class DecodeGraph:
+    """mamba2_decode_graph_*: the one-token decode (conv1d_update + state_update) of a list of
+    layer entries, captured once as a HIP graph and replayed with one launch.
+
+    Each entry is a dict with the tensors of one layer at one step: xbc [batch, Cdim] raw,
+    conv_w, conv_b (or None), xbc_post [batch, Cdim], conv_pool, dt_raw [batch, H], A_log,
+    dt_bias, D, z (or None), y [batch, H*P], ssm_pool, state_indices [batch]. The graph keeps
+    their addresses (and this object keeps the tensors alive): refill them in place between
+    launches."""
+
+    def __init__(self, d: Dims, layers, *, xbc_dtype=None):
+        H = d.nheads
+        self._keep = [dict(L) for L in layers]
+        if not self._keep:
+            raise ValueError("no layers")
+        batch = int(self._keep[0]["state_indices"].shape[0])
+        arr = (CDecodeLayer * len(self._keep))()
+        for i, L in enumerate(self._keep):
+            _want(L["xbc"], "xbc", _TORCH_DT[d.act_dtype], (batch, d.conv_dim))
+            _want(L["conv_w"], "conv_w", torch.float32, (d.conv_dim, d.conv_width))
+            _want(L.get("conv_b"), "conv_b", torch.float32, (d.conv_dim,), optional=True)
+            _want(L["xbc_post"], "xbc_post", _xdt(d, xbc_dtype), (batch, d.conv_dim))
+            _want(L["dt_raw"], "dt_raw", _TORCH_DT[d.act_dtype], (batch, H))
+            for n in ("A_log", "dt_bias", "D"):
+                _want(L[n], n, torch.float32, (H,))
+            _want(L.get("z"), "z", _TORCH_DT[d.act_dtype], (batch, d.d_inner), optional=True)
+            _want(L["y"], "y", _TORCH_DT[d.out_dtype], (batch, d.d_inner))
+            ns = _both_slots(d, L["ssm_pool"], L["conv_pool"])
+            _want(L["state_indices"], "state_indices", torch.int32, (batch,))
+            arr[i] = CDecodeLayer(*(_ptr(L.get(k)) for k in ("xbc", "conv_w", "conv_b", "xbc_post", "conv_pool",
+                                                              "dt_raw", "A_log", "dt_bias", "D", "z", "y",
+                                                              "ssm_pool")),
+                                  ns, _ptr(L["state_indices"]))
+        self._h = ctypes.c_void_p()
+        cap = torch.cuda.Stream()
+        st = lib().mamba2_decode_graph_create(ctypes.byref(cdims(d, xbc_dtype)), ctypes.cast(arr, _P),
+                                              len(self._keep), batch, ctypes.c_void_p(cap.cuda_stream),
+                                              ctypes.byref(self._h))
+        if st != OK:
+            raise Mamba2Error(st, "mamba2_decode_graph_create",
+                              (lib().mamba2_decode_graph_last_error() or lib().mamba2_last_error()).decode())
+        self.batch = batch
+        self.layers = len(self._keep)
+
+    def launch(self, *, stream=None) -> None:
+        st = lib().mamba2_decode_graph_launch(self._h, _stream(stream))
+        if st != OK:
+            raise Mamba2Error(st, "mamba2_decode_graph_launch", lib().mamba2_decode_graph_last_error().decode())
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().mamba2_decode_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # ------------------------------------------------------------------ slot index safety

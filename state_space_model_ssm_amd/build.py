@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmamba2.so")
 SOURCES = ["api.cpp", "decode.hip", "conv.hip", "scan.hip", "fused.hip", "norm.hip", "selective.hip",
-           "static_scratch.hip"]
+           "static_scratch.hip", "graph.cpp"]
 ARCH = "gfx950"
 
 

@@ -6,6 +6,7 @@ benchmark times:
   state and conv cache, through mamba2_prefill_fwd and both forms of chunk_scan_fwd;
 * the mixed batch (8 varlen prefill sequences + 384 decode rows on a 1024-slot fp32 pool, one
   mamba2_mixed_fwd with a workspace): every token, row and slot, untouched slots bit-identical;
+  and the same iteration split into an eager prefill and a replayed decode graph;
 * the 48-layer decode stack replayed from one captured HIP graph: every row at concurrency 16,
   8 sampled rows at concurrency 64, per layer and step.
 
@@ -151,10 +152,15 @@ def check_mixed(w, T, y, ssm, conv, what):
         f"{what}: a slot no row uses was written"
 
 
-def test_mixed_8b_every_row():
-    """One mamba2_mixed_fwd with a prefill workspace on the benchmark's mixed batch: every
-    prefill token and head, every decode row, every used slot against the oracle; the 632 slots
-    no row uses stay bit-identical."""
+def test_mixed_8b_every_row_eager_and_split():
+    """The benchmark's mixed batch two ways, each from the same initial pools:
+
+    * eager: one mamba2_mixed_fwd with a prefill workspace; every prefill token and head, every
+      decode row, every used slot against the oracle, the 632 slots no row uses bit-identical;
+    * split: the prefill segment through mamba2_prefill_fwd (eager) and the 384 decode rows as a
+      replay of a captured decode graph (mamba2_decode_graph_*), run twice from fresh pools. It
+      runs the same kernels on the same data, so it must equal the eager call bit for bit, and
+      with it the oracle within the tolerances above."""
     print("[full size] mixed batch: 8 varlen sequences + 384 decode rows, 1024-slot fp32 pool", flush=True)
     w, T, dv = mixed_8b_inputs()
     d = D2
@@ -167,6 +173,27 @@ def test_mixed_8b_every_row():
                        ssm, conv, dv["cu"], dv["pidx"], dv["hi"], dv["didx"], ws)
     torch.cuda.synchronize()
     check_mixed(w, T, y, ssm, conv, "mixed")
+
+    ssm2, conv2 = dv["ssm0"].clone(), dv["conv0"].clone()
+    post2 = torch.empty_like(post)
+    y2 = torch.full_like(y, 5.0)
+    graph = B.DecodeGraph(d, [{"xbc": dv["xbc"][T:], "conv_w": dv["conv_w"], "conv_b": None, "xbc_post": post2[T:],
+                               "conv_pool": conv2, "dt_raw": dv["dt"][T:], "A_log": dv["A_log"],
+                               "dt_bias": dv["dt_bias"], "D": dv["D"], "z": None, "y": y2[T:], "ssm_pool": ssm2,
+                               "state_indices": dv["didx"]}])
+    for rep in range(2):
+        ssm2.copy_(dv["ssm0"])
+        conv2.copy_(dv["conv0"])
+        y2.fill_(5.0)
+        B.mamba2_prefill_fwd(d, dv["xbc"][:T], dv["dt"][:T], None, dv["conv_w"], None, dv["A_log"], dv["dt_bias"],
+                             dv["D"], y2[:T], ssm2, conv2, dv["cu"], dv["pidx"], dv["hi"], ws)
+        graph.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(y2, y), f"split iteration {rep}: y differs from the eager mixed call"
+        assert torch.equal(ssm2, ssm), f"split iteration {rep}: SSM pool differs"
+        assert torch.equal(conv2, conv), f"split iteration {rep}: conv pool differs"
+        assert torch.equal(post2[T:], post[T:]), f"split iteration {rep}: decode post-conv rows differ"
+    graph.close()
 
 
 # ------------------------------------------------------------------ 48-layer decode stack

@@ -143,3 +143,86 @@ def test_graph_replay_mixed_batch_and_multi_token():
         reset()
         run()  # eager work on the same buffers between replays
         torch.cuda.synchronize()
+
+
+def test_native_decode_graph_replays_match_eager():
+    """mamba2_decode_graph_*: 3 layers x 2 steps captured once (each step an entry of its own,
+    with its own input rows), replayed 4 times with the inputs refilled in place and eager work
+    on the same pools between replays; every replay equals the eager calls bit for bit."""
+    d = NEMOTRON_H_8B
+    c, nl, steps = 5, 3, 2
+    rng = np.random.default_rng(8)
+    layers = []
+    for l in range(nl):
+        w = synth.stack_layer(d, seed=4, layer=l, concurrency=c, steps=steps)
+        layers.append({"xbc": dev(w["xbc"], "bf16"), "dt": dev(w["dt_raw"], "bf16"),
+                       **{k: dev(w["params"][k], "f32") for k in ("conv_w", "A_log", "dt_bias", "D")}})
+    init = [(dev(rng.standard_normal((c + 2, d.nheads, d.headdim, d.dstate)) * 0.3, "bf16"),
+             dev(rng.standard_normal((c + 2, d.conv_width - 1, d.conv_dim)), "bf16")) for _ in range(nl)]
+    pools = [(s_.clone(), v.clone()) for s_, v in init]
+    idx = torch.tensor([4, 0, 6, 2, 1], dtype=torch.int32, device="cuda")
+    # static input buffers the graph reads (refilled before each replay) and per-entry outputs
+    xin = torch.empty(steps, nl, c, d.conv_dim, dtype=torch.bfloat16, device="cuda")
+    dtin = torch.empty(steps, nl, c, d.nheads, dtype=torch.bfloat16, device="cuda")
+    post = torch.empty(c, d.conv_dim, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(steps, nl, c, d.d_inner, dtype=torch.bfloat16, device="cuda")
+
+    def fill():
+        for s_ in range(steps):
+            for l, L in enumerate(layers):
+                xin[s_, l].copy_(L["xbc"][s_:s_ + c])
+                dtin[s_, l].copy_(L["dt"][s_:s_ + c])
+
+    def eager():
+        for s_ in range(steps):
+            for l, (L, (ssm, conv)) in enumerate(zip(layers, pools)):
+                B.mamba2_conv1d_update(d, xin[s_, l], L["conv_w"], None, post, conv, idx)
+                B.mamba2_state_update(d, post, dtin[s_, l], L["A_log"], L["dt_bias"], L["D"], None, y[s_, l], ssm,
+                                      idx)
+
+    def reset():
+        for (s_, v), (s0, v0) in zip(pools, init):
+            s_.copy_(s0)
+            v.copy_(v0)
+
+    fill()
+    eager()
+    torch.cuda.synchronize()
+    ref_y = y.clone()
+    ref_pools = [(s_.clone(), v.clone()) for s_, v in pools]
+    entries = [{"xbc": xin[s_, l], "conv_w": L["conv_w"], "conv_b": None, "xbc_post": post,
+                "conv_pool": pools[l][1], "dt_raw": dtin[s_, l], "A_log": L["A_log"], "dt_bias": L["dt_bias"],
+                "D": L["D"], "z": None, "y": y[s_, l], "ssm_pool": pools[l][0], "state_indices": idx}
+               for s_ in range(steps) for l, L in enumerate(layers)]
+    graph = B.DecodeGraph(d, entries)
+    assert graph.layers == steps * nl and graph.batch == c
+    for rep in range(4):
+        reset()
+        xin.zero_()
+        fill()  # the inputs are refilled in place: the graph reads the same buffers
+        y.zero_()
+        graph.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref_y), f"replay {rep}: y differs"
+        for (s_, v), (rs, rv) in zip(pools, ref_pools):
+            assert torch.equal(s_, rs) and torch.equal(v, rv), f"replay {rep}: pools differ"
+        eager()  # eager work on the same pools between replays
+        torch.cuda.synchronize()
+    graph.close()
+
+
+def test_native_decode_graph_rejects_bad_setup():
+    d = NEMOTRON_H_8B
+    with pytest.raises(ValueError, match="no layers"):
+        B.DecodeGraph(d, [])
+    ssm = torch.zeros(2, d.nheads, d.headdim, d.dstate, dtype=torch.bfloat16, device="cuda")
+    conv = torch.zeros(3, d.conv_width - 1, d.conv_dim, dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros(1, d.conv_dim, dtype=torch.bfloat16, device="cuda")
+    f = lambda *s: torch.zeros(*s, device="cuda")
+    entry = {"xbc": x, "conv_w": f(d.conv_dim, d.conv_width), "conv_b": None, "xbc_post": x.clone(),
+             "conv_pool": conv, "dt_raw": torch.zeros(1, d.nheads, dtype=torch.bfloat16, device="cuda"),
+             "A_log": f(d.nheads), "dt_bias": f(d.nheads), "D": f(d.nheads), "z": None,
+             "y": torch.zeros(1, d.d_inner, dtype=torch.bfloat16, device="cuda"), "ssm_pool": ssm,
+             "state_indices": torch.zeros(1, dtype=torch.int32, device="cuda")}
+    with pytest.raises(ValueError, match="same number of slots"):
+        B.DecodeGraph(d, [entry])
