@@ -25,7 +25,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # published fp32 vector peak (half of it without packed fp32 instructions)
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # published fp32 vector peak, which counts packed (two-per-lane) fp32 instructions
+# Without packed fp32 instructions (this build disables them) one FMA per lane and cycle:
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz = 78.6 TFLOP/s.
+FP32_VECTOR_UNPACKED_TFLOPS = 78.6
+# A transcendental (v_exp_f32) issues at a quarter of the FMA rate (measured 0.28x on this chip), so it
+# occupies the issue slots of 4 FMAs: 8 flop-equivalents against the peak above.
+EXP_FLOP_EQUIV = 8
 
 
 def log(msg):
@@ -43,9 +49,11 @@ def decode_bytes_per_row(d, state_bytes):
     return su, cu, minimum
 
 
-def scan_algorithmic(d, tokens, nseq, xbc_bytes, y_bytes, state_bytes):
-    """Bytes and flops the chunk scan must move/compute (causal SSD, per token)."""
-    H, P, N, G, Q = d.nheads, d.headdim, d.dstate, d.ngroups, d.chunk_size
+def scan_algorithmic(d, tokens, nseq, xbc_bytes, y_bytes, state_bytes, chunk=None):
+    """Bytes and flops the chunk scan must move/compute (causal SSD, per token) with chunks of
+    `chunk` tokens (the layer's chunk_size by default; the fused and block forms run 32)."""
+    H, P, N, G = d.nheads, d.headdim, d.dstate, d.ngroups
+    Q = d.chunk_size if chunk is None else chunk
     cdim = H * P + 2 * G * N
     nbytes = tokens * (cdim * xbc_bytes + H * 2 + H * P * y_bytes) + nseq * H * P * N * state_bytes
     # C.B^T (per group, causal) + intra-chunk output (causal) + chunk state + inter-chunk output
@@ -53,10 +61,10 @@ def scan_algorithmic(d, tokens, nseq, xbc_bytes, y_bytes, state_bytes):
     return nbytes, flops_per_tok * tokens
 
 
-def profiled_traffic(kernel):
-    """HBM bytes per launch of `kernel` as measured by the rocprofv3 FETCH_SIZE/WRITE_SIZE runs
-    recorded under profiles/ (calibrated against a plain copy). None when no record exists or
-    when the kernel's sources changed since the counters were taken."""
+def profiled_record(kernel):
+    """The `traffic-json` record of `kernel` under profiles/ (written by profile_report.py from
+    rocprofv3 runs: calibrated FETCH_SIZE + WRITE_SIZE bytes per launch, and the kernel-trace
+    average duration), or None when there is none or the kernel's sources changed since."""
     import glob
     import hashlib
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
@@ -72,8 +80,23 @@ def profiled_traffic(kernel):
                 if not os.path.exists(path_f):
                     return None
                 h.update(open(path_f, "rb").read())
-            return rec["bytes_per_launch"] if h.hexdigest()[:16] == rec["src_sha"] else None
+            return rec if h.hexdigest()[:16] == rec["src_sha"] else None
     return None
+
+
+def profiled_traffic(kernel):
+    rec = profiled_record(kernel)
+    return None if rec is None else rec["bytes_per_launch"]
+
+
+def rocprof_check(kernel, nbytes):
+    """Cross-check of a roofline from the profiled record: the kernel-trace average duration
+    and the fraction of HBM peak it gives for the same algorithmic bytes."""
+    rec = profiled_record(kernel)
+    if rec is None or not rec.get("avg_us"):
+        return None
+    gbs = nbytes / (rec["avg_us"] * 1e-6) / 1e9
+    return {"rocprof_avg_us": rec["avg_us"], "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def time_region(fn, iters, torch):
@@ -150,17 +173,15 @@ def bench_stack(args, torch, np, B, synth, d, dev, bf, time_region):
         run(1)
         torch.cuda.synchronize()
         ms_eager = time_region(run, 1, torch)
-        graph = torch.cuda.CUDAGraph()
-        stream = torch.cuda.Stream()
-        stream.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(stream):
-            graph.capture_begin()
-            run()
-            graph.capture_end()
-        torch.cuda.current_stream().wait_stream(stream)
-        graph.replay()
+        # the same 32 steps x 48 layers as one captured decode graph (mamba2_decode_graph_*)
+        graph = B.DecodeGraph(d, [{"xbc": L["xbc"][s_:s_ + c], "conv_w": L["conv_w"], "conv_b": None,
+                                   "xbc_post": post, "conv_pool": conv, "dt_raw": L["dt"][s_:s_ + c],
+                                   "A_log": L["A_log"], "dt_bias": L["dt_bias"], "D": L["D"], "z": None, "y": y,
+                                   "ssm_pool": ssm, "state_indices": idx}
+                                  for s_ in range(steps) for L, (ssm, conv) in zip(layers, pools)])
+        graph.launch()
         torch.cuda.synchronize()
-        ms_graph = time_region(graph.replay, 1, torch)
+        ms_graph = time_region(graph.launch, 1, torch)
         tok = c * steps
         bytes_ = row_b * c * NL * steps
         pt = {"concurrency": c,
@@ -168,13 +189,157 @@ def bench_stack(args, torch, np, B, synth, d, dev, bf, time_region):
                         "hbm_frac": round(bytes_ / (ms_eager * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
               "graph": {"tok_s": round(tok / (ms_graph * 1e-3), 1), "ms_per_step": round(ms_graph / steps, 4),
                         "hbm_frac": round(bytes_ / (ms_graph * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
-        if c <= 16:
-            pt["note"] = "per-layer working set fits the 256 MB memory-side cache: launch-bound, not HBM-bound"
+        state_mib = c * NL * 2 * d.nheads * d.headdim * d.dstate / 2 ** 20
+        if state_mib <= 256:
+            pt["note"] = (f"the stack's state ({state_mib:.0f} MiB) fits the 256 MB memory-side cache, so "
+                          "hbm_frac can exceed what HBM alone allows; launch-bound")
+        elif c <= 64:
+            pt["note"] = (f"state of {state_mib:.0f} MiB streamed from HBM every step; each layer's grid "
+                          f"({c} rows x 128 heads) is short, so launch gaps and the tail of each kernel "
+                          "dominate")
+        graph.close()
         out["points"].append(pt)
         log(f"stack c={c}: eager {ms_eager / steps * 1e3:.0f} us/step, graph {ms_graph / steps * 1e3:.0f} us/step")
-        del graph, pools, post, y
+        del pools, post, y
         torch.cuda.empty_cache()
     return out
+
+
+def t1_ab(args, result, torch, B, d, rows, xbc, conv_w, post, conv, idx, dt, A_log, dtb, D, y, ssm, decode_step):
+    """The vllm.cpp page's A/B at T = 1: the decode workload's rows, slots and pools through the
+    chunk-scan arm, each row a one-token sequence of conv1d_fwd + chunk_scan_fwd
+    (has_initial_state = 1, final states written back in place), without and with the scan's
+    optional workspace, against conv1d_update + state_update."""
+    cu1 = torch.arange(rows + 1, dtype=torch.int32, device="cuda")
+    hi1 = torch.ones(rows, dtype=torch.uint8, device="cuda")
+    ws1 = torch.empty(max(16, B.mamba2_chunk_scan_workspace_bytes(d, rows, rows)), dtype=torch.uint8, device="cuda")
+
+    def chunk_arm(ws=None):
+        B.mamba2_conv1d_fwd(d, xbc, conv_w, None, post, conv, cu1, idx, hi1)
+        B.mamba2_chunk_scan_fwd(d, post, dt, A_log, dtb, D, None, y, ssm, cu1, idx, hi1, ws)
+
+    for _ in range(3):
+        chunk_arm()
+        chunk_arm(ws1)
+    ms_chunk = time_region(chunk_arm, args.steps, torch)
+    ms_chunk_ws = time_region(lambda: chunk_arm(ws1), args.steps, torch)
+    ms_upd = time_region(decode_step, args.steps, torch)
+    post_b = rows * d.conv_dim * 2
+    moved = lambda a, b: round(abs(a - b) / b * 100.0, 1)
+    result["t1_ab"] = {
+        "workload": f"{rows} decode rows of one token on the decode workload's slots and pools: the chunk-scan "
+                    "arm (conv1d_fwd + chunk_scan_fwd, each row a one-token sequence, chunk 128) against "
+                    "conv1d_update + state_update",
+        "update_arm": {"us_per_token": round(ms_upd * 1e3 / rows, 4), "us_per_step": round(ms_upd * 1e3, 2),
+                       "kernel_launches": 2, "allocations": 0, "memsets": 0,
+                       "scratch_bytes": post_b, "scratch": "post-conv xBC rows (caller buffer)"},
+        "chunk_arm": {"us_per_token": round(ms_chunk * 1e3 / rows, 4), "us_per_step": round(ms_chunk * 1e3, 2),
+                      "kernel_launches": 3, "allocations": 0, "memsets": 0, "scratch_bytes": post_b,
+                      "scratch": "post-conv xBC rows (caller buffer)"},
+        "chunk_arm_with_workspace": {"us_per_token": round(ms_chunk_ws * 1e3 / rows, 4),
+                                     "us_per_step": round(ms_chunk_ws * 1e3, 2), "kernel_launches": 4,
+                                     "allocations": 0, "memsets": 0, "scratch_bytes": post_b + ws1.numel(),
+                                     "scratch": "post-conv xBC rows + the B/C operand planes (caller buffers)"},
+        "per_token_time_moved_pct": moved(ms_chunk, ms_upd),
+        "refuted_if_below_pct": 3.0,
+        "verdict": "confirmed: the update arm is faster" if moved(ms_chunk, ms_upd) >= 3.0 and ms_upd < ms_chunk
+                   else "refuted (under 3 %)"}
+    log(f"T=1 A/B: update arm {ms_upd * 1e3:.1f} us, chunk arm {ms_chunk * 1e3:.1f} us "
+        f"(with workspace {ms_chunk_ws * 1e3:.1f} us)")
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def single_thread_oracle(seconds):
+    """The decode sample of the CPU baseline on one thread: a child process with OMP_NUM_THREADS=1
+    (the oracle's OpenMP runtime in this process has already fixed its thread count)."""
+    import subprocess
+    code = ("import os, sys, time, numpy as np; sys.path.insert(0, %r); import oracle; "
+            "from state_space_model_ssm_amd import synth; from state_space_model_ssm_amd.configs import NEMOTRON_H_8B as d; "
+            "w = synth.decode_batch(d, seed=1, rows=16, num_slots=32, with_z=False); "
+            "kw = dict(H=d.nheads, P=d.headdim, N=d.dstate, G=d.ngroups); "
+            "cp = w['conv_pool'][w['slots']].astype(np.float64); sp = w['ssm_pool'][w['slots']].astype(np.float64); "
+            "t0 = time.perf_counter(); n = 0\n"
+            "while time.perf_counter() - t0 < %f:\n"
+            "    i = n %% 16; oracle.decode(w['xbc'][i:i+1], w['dt_raw'][i:i+1], w['params'], [0], cp[i:i+1], "
+            "sp[i:i+1], **kw); n += 1\n"
+            "print(n, time.perf_counter() - t0)") % (ROOT, seconds)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=600)
+    if r.returncode != 0:
+        return {"error": r.stderr[-400:]}
+    n, el = r.stdout.split()
+    n, el = int(n), float(el)
+    return {"value": round(n / el, 2), "unit": "tok/s", "cores": 1,
+            "sample": f"{n} decode row-steps (16 rows of the decode workload, all 128 heads) in {el:.1f} s"}
+
+
+def cpu_mixed_sample(oracle, synth, seconds):
+    """The oracle on a bounded sample of the mixed batch (fp32 state): its first prefill sequence's
+    tokens in 64-token pieces, then decode rows, until `seconds` pass; rate in tokens/s."""
+    import numpy as np
+    from state_space_model_ssm_amd.configs import F32, NEMOTRON_H_8B
+    d = NEMOTRON_H_8B.with_(state_dtype=F32)
+    kw = dict(H=d.nheads, P=d.headdim, N=d.dstate, G=d.ngroups)
+    w = synth.mixed_batch(d, seed=3, num_prefill=8, len_lo=256, len_hi=4096, decode_rows=16, num_slots=32)
+    L0 = int(w["cu_seqlens"][1])
+    cs = np.zeros((d.conv_width - 1, d.conv_dim))
+    hs = np.zeros((d.nheads, d.headdim, d.dstate))
+    t0 = time.perf_counter()
+    n = 0
+    while n < L0 and time.perf_counter() - t0 < seconds / 2:
+        _, _, cs, hs = oracle.layer_seq(w["prefill"]["xbc"][n:n + 64], w["prefill"]["dt_raw"][n:n + 64], w["params"],
+                                        cs, hs, **kw)
+        n += min(64, L0 - n)
+    t_pre = time.perf_counter() - t0
+    sl = w["decode_slots"]
+    cp = w["conv_pool"][sl].astype(np.float64)
+    sp = w["ssm_pool"][sl].astype(np.float64)
+    t1 = time.perf_counter()
+    r = 0
+    while time.perf_counter() - t1 < seconds / 2:
+        i = r % len(sl)
+        oracle.decode(w["decode"]["xbc"][i:i + 1], w["decode"]["dt_raw"][i:i + 1], w["params"], [0], cp[i:i + 1],
+                      sp[i:i + 1], **kw)
+        r += 1
+    t_dec = time.perf_counter() - t1
+    T3 = int(w["cu_seqlens"][-1])
+    est = T3 / (n / t_pre) + 384 / (r / t_dec)  # seconds the oracle would need for the whole mixed step
+    return {"value": round((T3 + 384) / est, 2), "unit": "tok/s", "kind": "oracle",
+            "sample": f"{n} prefill tokens of the first sequence in {t_pre:.1f} s and {r} decode row-steps in "
+                      f"{t_dec:.1f} s (fp32 state), scaled to the whole step ({T3} prefill tokens + 384 rows)"}
+
+
+def cpu_stack_sample(oracle, synth, seconds):
+    """The oracle on sampled rows of the 48-layer decode stack: one row of each of the first 8 layers
+    (their own seeded parameters, inputs and initial slot), one decode step per call, cycled until
+    `seconds` pass; the rate is scaled to tokens/s of the whole 48-layer stack."""
+    import numpy as np
+    from state_space_model_ssm_amd.configs import NEMOTRON_H_8B as d, NEMOTRON_H_8B_MAMBA_LAYERS as NL
+    kw = dict(H=d.nheads, P=d.headdim, N=d.dstate, G=d.ngroups)
+    layers = []
+    for l in range(8):
+        w = synth.stack_layer(d, seed=4, layer=l, concurrency=1, steps=1)
+        s_, c_ = synth.stack_slot(d, seed=4, layer=l, slot=0)
+        layers.append((w, c_[None].astype(np.float64), s_[None].astype(np.float64)))
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        w, cp, sp = layers[n % len(layers)]
+        oracle.decode(w["xbc"][:1], w["dt_raw"][:1], w["params"], [0], cp, sp, **kw)
+        n += 1
+    el = time.perf_counter() - t0
+    return {"value": round(n / el / NL, 3), "unit": "tok/s", "kind": "oracle",
+            "sample": f"{n} row-layer decode steps (one row of each of 8 stack layers, cycled) in {el:.1f} s; "
+                      f"tokens/s of the stack = row-layer steps/s / {NL} layers"}
 
 
 def main():
@@ -188,6 +353,7 @@ def main():
     ap.add_argument("--no-fewer-seqs", action="store_true",
                     help="skip the 1- and 2-sequence prefill timings (keeps per-kernel profiles to one workload)")
     ap.add_argument("--no-multi", action="store_true", help="skip the multi-token decode section")
+    ap.add_argument("--no-t1ab", action="store_true", help="skip the chunk-scan vs state-update A/B at T = 1")
     ap.add_argument("--no-mamba1", action="store_true", help="skip the Mamba-1 selective scan section")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -279,12 +445,19 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "state_update_kernel", "achieved": round(su_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(su_gbs / HBM_PEAK_GBS, 4),
                      "traffic": profiled_traffic("state_update_kernel"), "algorithmic_bytes_per_launch": su_b * rows,
-                     "avg_launch_us": round(ms_su * 1e3, 2)},
+                     "avg_launch_us": round(ms_su * 1e3, 2),
+                     "rocprof_check": rocprof_check("state_update_kernel", su_b * rows)},
         "decode_detail": {"us_per_step": round(ms_step * 1e3, 2), "state_update_us": round(ms_su * 1e3, 2),
                           "conv_update_us": round(ms_conv * 1e3, 2),
                           "step_algorithmic_bytes": min_b * rows,
                           "step_hbm_frac": round(min_b * rows / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
+    # ------------------------------------------------------------ the vllm.cpp page's A/B at T = 1
+    # The same 256 rows, slots and pools through the chunk-scan arm: each row a one-token
+    # sequence of conv1d_fwd + chunk_scan_fwd (has_initial_state = 1, final states written
+    # back in place), without and with the scan's optional workspace.
+    if not args.no_t1ab:
+        t1_ab(args, result, torch, B, d, rows, xbc, conv_w, post, conv, idx, dt, A_log, dtb, D, y, ssm, decode_step)
     del ssm, conv, xbc, dt, post, y
     torch.cuda.empty_cache()
 
@@ -412,15 +585,17 @@ def main():
             ms_b = time_region(few_step, args.prefill_steps, torch)
             few[f"{nb}x8192"] = {"ms_per_step": round(ms_b, 4), "tok_s": round(Tb / (ms_b * 1e-3), 1)}
             log(f"prefill {nb} x 8192: {ms_b * 1e3:.1f} us/step ({Tb / (ms_b * 1e-3) / 1e6:.2f} M tok/s)")
-        # algorithmic minimum of the whole prefill: raw bf16 xBC + dt in, bf16 y out, final fp32 states
-        pb, pf = scan_algorithmic(d2, T, 4, 2, 2, 4)
+        # algorithmic minimum of the whole prefill: raw bf16 xBC + dt in, bf16 y out, final fp32 states;
+        # flops of the chunk length each form runs (32-token blocks fused and with a workspace, 128 without)
+        pb, pf = scan_algorithmic(d2, T, 4, 2, 2, 4, chunk=32)
         pre_gbs = pb / (ms_pre * 1e-3) / 1e9
         pre_tfs = pf / (ms_pre * 1e-3) / 1e12
-        sb, sf = scan_algorithmic(d2, T, 4, 4, 2, 4)
+        sb, sf = scan_algorithmic(d2, T, 4, 4, 2, 4, chunk=32)
         scan_gbs = sb / (ms_scan * 1e-3) / 1e9
         scan_tfs = sf / (ms_scan * 1e-3) / 1e12
+        _, sf128 = scan_algorithmic(d2, T, 4, 4, 2, 4, chunk=128)
         chunks_gbs = sb / (ms_chunks * 1e-3) / 1e9
-        chunks_tfs = sf / (ms_chunks * 1e-3) / 1e12
+        chunks_tfs = sf128 / (ms_chunks * 1e-3) / 1e12
         pre_tok_s = T / (ms_pre * 1e-3)
         log(f"prefill (fused): {ms_pre * 1e3:.1f} us/step ({pre_tok_s / 1e6:.2f} M tok/s, {pre_gbs:.0f} GB/s, "
             f"{pre_tfs:.1f} TFLOP/s); unfused {ms_unf * 1e3:.1f} us = conv1d_fwd {ms_cf * 1e3:.1f} + chunk_scan "
@@ -428,15 +603,17 @@ def main():
         result["prefill"] = {
             "value": round(pre_tok_s, 1), "unit": "tok/s", "ms_per_step": round(ms_pre, 4),
             "steps": args.prefill_steps,
-            "workload": "Nemotron-H-8B layer prefill: 4 x 8192 tokens (cu_seqlens), chunk 128, bf16 inputs, "
-                        "fp32 state, bf16 y, zero initial state, final conv/SSM states to pool slots; "
-                        "step = mamba2_prefill_fwd (per-group B/C prep kernel + fused conv/scan kernel over "
-                        "32-token blocks + conv cache update); the unfused detail runs conv1d_fwd and "
-                        "chunk_scan_fwd, with a workspace (32-token blocks) and without (chunks of 128)",
+            "workload": "Nemotron-H-8B layer prefill: 4 x 8192 tokens (cu_seqlens), bf16 inputs, fp32 state, "
+                        "bf16 y, zero initial state, final conv/SSM states to pool slots; layer chunk_size 128; "
+                        "step = mamba2_prefill_fwd, whose fused path cuts chunks at 32-token blocks (per-group "
+                        "B/C prep kernel + fused conv/scan kernel + conv cache update; flops counted at 32); "
+                        "the unfused detail runs conv1d_fwd and chunk_scan_fwd, with a workspace (32-token "
+                        "blocks) and without (chunks of 128, flops counted at 128)",
             "roofline": {"bound": "hbm", "kernel": "mamba2_prefill_fwd (whole call)", "achieved": round(pre_gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(pre_gbs / HBM_PEAK_GBS, 4),
                          "traffic": profiled_traffic("mamba2_prefill_fwd"),
                          "algorithmic_bytes_per_launch": pb, "algorithmic_flops_per_launch": pf,
+                         "flops_chunk_length": 32,
                          "mfma_achieved_tflops": round(pre_tfs, 2),
                          "mfma_frac": round(pre_tfs / MFMA_BF16_PEAK_TFLOPS, 4)},
             "fewer_sequences": few,
@@ -457,7 +634,7 @@ def main():
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(chunks_tfs / MFMA_BF16_PEAK_TFLOPS, 4),
                     "traffic": profiled_traffic("chunk_scan_fast_kernel"),
-                    "algorithmic_flops_per_launch": sf, "algorithmic_bytes_per_launch": sb,
+                    "algorithmic_flops_per_launch": sf128, "algorithmic_bytes_per_launch": sb,
                     "hbm_achieved_gbs": round(chunks_gbs, 1), "hbm_frac": round(chunks_gbs / HBM_PEAK_GBS, 4)},
             },
         }
@@ -487,9 +664,11 @@ def main():
             sel_step()
         ms_sel = time_region(sel_step, max(3, args.prefill_steps), torch)
         elems = T1 * d1.dim * d1.dstate
-        sel_flops = 6 * elems  # per state element: delta*A, a*h + (delta*u)*B, C.h accumulate (exp not counted)
+        sel_flops = 6 * elems  # per state element: delta*A, a*h + (delta*u)*B, C.h accumulate
+        sel_equiv = sel_flops + EXP_FLOP_EQUIV * elems  # plus the exp2 per state element, in FMA issue slots
         sel_bytes = T1 * (3 * d1.dim * 2 + 2 * d1.ngroups * d1.dstate * 2) + 4 * d1.dim * d1.dstate * 4
         sel_tfs = sel_flops / (ms_sel * 1e-3) / 1e12
+        sel_eq_tfs = sel_equiv / (ms_sel * 1e-3) / 1e12
         log(f"mamba-1 selective scan: {ms_sel * 1e3:.1f} us ({T1 / (ms_sel * 1e-3) / 1e6:.2f} M tok/s, "
             f"{sel_tfs:.1f} TFLOP/s, {elems / (ms_sel * 1e-3) / 1e12:.2f} T state updates/s)")
         result["mamba1_scan"] = {
@@ -497,9 +676,13 @@ def main():
                         "group, bf16 u/delta/B/C and y, fp32 state, softplus(delta + bias), D skip, zero initial "
                         "state, final states to pool slots",
             "value": round(T1 / (ms_sel * 1e-3), 1), "unit": "tok/s", "ms_per_step": round(ms_sel, 4),
-            "roofline": {"bound": "alu", "kernel": "selective_scan_kernel", "achieved": round(sel_tfs, 2),
-                         "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(sel_tfs / FP32_VECTOR_PEAK_TFLOPS, 4),
+            "roofline": {"bound": "alu", "kernel": "selective_scan_kernel", "achieved": round(sel_eq_tfs, 2),
+                         "peak": FP32_VECTOR_UNPACKED_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(sel_eq_tfs / FP32_VECTOR_UNPACKED_TFLOPS, 4),
+                         "counting": "6 flops per state update plus its exp2 as 8 flop-equivalents (the issue "
+                                     "slots of 4 FMAs), against the fp32 vector peak without packed instructions",
+                         "flops_only_tflops": round(sel_tfs, 2),
+                         "flops_only_frac_of_published_packed_peak": round(sel_tfs / FP32_VECTOR_PEAK_TFLOPS, 4),
                          "traffic": profiled_traffic("selective_scan_kernel"),
                          "algorithmic_flops_per_launch": sel_flops, "exp_per_launch": elems,
                          "algorithmic_bytes_per_launch": sel_bytes,
@@ -560,9 +743,29 @@ def main():
             B.mamba2_mixed_fwd(d3, xbc3, dt3, None, cw3, None, A3, dtb3, D3, post3, y3, ssm3, conv3, cu3, pidx3, hi3,
                                didx3, ws3)
 
+        # the split iteration: the prefill segment eagerly, the 384 decode rows as one replay of a
+        # captured decode graph over the same buffers
+        graph3 = B.DecodeGraph(d3, [{"xbc": xbc3[T3:], "conv_w": cw3, "conv_b": None, "xbc_post": post3[T3:],
+                                     "conv_pool": conv3, "dt_raw": dt3[T3:], "A_log": A3, "dt_bias": dtb3, "D": D3,
+                                     "z": None, "y": y3[T3:], "ssm_pool": ssm3, "state_indices": didx3}])
+
+        def split_step():
+            B.mamba2_prefill_fwd(d3, xbc3[:T3], dt3[:T3], None, cw3, None, A3, dtb3, D3, y3[:T3], ssm3, conv3, cu3,
+                                 pidx3, hi3, ws3)
+            graph3.launch()
+
+        def prefill_part():
+            B.mamba2_prefill_fwd(d3, xbc3[:T3], dt3[:T3], None, cw3, None, A3, dtb3, D3, y3[:T3], ssm3, conv3, cu3,
+                                 pidx3, hi3, ws3)
+
         for _ in range(args.prefill_warmup):  # untimed, as for the prefill
             mixed_step()
+            split_step()
         ms_mix = time_region(mixed_step, max(3, args.prefill_steps), torch)
+        ms_split = time_region(split_step, max(3, args.prefill_steps), torch)
+        ms_mix_pre = time_region(prefill_part, max(3, args.prefill_steps), torch)
+        ms_mix_dec = time_region(graph3.launch, max(3, args.prefill_steps), torch)
+        graph3.close()
         dec_b = 384 * decode_bytes_per_row(d3, 4)[2]
         pre_b, _ = scan_algorithmic(d3, T3, 8, 2, 2, 4)
         result["mixed"] = {
@@ -572,8 +775,15 @@ def main():
             "value": round(rows3 / (ms_mix * 1e-3), 1), "unit": "tok/s", "ms_per_step": round(ms_mix, 4),
             "prefill_tokens": T3, "decode_rows": 384,
             "algorithmic_bytes": int(dec_b + pre_b),
-            "hbm_frac": round((dec_b + pre_b) / (ms_mix * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        log(f"mixed: {ms_mix * 1e3:.1f} us/step ({rows3} rows)")
+            "hbm_frac": round((dec_b + pre_b) / (ms_mix * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "split": {"step": "mamba2_prefill_fwd on the prefill segment (eager) + one replay of the decode rows' "
+                              "captured graph (mamba2_decode_graph_launch)",
+                      "ms_per_step": round(ms_split, 4), "tok_s": round(rows3 / (ms_split * 1e-3), 1),
+                      "hbm_frac": round((dec_b + pre_b) / (ms_split * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "prefill_part_ms": round(ms_mix_pre, 4), "decode_graph_ms": round(ms_mix_dec, 4),
+                      "decode_graph_hbm_frac": round(dec_b / (ms_mix_dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+        log(f"mixed: {ms_mix * 1e3:.1f} us/step eager, {ms_split * 1e3:.1f} us split ({rows3} rows; prefill "
+            f"{ms_mix_pre * 1e3:.1f} + decode graph {ms_mix_dec * 1e3:.1f})")
         del xbc3, dt3, ssm3, conv3, post3, y3, ws3
         torch.cuda.empty_cache()
 
@@ -583,10 +793,10 @@ def main():
 
     # ------------------------------------------------------------ CPU baseline (oracle)
     if not args.no_cpu_baseline:
-        import oracle
-        kw = dict(H=d.nheads, P=d.headdim, N=d.dstate, G=d.ngroups)
         cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
         os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+        import oracle
+        kw = dict(H=d.nheads, P=d.headdim, N=d.dstate, G=d.ngroups)
         ssm_h = host_slots[0].astype(np.float64)
         conv_h = host_slots[1].astype(np.float64)
         nrow = ssm_h.shape[0]
@@ -600,8 +810,12 @@ def main():
         el = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": round(done / el, 2), "unit": "tok/s", "cores": cores, "kind": "oracle",
                                   "sample": f"{done} decode row-steps (cycling over {nrow} of the 256 rows, all 128 "
-                                            f"heads each) through the fp64 C oracle in {el:.1f} s"}
+                                            f"heads each) through the fp64 C oracle in {el:.1f} s",
+                                  "cpu_model": cpu_model(), "host_threads_visible": len(os.sched_getaffinity(0))}
         log(f"cpu baseline: {done} rows in {el:.1f} s on {cores} threads")
+        result["cpu_baseline"]["single_thread"] = single_thread_oracle(args.cpu_seconds / 3)
+        result["cpu_baseline"]["mixed"] = cpu_mixed_sample(oracle, synth, args.cpu_seconds / 2)
+        result["cpu_baseline"]["stack"] = cpu_stack_sample(oracle, synth, args.cpu_seconds / 2)
         if not args.no_prefill:
             t0 = time.perf_counter()
             n = 0
