@@ -82,7 +82,7 @@ int check_scan(const mamba2_dims *d) {
     if (st) return st;
     if (!m2::scan_supported(shape_of(d)))
         return fail(MAMBA2_ERR_UNSUPPORTED,
-                    "chunk scan supports (headdim, dstate, chunk) in {(16,16,16|32), (64,128,64|128)}; got (%d,%d,%d)",
+                    "chunk scan supports (headdim, dstate, chunk) in {(16,16,16|32|64), (64,128,64|128)}; got (%d,%d,%d)",
                     d->headdim, d->dstate, d->chunk_size);
     return MAMBA2_OK;
 }

@@ -323,6 +323,7 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
         dr = (float)static_cast<const AT *>(a.dt_raw)[((int64_t)row * T + min(t0 + u, T - 1)) * H + head];
     };
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int t_stage = 0;  // first token of the block being staged
     auto stage_block = [&]() {
         if (tid < NT4) {
             const int u = tid / (N / 2), rem = tid % (N / 2), which = rem / (N / 4), n4 = rem % (N / 4);
@@ -331,9 +332,12 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
         if (wave == 0) {  // the scalars of the block's tokens once per workgroup, not once per wave
             const float dt_l = softplus_f(dr + dtb);
             const float dec_l = expf(dt_l * A);
+            // tokens past T (a last block shorter than TB) take dt = 0 and decay = 1: the state
+            // update then gives the state back unchanged, and their y is not stored
+            const bool live = t_stage + (tid & 63) < T;
             if ((tid & 63) < TB) {
-                sDt[0][tid & 63] = dt_l;
-                sDt[1][tid & 63] = dec_l;
+                sDt[0][tid & 63] = live ? dt_l : 0.0f;
+                sDt[1][tid & 63] = live ? dec_l : 1.0f;
             }
         }
     };
@@ -348,14 +352,15 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
             __syncthreads();  // previous block's B/C fully read
             load_block(t0);
         }
+        t_stage = t0;
         stage_block();
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
             const int t = t0 + u;
-            // (skipped, not left with a break: a break makes the compiler keep a second copy
-            // of the state registers for the loop's exit)
-            if (t >= T) continue;
+            // every token of the block runs (no branch around it, which would make the compiler
+            // keep copies of the state registers): past T the decay is 1 and the input 0
+            const bool live = t < T;
             float Bv[kVec], Cv[kVec];
 #pragma unroll
             for (int j = 0; j < kVec; j += 4) {
@@ -366,8 +371,10 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
             }
             const float dt = sDt[0][u];
             const float decay = sDt[1][u];
-            const int d = a.dst ? pool_slot(a.dst[(int64_t)row * T + t], a.num_slots, a.err, blockIdx.x == 0 && tid == 0)
-                                : -1;
+            // (the final-state form, CONSEC, is the one launched without a destination table)
+            const int d = (!CONSEC && live && a.dst)
+                              ? pool_slot(a.dst[(int64_t)row * T + t], a.num_slots, a.err, blockIdx.x == 0 && tid == 0)
+                              : -1;
             float yv[ITERS];
 #pragma unroll
             for (int it = 0; it < ITERS; ++it) {
@@ -384,13 +391,14 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
                 yv[it] = fmaf(Dh, x, acc);
                 if constexpr (HasZ) yv[it] *= silu_f(zval(u, it));
                 if constexpr (!CONSEC)  // (stored at once: holding them costs registers here)
-                    if (ylane && prow(it) < P)
+                    if (live && ylane && prow(it) < P)
                         st(a.y, out_dt, ((int64_t)row * T + t) * HP + (int64_t)head * P + prow(it), yv[it]);
             }
-            if constexpr (CONSEC) store_y(t, yv);
+            if constexpr (CONSEC)
+                if (live) store_y(t, yv);
         }
     }
-    if (!a.dst)
+    if (CONSEC || !a.dst)
 #pragma unroll
         for (int it = 0; it < ITERS; ++it)
             if (prow(it) < P) nt_store16<ST>(pool + (int64_t)src * H * P * N + tile0 + (int64_t)prow(it) * N, h[it]);

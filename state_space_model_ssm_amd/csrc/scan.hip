@@ -791,7 +791,7 @@ static hipError_t launch_scan_s(const LayerShape &s, const ScanArgs &a, hipStrea
 }
 
 bool scan_supported(const LayerShape &s) {
-    if (s.P == 16 && s.N == 16) return s.Q == 16 || s.Q == 32;
+    if (s.P == 16 && s.N == 16) return s.Q == 16 || s.Q == 32 || s.Q == 64;
     if (s.P == 64 && s.N == 128) return s.Q == 64 || s.Q == 128;
     return false;
 }
@@ -801,6 +801,7 @@ hipError_t launch_chunk_scan(const LayerShape &s, const ScanArgs &a, hipStream_t
     if (s.P == 16 && s.N == 16) {
         if (s.Q == 16) return launch_scan_s<16, 16, 16>(s, a, stream);
         if (s.Q == 32) return launch_scan_s<16, 16, 32>(s, a, stream);
+        if (s.Q == 64) return launch_scan_s<16, 16, 64>(s, a, stream);
     }
     if (s.P == 64 && s.N == 128) {
         if (s.Q == 64) return launch_scan_s<64, 128, 64>(s, a, stream);
