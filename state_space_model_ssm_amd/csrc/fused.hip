@@ -474,18 +474,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
         Hacc[nt] = f32x4{v[0], v[1], v[2], v[3]};
     }
 
-    // D x as an MFMA: column t of a 32-token block picks k-slot t with weight D (hi + lo)
-    bf16x8 Dsel[2][2];  // [hi, lo][t-tile parity]
+    // D x as an MFMA: column t of a 32-token block picks k-slot t with weight D (in bf16: x is
+    // a bf16 operand already, and y is stored in bf16, whose rounding is of the same size)
+    bf16x8 Dsel[2];  // [t-tile parity]
     {
-        const bf16 dh = f32_to_bf16(Dh), dl = f32_to_bf16(Dh - (float)dh), zero = f32_to_bf16(0.0f);
+        const bf16 dh = f32_to_bf16(Dh), zero = f32_to_bf16(0.0f);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const bool on = 8 * q + j == 16 * h + col;
-                Dsel[0][h][j] = on ? dh : zero;
-                Dsel[1][h][j] = on ? dl : zero;
-            }
+            for (int j = 0; j < 8; ++j) Dsel[h][j] = 8 * q + j == 16 * h + col ? dh : zero;
     }
 
     // ---- loads of a block into registers (raw bits, converted where used)
@@ -741,8 +738,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 #pragma unroll
             for (int m = 0; m < KL; ++m)
                 if (2 * m <= tt) acc[tt] = mma(XDc[m], sM[buf][(tt * KL + m) * 64 + lane], acc[tt]);
-            acc[tt] = mma(Xc[tt / 2], Dsel[0][tt & 1], acc[tt]);
-            acc[tt] = mma(Xc[tt / 2], Dsel[1][tt & 1], acc[tt]);
+            acc[tt] = mma(Xc[tt / 2], Dsel[tt & 1], acc[tt]);
         }
         // carried state: H^T <- exp(lam_end) H^T + sum_s B^T[n][s] (x w)[s][p]   (3-term split)
 #pragma unroll
