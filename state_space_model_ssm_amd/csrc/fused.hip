@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(XT) 
     constexpr bool CONV = W > 1;
     constexpr int P = 64, N = 128;
     constexpr int RL = L / 8;   // tokens per thread
-    constexpr int NS = N + 8;   // bf16 row stride of the token-major tiles
+    constexpr int NS = N + 16;  // bf16 row stride of the token-major tiles (288 bytes: conflict-free operand reads)
     constexpr int CBS = L + 4;  // float row stride of the C.B^T tile
     constexpr int TL = L / 16, KL = L / 32, KN = N / 32;
     __shared__ __attribute__((aligned(16))) bf16 sB[2][L * NS];
@@ -381,14 +381,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(XT) 
 // output, D x, the state update: MFMA work on LDS tiles staged one iteration
 // earlier) and stages block b + 1 (tiles into the other LDS buffer, token
 // arrays, conv + SiLU of x, decayed C.B^T: VALU work), in one instruction
-// stream so the two overlap; then it issues the loads of block b + 2 and meets
-// the other waves at the one barrier of the iteration.
+// stream so the two overlap. The loads of block b + 2 go out as the registers
+// they fill come free, and the waves meet at the one barrier of the iteration.
 template <int L, int W, typename ST, typename AT, typename XT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fused_scan_kernel(FusedArgs a, int H, int G) {
     constexpr int P = 64, N = 128, NT = 256;
     constexpr int TL = L / 16, KL = L / 32, KN = N / 32, NTL = N / 16;
-    constexpr int BTS = L + 8;                 // bf16 row stride of the B^T tiles [n][s]
-    constexpr int CS = N + 8;                  // bf16 row stride of the C tile [t][n]
+    // Row strides of the LDS tiles read as MFMA operands (16 bytes per lane, rows by lane & 15,
+    // pieces by lane >> 4): a stride of 32 mod 64 bytes keeps those reads free of bank
+    // conflicts on gfx950 (measured: 80 or 272 bytes cost two passes, 96 or 288 one). With
+    // fp32 x rows the wider B^T stride would leave room for one workgroup per CU, not two.
+    constexpr int BTS = sizeof(XT) == 2 ? L + 16 : L + 8;  // bf16 row stride of the B^T tiles [n][s]
+    constexpr int CS = N + 16;                               // bf16 row stride of the C tile [t][n]
     constexpr bool CONV = W > 1;               // W == 1: xbc is already conv + SiLU output (taken as is)
     constexpr int XR = 8 + W - 1;              // raw x rows behind one lane's 8 tokens
     constexpr int XRW = L + W - 1;             // raw x rows of a block
@@ -509,7 +513,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     const uint32_t clane = (uint32_t)(tid / (N / 8)) * crow + 16 * (tid % (N / 8));
     const uint32_t zrow = (uint32_t)HP * AS;                               // bytes per z row
     const uint32_t ylane = col * (uint32_t)HP * 2 + 8 * q;                 // y: row col of a t-tile, channels 4q..
-    auto prefetch = [&](int64_t b) {
+    // Loads of a block in two parts, each issued as soon as the registers it fills are free
+    // (the tiles' once they are staged into LDS, the token and C.B^T values' once the operands
+    // are formed), so each part has a whole iteration to arrive.
+    auto prefetch_tiles = [&](int64_t b) {
         const int64_t bL = b * L;
         const char *btb = static_cast<const char *>(a.bt) + (b * G + g) * (int64_t)(2 * N * L * 2);
 #pragma unroll
@@ -524,14 +531,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
         const int hi = (int)(end - 1 - bL < L + 8 ? end - 1 - bL : L + 8);  // last valid row
         // first x row that holds data: a later segment's context rows are tokens of its sequence
         const int xl = first ? lo : (int)(start - (W - 1) - bL > -W ? start - (W - 1) - bL : -W);
-        const char *dtc = static_cast<const char *>(a.dt_raw) + (bL * H + head) * AS;
-        dtr = ld_bits(reinterpret_cast<const AT *>(dtc + min(max(dtlane, (uint32_t)max(lo, 0) * H * AS), (uint32_t)hi * H * AS)));
         // raw x rows bL - (W-1) + rho, rho in [0, L + W - 1), of this wave's 16 channels
         const char *xc = static_cast<const char *>(a.xbc) + ((bL - (W - 1)) * cdim + (int64_t)head * P + 16 * wv) * XS;
         const uint32_t xlo = (uint32_t)(xl + (W - 1) > 0 ? xl + (W - 1) : 0) * xrow, xhi = (uint32_t)(hi + (W - 1)) * xrow;
 #pragma unroll
         for (int k = 0; k < XP; ++k)
             xq[k] = *reinterpret_cast<const u32x4 *>(xc + (min(max(xq_off[k], xlo), xhi) + xq_part[k]));
+    };
+    auto prefetch_ops = [&](int64_t b) {
+        const int64_t bL = b * L;
+        const int lo = (int)(start - bL > -W ? start - bL : -W);           // first valid row, block-relative
+        const int hi = (int)(end - 1 - bL < L + 8 ? end - 1 - bL : L + 8);  // last valid row
+        const char *dtc = static_cast<const char *>(a.dt_raw) + (bL * H + head) * AS;
+        dtr = ld_bits(reinterpret_cast<const AT *>(dtc + min(max(dtlane, (uint32_t)max(lo, 0) * H * AS), (uint32_t)hi * H * AS)));
         const char *cbb = static_cast<const char *>(a.cb) + ((b * G + g) * (int64_t)(TL * KL) + ttw * KL) * 512 * 4;
 #pragma unroll
         for (int m = 0; m < KL; ++m)
@@ -669,10 +681,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 
     const int64_t b0 = start / L, b1 = end > start ? (end - 1) / L : b0 - 1;
     if (b0 <= b1) {
-        prefetch(b0);
+        prefetch_tiles(b0);
+        prefetch_ops(b0);
         stage_tiles(b0, 0);
         stage_ops(b0, 0);
-        prefetch(b0 < b1 ? b0 + 1 : b0);
+        prefetch_tiles(b0 < b1 ? b0 + 1 : b0);
+        prefetch_ops(b0 < b1 ? b0 + 1 : b0);
         __syncthreads();
     }
 
@@ -704,8 +718,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
                     zc + (min(max(col * zrow + (uint32_t)(16 * tt) * zrow, zlo), zhi) + 4 * q * AS)));
         }
 
-        // tiles of the next block into the other buffer
+        // tiles of the next block into the other buffer, then the tile loads of block b + 2
+        // (the last blocks reload themselves, keeping the loads unconditional)
+        const int64_t b2 = b + 2 <= b1 ? b + 2 : b1;
         stage_tiles(b < b1 ? b + 1 : b, buf ^ 1);
+        prefetch_tiles(b2);
 
         // carried-state output: y[t][p] = exp(lam_t) sum_n C_t[n] H[p][n]
         f32x4 acc[TL];
@@ -728,8 +745,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             }
         }
 
-        // operands of the next block (the last block restages itself into the unused buffer)
+        // operands of the next block (the last block restages itself into the unused buffer),
+        // then the token and C.B^T loads of block b + 2
         stage_ops(b < b1 ? b + 1 : b, buf ^ 1);
+        prefetch_ops(b2);
 
         // intra-block output and D x, then the epilogue
 #pragma unroll
@@ -774,8 +793,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             }
         }
 
-        // loads of block b + 2 (the last blocks reload themselves, keeping the loads unconditional)
-        prefetch(b + 2 <= b1 ? b + 2 : b1);
         __syncthreads();
     }
 
@@ -873,7 +890,7 @@ constexpr int kFixNB = 3;  // register buffers of the fix-up pass
 template <typename AT, bool HasZ>
 __global__ __launch_bounds__(256) void fused_seg_fix_kernel(FusedArgs a, int H, int G, int nseg, int smax) {
     constexpr int P = 64, N = 128, L = 32, TL = 2, KN = 4;
-    constexpr int CS = N + 8;  // LDS row stride (bf16): 16-byte reads of 8 rows hit distinct banks
+    constexpr int CS = N + 16;  // LDS row stride (bf16): 288 bytes, 32 mod 64, keeps the 16-byte operand reads conflict-free
     __shared__ __align__(16) bf16 sC[2][L * CS];
     constexpr float LOG2E = 1.4426950408889634f;
     const int tid = threadIdx.x, lane = tid & 63;
