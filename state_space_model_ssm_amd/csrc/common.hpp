@@ -188,6 +188,15 @@ template <int K> __device__ __forceinline__ float group_sum_last(float v) {
     return v;
 }
 
+// Inclusive prefix sum over the 64 lanes with DPP: shifts within rows of 16,
+// then row broadcasts of lane 15 and lane 31 (no LDS round trips).
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+    v = group_sum_last<16>(v);              // window sums inside each row of 16
+    v += dpp_add_src<0x142, 0xA>(v);        // row_bcast:15 into rows 1 and 3
+    v += dpp_add_src<0x143, 0xC>(v);        // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
 // Sequence of packed token t: the largest i with cu[i] <= t (sequences may be empty).
 __device__ __forceinline__ int find_seq(const int32_t *cu, int nseq, int64_t t) {
     int lo = 0, hi = nseq;  // answer in [0, nseq-1]

@@ -68,15 +68,6 @@ template <typename T> __device__ __forceinline__ float bits_f(uint32_t v) {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-// Inclusive prefix sum over the 64 lanes with DPP: shifts within rows of 16,
-// then row broadcasts of lane 15 and lane 31 (no LDS round trips).
-__device__ __forceinline__ float wave_prefix_sum(float v) {
-    v = group_sum_last<16>(v);              // window sums inside each row of 16
-    v += dpp_add_src<0x142, 0xA>(v);        // row_bcast:15 into rows 1 and 3
-    v += dpp_add_src<0x143, 0xC>(v);        // row_bcast:31 into rows 2 and 3
-    return v;
-}
-
 // segment flags (segment mode): the sequence's first segment; its only one
 constexpr int kSegFirst = 1, kSegOnly = 2;
 constexpr int kMinSeg = 1024;  // tokens per segment at least

@@ -535,32 +535,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             }
         }
     };
-    // wave 0: lam (log2 units), dt and state weights of a chunk into buffer `buf`
+    // wave 0: lam (log2 units), dt and state weights of a chunk into buffer `buf`. The other
+    // waves meet wave 0 at the barrier after this, so it stays short: hardware exp2 / log2
+    // softplus and DPP prefix sums (no LDS round trips).
+    const float A2 = A * LOG2E;
     auto token_arrays = [&](int buf, int cl) {
-        float carry = 0.0f, lamv[LB], dtv[LB];
+        float carry = 0.0f, l2v[LB], dtv[LB];
 #pragma unroll
         for (int b = 0; b < LB; ++b) {
             const int t = b * 64 + lane;
-            const float dtt = (t < cl) ? softplus_f(dtr[b] + dtb) : 0.0f;
-            float v = dtt * A;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(v, off, 64);
-                if (lane >= off) v += o;
-            }
-            v += carry;
-            lamv[b] = v;
+            const float dtt = (t < cl) ? softplus_fast(dtr[b] + dtb) : 0.0f;
+            const float v = wave_prefix_sum(dtt * A2) + carry;
+            l2v[b] = v;
             dtv[b] = dtt;
-            carry = __shfl(v, 63, 64);
+            carry = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
         }
-        const float lam_end = __shfl(lamv[(L - 1) / 64], (L - 1) % 64, 64);
+        const float l2end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l2v[(L - 1) / 64]), (L - 1) % 64));
 #pragma unroll
         for (int b = 0; b < LB; ++b) {
             const int t = b * 64 + lane;
             if (t < L) {
-                sL2[buf][t] = lamv[b] * LOG2E;
+                sL2[buf][t] = l2v[b];
                 sDt[buf][t] = dtv[b];
-                sW[buf][t] = dtv[b] * __builtin_amdgcn_exp2f((lam_end - lamv[b]) * LOG2E);
+                sW[buf][t] = dtv[b] * __builtin_amdgcn_exp2f(l2end - l2v[b]);
             }
         }
     };
