@@ -736,21 +736,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             }
         }
 
-        // operands of the next block (the last block restages itself into the unused buffer),
-        // then the token and C.B^T loads of block b + 2
-        stage_ops(b < b1 ? b + 1 : b, buf ^ 1);
-        prefetch_ops(b2);
-
-        // intra-block output and D x, then the epilogue
-#pragma unroll
-        for (int tt = 0; tt < TL; ++tt) {
-            acc[tt] *= elc[tt];
-#pragma unroll
-            for (int m = 0; m < KL; ++m)
-                if (2 * m <= tt) acc[tt] = mma(XDc[m], sM[buf][(tt * KL + m) * 64 + lane], acc[tt]);
-            acc[tt] = mma(Xc[tt / 2], Dsel[tt & 1], acc[tt]);
-        }
-        // carried state: H^T <- exp(lam_end) H^T + sum_s B^T[n][s] (x w)[s][p]   (3-term split)
+        // carried state: H^T <- exp(lam_end) H^T + sum_s B^T[n][s] (x w)[s][p]   (3-term split).
+        // Issued before the staging below, so the matrix cores work through these while the
+        // VALU stages the next block.
 #pragma unroll
         for (int nt = 0; nt < NTL; ++nt) Hacc[nt] *= decc;
 #pragma unroll
@@ -765,6 +753,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
                 Hacc[nt] = mma(bh, XSlc[m], Hacc[nt]);
             }
         }
+        // intra-block output and D x
+#pragma unroll
+        for (int tt = 0; tt < TL; ++tt) {
+            acc[tt] *= elc[tt];
+#pragma unroll
+            for (int m = 0; m < KL; ++m)
+                if (2 * m <= tt) acc[tt] = mma(XDc[m], sM[buf][(tt * KL + m) * 64 + lane], acc[tt]);
+            acc[tt] = mma(Xc[tt / 2], Dsel[tt & 1], acc[tt]);
+        }
+        // operands of the next block (VALU work beside the MFMAs above; the last block restages
+        // itself into the unused buffer), then the token and C.B^T loads of block b + 2
+        stage_ops(b < b1 ? b + 1 : b, buf ^ 1);
+        prefetch_ops(b2);
+
+        // epilogue
         {
             char *yc = reinterpret_cast<char *>(y + bL * HP + (int64_t)head * P + 16 * wv);
 #pragma unroll
