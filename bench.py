@@ -489,7 +489,9 @@ def main():
         for _ in range(2):
             multi_step(dstm)
             multi_step(None)
+        settle(lambda: multi_step(dstm), torch)  # untimed, as for decode: clocks to their sustained state
         ms_snap = time_region(lambda: multi_step(dstm), args.steps, torch)
+        settle(lambda: multi_step(None), torch)
         ms_fin = time_region(lambda: multi_step(None), args.steps, torch)
         H, P, N, G, W = d.nheads, d.headdim, d.dstate, d.ngroups, d.conv_width
         cdim = d.conv_dim
