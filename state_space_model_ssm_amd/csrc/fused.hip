@@ -35,14 +35,15 @@
 //        for the state), so post-conv x is never shared or stored; its raw
 //        rows reach the lanes through a small wave-private LDS tile;
 //      * D x is one more MFMA per t-tile, against a selector operand that
-//        holds D (hi and lo) on the diagonal;
+//        holds D (in bf16) on the diagonal;
 //      * the shared LDS tiles are B^T hi/lo, C and the decayed C.B^T operands
-//        (each wave forms half of one t-tile's), double-buffered: about 70 KB
+//        (each wave forms half of one t-tile's), double-buffered: about 80 KB
 //        per workgroup with the wave-private tiles, so two workgroups share a
 //        CU and overlap each other's phases;
 //      * block b computes from tiles staged one iteration earlier while block
-//        b + 1 is staged into the other buffer and block b + 2's tiles, dt
-//        and raw x are loaded into registers.
+//        b + 1 is staged into the other buffer; block b + 2's tiles, raw x,
+//        dt and C.B^T are loaded into registers as soon as the registers
+//        they fill are free.
 //
 // With conv width W = 1 both kernels take post-conv xBC as it is (no conv, no
 // SiLU, no context rows): that instantiation is mamba2_chunk_scan_fwd's form
