@@ -115,6 +115,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(XT) 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, q = lane >> 4;
     const int blk = blockIdx.x, g = blockIdx.y;
+    const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N, cdim = HP + 2 * GN;
+    const int cg = tid & 31, run = tid >> 5;
+    const bool isC = cg >= 16;
+    const int n0 = 8 * (cg & 15);
+    const int64_t c0 = HP + (isC ? GN : 0) + (int64_t)g * N + n0;  // first of this thread's 8 channels
+    const int64_t t0 = (int64_t)blk * L + run * RL;
+    const XT *in = static_cast<const XT *>(a.xbc) + c0;
+
+    float w[8 * W], bias[8];
+    if constexpr (CONV) {
+        load_k<float, 8 * W>(a.conv_w + c0 * W, w);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bias[j] = a.conv_b ? a.conv_b[c0 + j] : 0.0f;
+    }
+    // The run's raw rows (the conv window of its RL tokens) as raw bits at 32-bit offsets from
+    // the window's first row, clamped only to the packed rows [0, T): issued before the
+    // sequence lookup below, whose cu_seqlens load would otherwise come first. Rows outside
+    // the run's sequence are replaced by its context or never used.
+    constexpr int NR = RL + W - 1;
+    const int64_t r0 = t0 - (W - 1);
+    Raw<XT, 8> rw[CONV ? NR : 1];
+    if (CONV && t0 < a.T) {
+        const char *wbase = reinterpret_cast<const char *>(in + r0 * cdim);
+        const uint32_t rowb = (uint32_t)(cdim * (int64_t)sizeof(XT));
+#pragma unroll
+        for (int i = 0; i < (CONV ? NR : 1); ++i) {
+            int64_t r = r0 + i;
+            r = r < 0 ? 0 : (r > a.T - 1 ? a.T - 1 : r);
+            rw[i].load(reinterpret_cast<const XT *>(wbase + (uint32_t)(r - r0) * rowb));
+        }
+    }
+
     // one coalesced load of cu_seqlens per workgroup, then searches in LDS (global
     // binary search, one dependent load per step, past kCu sequences)
     if (smax && blockIdx.x == 0 && blockIdx.y == 0)  // segment mode: the plan (the scan runs after this kernel)
@@ -124,25 +156,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(XT) 
         for (int i = tid; i <= a.nseq; i += 256) sCu[i] = a.cu[i];
     __syncthreads();
     const int32_t *cus = cu_lds ? sCu : a.cu;
-    const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N, cdim = HP + 2 * GN;
-    const int cg = tid & 31, run = tid >> 5;
-    const bool isC = cg >= 16;
-    const int n0 = 8 * (cg & 15);
-    const int64_t c0 = HP + (isC ? GN : 0) + (int64_t)g * N + n0;  // first of this thread's 8 channels
-    const int64_t t0 = (int64_t)blk * L + run * RL;
-
-    float w[8 * W], bias[8];
-    if constexpr (CONV) {
-        load_k<float, 8 * W>(a.conv_w + c0 * W, w);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) bias[j] = a.conv_b ? a.conv_b[c0 + j] : 0.0f;
-    }
 
     // Token i of the thread's run leaves as soon as it is computed: B as hi / lo rows of
     // the token-major tiles (C.B^T below, and the transposed planes); C in natural order
     // in LDS and as a permuted token-major row of the workspace. Rows past T or of
     // padding sequences are zeros.
-    const XT *in = static_cast<const XT *>(a.xbc) + c0;
     const int tl0 = run * RL;  // first token of the thread inside the block
     bf16 *cp = static_cast<bf16 *>(a.cp) + (int64_t)g * N + (n0 & ~31);
     const int u0 = n0 & 31;
@@ -188,22 +206,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(XT) 
         const int64_t tl = (t0 + RL < a.T ? t0 + RL : a.T) - 1;  // last token of the run
         const int sa = find_seq(cus, a.nseq, t0), sb = find_seq(cus, a.nseq, tl);
         if (sa == sb) {
-            // one sequence holds the whole run: every row is loaded up front, clamped into it
-            constexpr int NR = RL + W - 1;
-            const int64_t ss = cus[sa], se = cus[sa + 1];
+            // one sequence holds the whole run: its rows were loaded up front (rw)
+            const int64_t ss = cus[sa];
             const int slot = pool_slot(a.idx[sa], a.num_slots, a.err, false);
-            // rows as raw bits (widened where used) at 32-bit offsets from the window's
-            // first row: fewer registers, so more workgroups share a CU
-            const int64_t r0 = t0 - (W - 1);
-            const char *wbase = reinterpret_cast<const char *>(in + r0 * cdim);
-            const uint32_t rowb = (uint32_t)(cdim * (int64_t)sizeof(XT));
-            Raw<XT, 8> rw[NR];
-#pragma unroll
-            for (int i = 0; i < NR; ++i) {
-                int64_t r = r0 + i;
-                r = r < ss ? ss : (r > se - 1 ? se - 1 : r);
-                rw[i].load(reinterpret_cast<const XT *>(wbase + (uint32_t)(r - r0) * rowb));
-            }
             // rows before the sequence (only among the first W - 1): its cached raw inputs or zeros
             const bool head = r0 < ss;
             float ctx[W - 1][8];
