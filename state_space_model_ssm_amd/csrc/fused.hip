@@ -41,9 +41,9 @@
 //        per workgroup with the wave-private tiles, so two workgroups share a
 //        CU and overlap each other's phases;
 //      * block b computes from tiles staged one iteration earlier while block
-//        b + 1 is staged into the other buffer; block b + 2's tiles, raw x,
-//        dt and C.B^T are loaded into registers as soon as the registers
-//        they fill are free.
+//        b + 1 is staged into the other buffer; block b + 3's tiles, raw x,
+//        dt and C.B^T are loaded into one of two register sets as soon as
+//        the registers they fill are free, two iterations ahead of use.
 //
 // With conv width W = 1 both kernels take post-conv xBC as it is (no conv, no
 // SiLU, no context rows): that instantiation is mamba2_chunk_scan_fwd's form
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(XT) 
 // output, D x, the state update: MFMA work on LDS tiles staged one iteration
 // earlier) and stages block b + 1 (tiles into the other LDS buffer, token
 // arrays, conv + SiLU of x, decayed C.B^T: VALU work), in one instruction
-// stream so the two overlap. The loads of block b + 2 go out as the registers
+// stream so the two overlap. The loads of block b + 3 go out as the registers
 // they fill come free, and the waves meet at the one barrier of the iteration.
 template <int L, int W, typename ST, typename AT, typename XT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fused_scan_kernel(FusedArgs a, int H, int G) {
@@ -489,9 +489,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     // ---- loads of a block into registers (raw bits, converted where used)
     const int ttw = MSPLIT ? (wv >> 1) : (wv < TL ? wv : TL - 1);
     const int mj0 = MSPLIT ? 4 * (wv & 1) : 0;
-    u32x4 btr[BTP], cr[CPC], xq[XP];
-    f32x4 cbr[KL][MJ / 4];
-    uint32_t dtr;
+    struct Pre {  // one block's loads in registers: B^T, C, raw x, C.B^T and dt
+        u32x4 btr[BTP], cr[CPC], xq[XP];
+        f32x4 cbr[KL][MJ / 4];
+        uint32_t dtr;
+    };
+    Pre P0, P1;  // two sets in turn, so each block's loads have two iterations to arrive
     // Loads take a wave-uniform base plus a 32-bit unsigned byte offset per lane
     // (the global_load scalar-base form). Rows are clamped in offset space
     // (offsets grow with the row), so a block at a sequence edge costs one
@@ -512,18 +515,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     const uint32_t ylane = col * (uint32_t)HP * 2 + 8 * q;                 // y: row col of a t-tile, channels 4q..
     // Loads of a block in two parts, each issued as soon as the registers it fills are free
     // (the tiles' once they are staged into LDS, the token and C.B^T values' once the operands
-    // are formed), so each part has a whole iteration to arrive.
-    auto prefetch_tiles = [&](int64_t b) {
+    // are formed), into the set that block b + 1 has just left: two iterations to arrive.
+    auto prefetch_tiles = [&](int64_t b, Pre &R) __attribute__((always_inline)) {
         const int64_t bL = b * L;
         const char *btb = static_cast<const char *>(a.bt) + (b * G + g) * (int64_t)(2 * N * L * 2);
 #pragma unroll
-        for (int i = 0; i < BTP; ++i) btr[i] = *reinterpret_cast<const u32x4 *>(btb + 16u * (tid + i * NT));
+        for (int i = 0; i < BTP; ++i) R.btr[i] = *reinterpret_cast<const u32x4 *>(btb + 16u * (tid + i * NT));
         const int tmax = (int)(a.T - 1 - bL < L - 1 ? a.T - 1 - bL : L - 1);  // C rows end at T
         const char *cpb = static_cast<const char *>(a.cp) + (bL * GN + (int64_t)g * N) * 2;
         const uint32_t cmax = (uint32_t)tmax * crow + 16 * (tid % (N / 8));
 #pragma unroll
         for (int i = 0; i < CPC; ++i)
-            cr[i] = *reinterpret_cast<const u32x4 *>(cpb + min(clane + (uint32_t)(i * (NT / (N / 8))) * crow, cmax));
+            R.cr[i] = *reinterpret_cast<const u32x4 *>(cpb + min(clane + (uint32_t)(i * (NT / (N / 8))) * crow, cmax));
         const int lo = (int)(start - bL > -W ? start - bL : -W);           // first valid row, block-relative
         const int hi = (int)(end - 1 - bL < L + 8 ? end - 1 - bL : L + 8);  // last valid row
         // first x row that holds data: a later segment's context rows are tokens of its sequence
@@ -533,20 +536,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
         const uint32_t xlo = (uint32_t)(xl + (W - 1) > 0 ? xl + (W - 1) : 0) * xrow, xhi = (uint32_t)(hi + (W - 1)) * xrow;
 #pragma unroll
         for (int k = 0; k < XP; ++k)
-            xq[k] = *reinterpret_cast<const u32x4 *>(xc + (min(max(xq_off[k], xlo), xhi) + xq_part[k]));
+            R.xq[k] = *reinterpret_cast<const u32x4 *>(xc + (min(max(xq_off[k], xlo), xhi) + xq_part[k]));
     };
-    auto prefetch_ops = [&](int64_t b) {
+    auto prefetch_ops = [&](int64_t b, Pre &R) __attribute__((always_inline)) {
         const int64_t bL = b * L;
         const int lo = (int)(start - bL > -W ? start - bL : -W);           // first valid row, block-relative
         const int hi = (int)(end - 1 - bL < L + 8 ? end - 1 - bL : L + 8);  // last valid row
         const char *dtc = static_cast<const char *>(a.dt_raw) + (bL * H + head) * AS;
-        dtr = ld_bits(reinterpret_cast<const AT *>(dtc + min(max(dtlane, (uint32_t)max(lo, 0) * H * AS), (uint32_t)hi * H * AS)));
+        R.dtr = ld_bits(reinterpret_cast<const AT *>(dtc + min(max(dtlane, (uint32_t)max(lo, 0) * H * AS), (uint32_t)hi * H * AS)));
         const char *cbb = static_cast<const char *>(a.cb) + ((b * G + g) * (int64_t)(TL * KL) + ttw * KL) * 512 * 4;
 #pragma unroll
         for (int m = 0; m < KL; ++m)
 #pragma unroll
             for (int h = 0; h < MJ / 4; ++h)
-                cbr[m][h] = *reinterpret_cast<const f32x4 *>(cbb + (lane * 32u + (uint32_t)(m * 2048 + 4 * mj0 + 16 * h)));
+                R.cbr[m][h] = *reinterpret_cast<const f32x4 *>(cbb + (lane * 32u + (uint32_t)(m * 2048 + 4 * mj0 + 16 * h)));
     };
 
     // ---- staging of a block (from the prefetch registers) for the next iteration
@@ -554,7 +557,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     float el[TL], dec = 1.0f, l2e = 0.0f;    // exp(lam_t) for t = 16 tt + col; exp(lam_end); lam_end (log2)
     float lsum = 0.0f;                       // log2 of the decay over the blocks computed so far
     // tiles of block b into LDS buffer buf: B^T and C (shared), raw x rows (this wave's)
-    auto stage_tiles = [&](int64_t b, int buf) {
+    auto stage_tiles = [&](int64_t b, int buf, Pre &R) __attribute__((always_inline)) {
         const int64_t bL = b * L;
         // shared tiles
         bf16 *sbt = sBT[buf];
@@ -562,12 +565,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 #pragma unroll
         for (int i = 0; i < BTP; ++i) {
             const int id = tid + i * NT, n = (id / (L / 8)) % N, hl = id / (N * L / 8);
-            *reinterpret_cast<u32x4 *>(&sbt[hl * N * BTS + n * BTS + 8 * (id % (L / 8))]) = btr[i];
+            *reinterpret_cast<u32x4 *>(&sbt[hl * N * BTS + n * BTS + 8 * (id % (L / 8))]) = R.btr[i];
         }
 #pragma unroll
         for (int i = 0; i < CPC; ++i) {
             const int id = tid + i * NT;
-            *reinterpret_cast<u32x4 *>(&sc[(id / (N / 8)) * CS + 8 * (id % (N / 8))]) = cr[i];
+            *reinterpret_cast<u32x4 *>(&sc[(id / (N / 8)) * CS + 8 * (id % (N / 8))]) = R.cr[i];
         }
         // raw x rows into this wave's tile (lanes past the last piece repeat it)
         char *xt = sXr[wv];
@@ -575,12 +578,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
         for (int k = 0; k < XP; ++k) {
             const int id = min(lane + 64 * k, CPR * XRW - 1);
             char *d = xt + (id / CPR) * XRB + 16 * (id % CPR);
-            *reinterpret_cast<uint2 *>(d) = uint2{xq[k][0], xq[k][1]};
-            *reinterpret_cast<uint2 *>(d + 8) = uint2{xq[k][2], xq[k][3]};
+            *reinterpret_cast<uint2 *>(d) = uint2{R.xq[k][0], R.xq[k][1]};
+            *reinterpret_cast<uint2 *>(d + 8) = uint2{R.xq[k][2], R.xq[k][3]};
         }
     };
     // operands of block b (token arrays, conv + SiLU of x, decayed C.B^T into sM[buf])
-    auto stage_ops = [&](int64_t b, int buf) {
+    auto stage_ops = [&](int64_t b, int buf, Pre &R) __attribute__((always_inline)) {
         const int64_t bL = b * L;
         const int lo = (int)(start - bL > 0 ? start - bL : 0);
         const int hi = (int)(end - bL < L ? end - bL : L);
@@ -589,7 +592,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
         // token arrays, every wave its own copy: dt, inclusive lam, dt exp(lam_end - lam)
         {
             // (softplus for every lane, then a multiply by 0 / 1: no branch around it)
-            const float dt = softplus_fast(bits_f<AT>(dtr) + dtb) * (lane < L && lane >= lo && lane < hi ? 1.0f : 0.0f);
+            const float dt = softplus_fast(bits_f<AT>(R.dtr) + dtb) * (lane < L && lane >= lo && lane < hi ? 1.0f : 0.0f);
             const float v = wave_prefix_sum(dt * A2);
             const float l2end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), L - 1));
             sTok[wv][0][lane] = dt;  // lanes >= L fill padding
@@ -667,7 +670,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
                     const f32x4 ls = *reinterpret_cast<const f32x4 *>(&sTok[wv][1][s0 + 4 * h]);
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        mv[4 * h + j] = s0 + 4 * h + j <= t ? cbr[m][h][j] * __builtin_amdgcn_exp2f(l2t - ls[j]) : 0.0f;
+                        mv[4 * h + j] = s0 + 4 * h + j <= t ? R.cbr[m][h][j] * __builtin_amdgcn_exp2f(l2t - ls[j]) : 0.0f;
                 }
                 bf16 *dst = reinterpret_cast<bf16 *>(&sM[buf][(ttw * KL + m) * 64 + lane]) + mj0;
                 if constexpr (MJ == 8) *reinterpret_cast<bf16x8 *>(dst) = cvt8(mv);
@@ -678,16 +681,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 
     const int64_t b0 = start / L, b1 = end > start ? (end - 1) / L : b0 - 1;
     if (b0 <= b1) {
-        prefetch_tiles(b0);
-        prefetch_ops(b0);
-        stage_tiles(b0, 0);
-        stage_ops(b0, 0);
-        prefetch_tiles(b0 < b1 ? b0 + 1 : b0);
-        prefetch_ops(b0 < b1 ? b0 + 1 : b0);
+        prefetch_tiles(b0, P0);
+        prefetch_ops(b0, P0);
+        stage_tiles(b0, 0, P0);
+        stage_ops(b0, 0, P0);
+        prefetch_tiles(b0 + 1 <= b1 ? b0 + 1 : b1, P1);
+        prefetch_ops(b0 + 1 <= b1 ? b0 + 1 : b1, P1);
+        prefetch_tiles(b0 + 2 <= b1 ? b0 + 2 : b1, P0);
+        prefetch_ops(b0 + 2 <= b1 ? b0 + 2 : b1, P0);
         __syncthreads();
     }
 
-    for (int64_t b = b0; b <= b1; ++b) {
+    // block b: computes b, stages b + 1 from R (the set that holds it) and loads b + 3 into R
+    auto block = [&](int64_t b, Pre &R) __attribute__((always_inline)) {
         const int buf = (int)((b - b0) & 1);
         const int64_t bL = b * L;
         const int lo = (int)(start - bL > 0 ? start - bL : 0);
@@ -715,11 +721,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
                     zc + (min(max(col * zrow + (uint32_t)(16 * tt) * zrow, zlo), zhi) + 4 * q * AS)));
         }
 
-        // tiles of the next block into the other buffer, then the tile loads of block b + 2
+        // tiles of the next block into the other buffer, then the tile loads of block b + 3
         // (the last blocks reload themselves, keeping the loads unconditional)
-        const int64_t b2 = b + 2 <= b1 ? b + 2 : b1;
-        stage_tiles(b < b1 ? b + 1 : b, buf ^ 1);
-        prefetch_tiles(b2);
+        const int64_t b3 = b + 3 <= b1 ? b + 3 : b1;
+        stage_tiles(b < b1 ? b + 1 : b, buf ^ 1, R);
+        prefetch_tiles(b3, R);
 
         // carried-state output: y[t][p] = exp(lam_t) sum_n C_t[n] H[p][n]
         f32x4 acc[TL];
@@ -769,9 +775,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             acc[tt] = mma(Xc[tt / 2], Dsel[tt & 1], acc[tt]);
         }
         // operands of the next block (VALU work beside the MFMAs above; the last block restages
-        // itself into the unused buffer), then the token and C.B^T loads of block b + 2
-        stage_ops(b < b1 ? b + 1 : b, buf ^ 1);
-        prefetch_ops(b2);
+        // itself into the unused buffer), then the token and C.B^T loads of block b + 3
+        stage_ops(b < b1 ? b + 1 : b, buf ^ 1, R);
+        prefetch_ops(b3, R);
 
         // epilogue
         {
@@ -794,6 +800,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
         }
 
         __syncthreads();
+    };
+    for (int64_t b = b0; b <= b1; b += 2) {
+        block(b, P1);
+        if (b + 1 <= b1) block(b + 1, P0);
     }
 
     if (!only) {
