@@ -120,7 +120,8 @@ int mamba2_chunk_scan_workspace_bytes(const mamba2_dims *dims, int64_t total_tok
  *   xbc            [total_tokens][Cdim] act_dtype, raw inputs (not modified)
  *   xbc_out        [total_tokens][Cdim] xbc_dtype, SiLU(conv); must not alias xbc
  *   cu_seqlens     [nseq+1] int32 device, cu_seqlens[0] = 0, nondecreasing,
- *                  cu_seqlens[nseq] = total_tokens
+ *                  cu_seqlens[nseq] = total_tokens (so total_tokens <= INT32_MAX;
+ *                  larger totals return MAMBA2_ERR_INVALID_ARG)
  *   state_indices  [nseq] int32 device: conv pool slot of each sequence
  *   has_initial_state [nseq] uint8 device or NULL (all 0): 1 = left context is
  *                  the slot's cached inputs, 0 = zeros

@@ -158,6 +158,8 @@ int mamba2_conv1d_fwd(const mamba2_dims *d, const void *xbc, const float *conv_w
     if (st) return st;
     if (num_slots < 0) return fail(MAMBA2_ERR_INVALID_ARG, "num_slots must be >= 0 (got %d)", num_slots);
     if (nseq < 0 || total_tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative nseq or total_tokens");
+    if (total_tokens > INT32_MAX)  // (cu_seqlens are int32)
+        return fail(MAMBA2_ERR_INVALID_ARG, "total_tokens %lld beyond the int32 range of cu_seqlens", (long long)total_tokens);
     if (nseq == 0) {
         if (total_tokens != 0) return fail(MAMBA2_ERR_INVALID_ARG, "tokens without sequences");
         return ok();
@@ -197,6 +199,8 @@ int mamba2_chunk_scan_fwd(const mamba2_dims *d, const void *xbc, const void *dt_
     if (st) return st;
     if (num_slots < 0) return fail(MAMBA2_ERR_INVALID_ARG, "num_slots must be >= 0 (got %d)", num_slots);
     if (nseq < 0 || total_tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative nseq or total_tokens");
+    if (total_tokens > INT32_MAX)  // (cu_seqlens are int32)
+        return fail(MAMBA2_ERR_INVALID_ARG, "total_tokens %lld beyond the int32 range of cu_seqlens", (long long)total_tokens);
     if (nseq == 0) {
         if (total_tokens != 0) return fail(MAMBA2_ERR_INVALID_ARG, "tokens without sequences");
         return ok();
@@ -289,6 +293,8 @@ int mamba2_mixed_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw, 
     int st = mamba2_check_dims(d);
     if (st) return st;
     if (nseq < 0 || total_tokens < 0 || decode_batch < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative size");
+    if (total_tokens > INT32_MAX)  // (cu_seqlens are int32)
+        return fail(MAMBA2_ERR_INVALID_ARG, "total_tokens %lld beyond the int32 range of cu_seqlens", (long long)total_tokens);
     const m2::LayerShape s = shape_of(d);
     const int64_t cdim = s.cdim(), hp = (int64_t)s.H * s.P;
     const size_t ab = dtype_bytes(d->act_dtype), xb = dtype_bytes(d->xbc_dtype), ob = dtype_bytes(d->out_dtype);
@@ -397,6 +403,8 @@ int mamba2_prefill_fwd(const mamba2_dims *d, const void *xbc, const void *dt_raw
         if (!(norm_eps >= 0.0f)) return fail(MAMBA2_ERR_INVALID_ARG, "norm_eps must be >= 0");
     }
     if (nseq < 0 || total_tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative nseq or total_tokens");
+    if (total_tokens > INT32_MAX)  // (cu_seqlens are int32)
+        return fail(MAMBA2_ERR_INVALID_ARG, "total_tokens %lld beyond the int32 range of cu_seqlens", (long long)total_tokens);
     if (nseq == 0) {
         if (total_tokens != 0) return fail(MAMBA2_ERR_INVALID_ARG, "tokens without sequences");
         return ok();
@@ -502,6 +510,8 @@ int mamba1_selective_scan_fwd(const mamba1_dims *d, const void *u, const void *d
     if (st) return st;
     if (num_slots < 0) return fail(MAMBA2_ERR_INVALID_ARG, "num_slots must be >= 0 (got %d)", num_slots);
     if (nseq < 0 || total_tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative nseq or total_tokens");
+    if (total_tokens > INT32_MAX)  // (cu_seqlens are int32)
+        return fail(MAMBA2_ERR_INVALID_ARG, "total_tokens %lld beyond the int32 range of cu_seqlens", (long long)total_tokens);
     if (nseq == 0) {
         if (total_tokens != 0) return fail(MAMBA2_ERR_INVALID_ARG, "tokens without sequences");
         return ok();

@@ -513,6 +513,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     const uint32_t clane = (uint32_t)(tid / (N / 8)) * crow + 16 * (tid % (N / 8));
     const uint32_t zrow = (uint32_t)HP * AS;                               // bytes per z row
     const uint32_t ylane = col * (uint32_t)HP * 2 + 8 * q;                 // y: row col of a t-tile, channels 4q..
+    // The workgroup's blocks, and the sequence (or segment) bounds and the packed end relative to
+    // the first one's start: per block, edges are then 32-bit differences (a sequence has fewer
+    // than 2^31 tokens), not 64-bit compares and selects.
+    const int64_t b0 = start / L, b1 = end > start ? (end - 1) / L : b0 - 1;
+    const int32_t s_rel = (int32_t)(start - b0 * L), e_rel = (int32_t)(end - b0 * L);
+    const int32_t t_rel = (int32_t)(a.T - b0 * L);  // (T fits: the boundary refuses totals past int32)
+    auto rel = [&](int64_t b) { return (int32_t)(b - b0) * L; };  // block b's first token, relative to block b0
     // Loads of a block in two parts, each issued as soon as the registers it fills are free
     // (the tiles' once they are staged into LDS, the token and C.B^T values' once the operands
     // are formed), into the set that block b + 1 has just left: two iterations to arrive.
@@ -521,16 +528,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
         const char *btb = static_cast<const char *>(a.bt) + (b * G + g) * (int64_t)(2 * N * L * 2);
 #pragma unroll
         for (int i = 0; i < BTP; ++i) R.btr[i] = *reinterpret_cast<const u32x4 *>(btb + 16u * (tid + i * NT));
-        const int tmax = (int)(a.T - 1 - bL < L - 1 ? a.T - 1 - bL : L - 1);  // C rows end at T
+        const int tr = t_rel - 1 - rel(b);
+        const int tmax = tr < L - 1 ? tr : L - 1;  // C rows end at T
         const char *cpb = static_cast<const char *>(a.cp) + (bL * GN + (int64_t)g * N) * 2;
         const uint32_t cmax = (uint32_t)tmax * crow + 16 * (tid % (N / 8));
 #pragma unroll
         for (int i = 0; i < CPC; ++i)
             R.cr[i] = *reinterpret_cast<const u32x4 *>(cpb + min(clane + (uint32_t)(i * (NT / (N / 8))) * crow, cmax));
-        const int lo = (int)(start - bL > -W ? start - bL : -W);           // first valid row, block-relative
-        const int hi = (int)(end - 1 - bL < L + 8 ? end - 1 - bL : L + 8);  // last valid row
+        const int sr = s_rel - rel(b), er = e_rel - 1 - rel(b);
+        const int lo = sr > -W ? sr : -W;          // first valid row, block-relative
+        const int hi = er < L + 8 ? er : L + 8;    // last valid row
         // first x row that holds data: a later segment's context rows are tokens of its sequence
-        const int xl = first ? lo : (int)(start - (W - 1) - bL > -W ? start - (W - 1) - bL : -W);
+        const int xl = first ? lo : (sr - (W - 1) > -W ? sr - (W - 1) : -W);
         // raw x rows bL - (W-1) + rho, rho in [0, L + W - 1), of this wave's 16 channels
         const char *xc = static_cast<const char *>(a.xbc) + ((bL - (W - 1)) * cdim + (int64_t)head * P + 16 * wv) * XS;
         const uint32_t xlo = (uint32_t)(xl + (W - 1) > 0 ? xl + (W - 1) : 0) * xrow, xhi = (uint32_t)(hi + (W - 1)) * xrow;
@@ -540,8 +549,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     };
     auto prefetch_ops = [&](int64_t b, Pre &R) __attribute__((always_inline)) {
         const int64_t bL = b * L;
-        const int lo = (int)(start - bL > -W ? start - bL : -W);           // first valid row, block-relative
-        const int hi = (int)(end - 1 - bL < L + 8 ? end - 1 - bL : L + 8);  // last valid row
+        const int sr = s_rel - rel(b), er = e_rel - 1 - rel(b);
+        const int lo = sr > -W ? sr : -W;          // first valid row, block-relative
+        const int hi = er < L + 8 ? er : L + 8;    // last valid row
         const char *dtc = static_cast<const char *>(a.dt_raw) + (bL * H + head) * AS;
         R.dtr = ld_bits(reinterpret_cast<const AT *>(dtc + min(max(dtlane, (uint32_t)max(lo, 0) * H * AS), (uint32_t)hi * H * AS)));
         const char *cbb = static_cast<const char *>(a.cb) + ((b * G + g) * (int64_t)(TL * KL) + ttw * KL) * 512 * 4;
@@ -585,10 +595,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     // operands of block b (token arrays, conv + SiLU of x, decayed C.B^T into sM[buf])
     auto stage_ops = [&](int64_t b, int buf, Pre &R) __attribute__((always_inline)) {
         const int64_t bL = b * L;
-        const int lo = (int)(start - bL > 0 ? start - bL : 0);
-        const int hi = (int)(end - bL < L ? end - bL : L);
+        const int sr = s_rel - rel(b), er = e_rel - rel(b);
+        const int lo = sr > 0 ? sr : 0;
+        const int hi = er < L ? er : L;
         // sequence start, block-relative (a later segment has none: its context rows are real tokens)
-        const int ctxlo = first ? (int)(start - bL > -W ? start - bL : -W) : -W;
+        const int ctxlo = first ? (sr > -W ? sr : -W) : -W;
         // token arrays, every wave its own copy: dt, inclusive lam, dt exp(lam_end - lam)
         {
             // (softplus for every lane, then a multiply by 0 / 1: no branch around it)
@@ -679,7 +690,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
         }
     };
 
-    const int64_t b0 = start / L, b1 = end > start ? (end - 1) / L : b0 - 1;
     if (b0 <= b1) {
         prefetch_tiles(b0, P0);
         prefetch_ops(b0, P0);
@@ -696,14 +706,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     auto block = [&](int64_t b, Pre &R) __attribute__((always_inline)) {
         const int buf = (int)((b - b0) & 1);
         const int64_t bL = b * L;
-        const int lo = (int)(start - bL > 0 ? start - bL : 0);
-        const int hi = (int)(end - bL < L ? end - bL : L);
+        const int sr = s_rel - rel(b), er = e_rel - rel(b);
+        const int lo = sr > 0 ? sr : 0;
+        const int hi = er < L ? er : L;
         // this block's staged operands (the next stage overwrites the variables)
         bf16x8 Xc[KL], XDc[KL], XShc[KL], XSlc[KL];
         float elc[TL];
         const float decc = dec;
         lsum += l2e;
-        if (a.seg && tid == 0 && bL >= start && bL + L <= end) a.seg_lam[b * H + head] = lsum;
+        if (a.seg && tid == 0 && rel(b) >= s_rel && rel(b) + L <= e_rel) a.seg_lam[b * H + head] = lsum;
 #pragma unroll
         for (int m = 0; m < KL; ++m) { Xc[m] = X[m]; XDc[m] = XD[m]; XShc[m] = XSh[m]; XSlc[m] = XSl[m]; }
 #pragma unroll

@@ -107,6 +107,12 @@ def test_invalid_arguments_rejected_without_gpu(lib):
     st = lib.mamba2_chunk_scan_fwd(_cd(), good, good, good, good, good, None, good, good, 8, good, 0, 5, good, None,
                                    None, 0, None)
     assert st == B.ERR_INVALID_ARG
+    # more packed tokens than int32 cu_seqlens can describe
+    st = lib.mamba2_chunk_scan_fwd(_cd(), good, good, good, good, good, None, good, good, 8, good, 1, 2 ** 31, good,
+                                   None, None, 0, None)
+    assert st == B.ERR_INVALID_ARG and b"int32" in lib.mamba2_last_error()
+    st = lib.mamba2_conv1d_fwd(_cd(), good, good, None, good, good, 8, good, 1, 2 ** 31, good, None, None)
+    assert st == B.ERR_INVALID_ARG and b"int32" in lib.mamba2_last_error()
     # a workspace smaller than the block form needs
     st = lib.mamba2_chunk_scan_fwd(_cd(), good, good, good, good, good, None, good, good, 8, good, 1, 64, good, None,
                                    good, 1024, None)
