@@ -168,7 +168,11 @@ int mamba2_chunk_scan_fwd(const mamba2_dims *dims, const void *xbc, const void *
  * right-hand column of "Cost, at T=1, chunk_size=128, nchunks=1": one launch,
  * no allocation, no memset, no scratch).
  *   xbc [batch][Cdim] xbc_dtype (post-conv); dt_raw [batch][H] act_dtype;
- *   z [batch][H*P] act_dtype or NULL; y [batch][H*P] out_dtype. */
+ *   z [batch][H*P] act_dtype or NULL; y [batch][H*P] out_dtype.
+ *   Supported: dstate 16, 64 or 128, headdim a multiple of 4, and Cdim and
+ *   headdim * dstate at most 2^24 (rows and state tiles are addressed by 32-bit
+ *   byte offsets); MAMBA2_ERR_UNSUPPORTED otherwise, here and in every entry
+ *   point that runs the update (multi-token, mixed). */
 int mamba2_state_update(const mamba2_dims *dims, const void *xbc, const void *dt_raw,
                         const float *A_log, const float *dt_bias, const float *D, const void *z,
                         void *y, void *ssm_pool, int32_t num_slots, const int32_t *state_indices,
@@ -189,7 +193,10 @@ int mamba2_state_update(const mamba2_dims *dims, const void *xbc, const void *dt
  *   xbc_out [batch][T][Cdim] xbc_dtype.
  * Every source slot is read before any destination is written only within a
  * row: a destination that is another row's source (or two rows writing one
- * slot) races. src_indices[i] < 0 marks a padding row (y = 0, no slot access). */
+ * slot) races. src_indices[i] < 0 marks a padding row (y = 0, no slot access).
+ * mamba2_state_update_multi addresses a row's tokens by 32-bit byte offsets:
+ * T * Cdim * 4 above 2^32 - 1 returns MAMBA2_ERR_UNSUPPORTED (T up to 104,857
+ * at Nemotron-H-8B dims). */
 int mamba2_conv1d_update_multi(const mamba2_dims *dims, const void *xbc, const float *conv_w,
                                const float *conv_b, void *xbc_out, void *conv_pool, int32_t num_slots,
                                const int32_t *src_indices, const int32_t *dst_indices,

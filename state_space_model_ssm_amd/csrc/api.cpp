@@ -74,6 +74,10 @@ int check_state_update(const mamba2_dims *d) {
     if (!m2::state_update_supported(s) || s.cdim() % 8 != 0 || s.P % 4 != 0)
         return fail(MAMBA2_ERR_UNSUPPORTED, "state update supports dstate in {16, 64, 128}, headdim %% 4 == 0 (N=%d)",
                     d->dstate);
+    // (the update kernels address a token's row and a head's state tile by 32-bit byte offsets)
+    if (s.cdim() > (1 << 24) || (int64_t)s.P * s.N > (1 << 24))
+        return fail(MAMBA2_ERR_UNSUPPORTED, "state update supports Cdim and headdim * dstate up to 2^24 (Cdim=%lld)",
+                    (long long)s.cdim());
     return MAMBA2_OK;
 }
 
@@ -273,6 +277,10 @@ int mamba2_state_update_multi(const mamba2_dims *d, const void *xbc, const void 
     if (num_slots < 0) return fail(MAMBA2_ERR_INVALID_ARG, "num_slots must be >= 0 (got %d)", num_slots);
     if (batch < 0 || tokens < 0) return fail(MAMBA2_ERR_INVALID_ARG, "negative batch or tokens");
     if (batch == 0 || tokens == 0) return ok();
+    // (a row's T tokens are addressed by 32-bit byte offsets from the row's start)
+    if ((int64_t)tokens * shape_of(d).cdim() * 4 > (int64_t)UINT32_MAX)
+        return fail(MAMBA2_ERR_UNSUPPORTED, "tokens x Cdim x 4 bytes beyond 2^32 (tokens=%d, Cdim=%lld)", tokens,
+                    (long long)shape_of(d).cdim());
     REQUIRE_PTR(xbc); REQUIRE_PTR(dt_raw); REQUIRE_PTR(A_log); REQUIRE_PTR(dt_bias); REQUIRE_PTR(D);
     OPT_PTR(z); REQUIRE_PTR(y); REQUIRE_PTR(ssm_pool); REQUIRE_IDX(src_indices);
     if (dst_indices && (reinterpret_cast<uintptr_t>(dst_indices) & 3u))

@@ -190,9 +190,11 @@ template <typename T, int K> struct RawRow {
 };
 
 // K consecutive outputs in one store (y of a thread's K rows)
-template <int K> __device__ __forceinline__ void store_row(void *p, int dt, int64_t i, const float *v) {
+// (i: a wave-uniform element index, l: the lane's element offset from it, kept 32-bit so
+// that the store takes the scalar-base form)
+template <int K> __device__ __forceinline__ void store_row(void *p, int dt, int64_t i, uint32_t l, const float *v) {
     if (dt == DT_BF16) {
-        bf16 *q = static_cast<bf16 *>(p) + i;
+        bf16 *q = reinterpret_cast<bf16 *>(static_cast<char *>(p) + i * 2 + 2u * l);
         if constexpr (K == 4) {
             typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
             *reinterpret_cast<bf16x4 *>(q) = bf16x4{f32_to_bf16(v[0]), f32_to_bf16(v[1]), f32_to_bf16(v[2]), f32_to_bf16(v[3])};
@@ -203,7 +205,7 @@ template <int K> __device__ __forceinline__ void store_row(void *p, int dt, int6
             *q = f32_to_bf16(v[0]);
         }
     } else {
-        float *q = static_cast<float *>(p) + i;
+        float *q = reinterpret_cast<float *>(static_cast<char *>(p) + i * 4 + 4u * l);
         if constexpr (K == 4) *reinterpret_cast<f32x4 *>(q) = f32x4{v[0], v[1], v[2], v[3]};
         else if constexpr (K == 2) *reinterpret_cast<float2 *>(q) = float2{v[0], v[1]};
         else *q = v[0];
@@ -255,11 +257,11 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
     auto store_y = [&](int t, const float *yv) {
         if (!ylane) return;
         if constexpr (CONSEC) {
-            if (prow(0) < P) store_row<ITERS>(a.y, out_dt, ybase + (int64_t)t * HP + prow(0), yv);
+            if (prow(0) < P) store_row<ITERS>(a.y, out_dt, ybase, (uint32_t)t * (uint32_t)HP + prow(0), yv);
         } else {
 #pragma unroll
             for (int it = 0; it < ITERS; ++it)
-                if (prow(it) < P) st(a.y, out_dt, ybase + (int64_t)t * HP + prow(it), yv[it]);
+                if (prow(it) < P) store_row<1>(a.y, out_dt, ybase, (uint32_t)t * (uint32_t)HP + prow(it), &yv[it]);
         }
     };
     const int src = pool_slot(a.src[row], a.num_slots, a.err, blockIdx.x == 0 && tid == 0);
@@ -271,8 +273,6 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
         return;
     }
     const int g = head / (H / G);
-    ST *pool = static_cast<ST *>(a.pool);
-    const int64_t tile0 = (int64_t)head * P * N + n0;
     const float A = -expf(a.A_log[head]);
     const float dtb = a.dt_bias[head];
     const float Dh = a.D[head];
@@ -293,8 +293,21 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
     RawRow<XT, XK> xr[TB][XI];
     RawRow<AT, XK> zr[HasZ ? TB : 1][HasZ ? XI : 1];
     float dr = 0.0f;
-    const XT *xh = static_cast<const XT *>(a.xbc) + (int64_t)row * T * cdim + (int64_t)head * P;
-    const AT *zh = static_cast<const AT *>(a.z) + ybase;
+    // Addresses: the row's (or the slot's) base, wave-uniform in scalar registers, plus a
+    // 32-bit byte offset per lane that includes the token (the scalar-base load and store
+    // form; the boundary keeps T x Cdim and P x N small enough for the offsets). With 64-bit
+    // address arithmetic per lane and access, which the compiler also makes of a 64-bit
+    // token term added to a loop-invariant lane offset, addresses cost a sixth of the
+    // kernel's VALU instructions.
+    constexpr uint32_t XS = sizeof(XT), AS = sizeof(AT), SS = sizeof(ST);
+    uint32_t xoff[XI], soff[ITERS];
+#pragma unroll
+    for (int i = 0; i < XI; ++i) xoff[i] = (uint32_t)pr[i] * XS;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) soff[it] = ((uint32_t)pr[it] * N + n0) * SS;
+    auto tk = [&](int t) { return (uint32_t)min(t, T - 1); };  // token t of the row, clamped to its last
+    const char *xrow_b = static_cast<const char *>(a.xbc) + ((int64_t)row * T * cdim + (int64_t)head * P) * XS;
+    const char *pool_b = static_cast<const char *>(a.pool) + (int64_t)head * P * N * SS;
     auto xval = [&](int u, int it) {
         if constexpr (CONSEC) return xr[u][0][it];
         else return xr[u][it][0];
@@ -307,20 +320,24 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
     auto load_block = [&](int t0) {
         if (tid < NT4) {
             const int u = tid / (N / 2), rem = tid % (N / 2), which = rem / (N / 4), n4 = rem % (N / 4);
-            const int64_t r = (int64_t)row * T + min(t0 + u, T - 1);
-            bcr.load(static_cast<const XT *>(a.xbc) + r * cdim + HP + (int64_t)which * G * N + (int64_t)g * N + 4 * n4);
+            const char *bc_b = static_cast<const char *>(a.xbc) + ((int64_t)row * T * cdim + HP + (int64_t)g * N) * XS;
+            bcr.load(reinterpret_cast<const XT *>(bc_b + (tk(t0 + u) * (uint32_t)cdim + which * G * N + 4 * n4) * XS));
         }
 #pragma unroll
         for (int u = 0; u < TB; ++u)
 #pragma unroll
-            for (int i = 0; i < XI; ++i) xr[u][i].load(xh + (int64_t)min(t0 + u, T - 1) * cdim + pr[i]);
+            for (int i = 0; i < XI; ++i)
+                xr[u][i].load(reinterpret_cast<const XT *>(xrow_b + (tk(t0 + u) * (uint32_t)cdim * XS + xoff[i])));
         if constexpr (HasZ)
 #pragma unroll
             for (int u = 0; u < TB; ++u)
 #pragma unroll
-                for (int i = 0; i < XI; ++i) zr[u][i].load(zh + (int64_t)min(t0 + u, T - 1) * HP + pr[i]);
+                for (int i = 0; i < XI; ++i)
+                    zr[u][i].load(reinterpret_cast<const AT *>(static_cast<const char *>(a.z) + ybase * AS +
+                                                                (tk(t0 + u) * (uint32_t)HP + pr[i]) * AS));
         const int u = (tid & 63) & (TB - 1);
-        dr = (float)static_cast<const AT *>(a.dt_raw)[((int64_t)row * T + min(t0 + u, T - 1)) * H + head];
+        dr = (float)*reinterpret_cast<const AT *>(static_cast<const char *>(a.dt_raw) + ((int64_t)row * T * H + head) * AS +
+                                                  tk(t0 + u) * (uint32_t)H * AS);
     };
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int t_stage = 0;  // first token of the block being staged
@@ -345,7 +362,8 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
     load_block(0);
     float h[ITERS][kVec];
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) nt_load16<ST>(pool + (int64_t)src * H * P * N + tile0 + (int64_t)pr[it] * N, h[it]);
+    for (int it = 0; it < ITERS; ++it)
+        nt_load16<ST>(reinterpret_cast<const ST *>(pool_b + (int64_t)src * H * P * N * SS + soff[it]), h[it]);
 
     for (int t0 = 0; t0 < T; t0 += TB) {
         if (t0 > 0) {
@@ -386,13 +404,14 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
                     h[it][j] = fmaf(decay, h[it][j], dx * Bv[j]);  // as the one-token kernel
                     acc = fmaf(Cv[j], h[it][j], acc);
                 }
-                if (d >= 0 && prow(it) < P) nt_store16<ST>(pool + (int64_t)d * H * P * N + tile0 + (int64_t)prow(it) * N, h[it]);
+                if (d >= 0 && prow(it) < P)
+                    nt_store16<ST>(reinterpret_cast<ST *>(const_cast<char *>(pool_b) + (int64_t)d * H * P * N * SS + soff[it]), h[it]);
                 acc = group_sum_last<kLpr>(acc);
                 yv[it] = fmaf(Dh, x, acc);
                 if constexpr (HasZ) yv[it] *= silu_f(zval(u, it));
                 if constexpr (!CONSEC)  // (stored at once: holding them costs registers here)
                     if (live && ylane && prow(it) < P)
-                        st(a.y, out_dt, ((int64_t)row * T + t) * HP + (int64_t)head * P + prow(it), yv[it]);
+                        store_row<1>(a.y, out_dt, ybase, (uint32_t)t * (uint32_t)HP + prow(it), &yv[it]);
             }
             if constexpr (CONSEC)
                 if (live) store_y(t, yv);
@@ -401,7 +420,8 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
     if (CONSEC || !a.dst)
 #pragma unroll
         for (int it = 0; it < ITERS; ++it)
-            if (prow(it) < P) nt_store16<ST>(pool + (int64_t)src * H * P * N + tile0 + (int64_t)prow(it) * N, h[it]);
+            if (prow(it) < P)
+                nt_store16<ST>(reinterpret_cast<ST *>(const_cast<char *>(pool_b) + (int64_t)src * H * P * N * SS + soff[it]), h[it]);
 }
 
 template <typename ST, typename XT, typename AT, int N, int ITERS, bool CONSEC>

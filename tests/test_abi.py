@@ -72,6 +72,10 @@ def test_check_dims(lib):
     with pytest.raises(B.Mamba2Error) as e:
         B.mamba2_check_dims(NEMOTRON_H_8B.with_(dstate=48))
     assert e.value.status == B.ERR_UNSUPPORTED
+    # the update kernels address rows and state tiles by 32-bit byte offsets: Cdim up to 2^24
+    with pytest.raises(B.Mamba2Error) as e:
+        B.mamba2_check_dims(NEMOTRON_H_8B.with_(nheads=1 << 18, ngroups=8))
+    assert e.value.status == B.ERR_UNSUPPORTED and "2^24" in str(e.value)
 
 
 def _cd(d=NEMOTRON_H_8B):
@@ -113,6 +117,10 @@ def test_invalid_arguments_rejected_without_gpu(lib):
     assert st == B.ERR_INVALID_ARG and b"int32" in lib.mamba2_last_error()
     st = lib.mamba2_conv1d_fwd(_cd(), good, good, None, good, good, 8, good, 1, 2 ** 31, good, None, None)
     assert st == B.ERR_INVALID_ARG and b"int32" in lib.mamba2_last_error()
+    # a multi-token row past the 32-bit byte offsets of its tokens (T x Cdim x 4 >= 2^32)
+    st = lib.mamba2_state_update_multi(_cd(), good, good, good, good, good, None, good, good, 8, good, None, 1,
+                                       2 ** 17, None)
+    assert st == B.ERR_UNSUPPORTED and b"2^32" in lib.mamba2_last_error()
     # a workspace smaller than the block form needs
     st = lib.mamba2_chunk_scan_fwd(_cd(), good, good, good, good, good, None, good, good, 8, good, 1, 64, good, None,
                                    good, 1024, None)
