@@ -116,8 +116,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(XT) 
     const int col = lane & 15, q = lane >> 4;
     const int blk = blockIdx.x, g = blockIdx.y;
     const int64_t HP = (int64_t)H * P, GN = (int64_t)G * N, cdim = HP + 2 * GN;
-    const int cg = tid & 31, run = tid >> 5;
-    const bool isC = cg >= 16;
+    // waves 0 and 2 take the B channels, waves 1 and 3 the C channels (16 groups of 8 channels x
+    // 4 runs of RL tokens each): the per-token output path is one branch per wave, not both
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const bool isC = wv & 1;
+    const int cg = (tid & 15) + (isC ? 16 : 0), run = ((tid >> 4) & 3) + 4 * (wv >> 1);
     const int n0 = 8 * (cg & 15);
     const int64_t c0 = HP + (isC ? GN : 0) + (int64_t)g * N + n0;  // first of this thread's 8 channels
     const int64_t t0 = (int64_t)blk * L + run * RL;
