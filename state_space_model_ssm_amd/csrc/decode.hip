@@ -558,66 +558,94 @@ hipError_t launch_conv_update(const LayerShape &s, const ConvUpdateArgs &a, hipS
 // T tokens per row: window = [cached W-1 inputs || token], shifted per token;
 // after token t the window goes to dst[row][t] when that slot is >= 0 (no dst
 // table: the final window to the source slot).
-template <typename AT, typename ST, typename XT, int W>
+template <typename AT, typename ST, typename XT, int W, int CPT>
 __global__ __launch_bounds__(256) void conv_update_multi_kernel(ConvMultiArgs a, int64_t cdim) {
     const int row = blockIdx.y;
-    const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * CPT;
     if (c0 >= cdim) return;
     const int T = a.T;
     const int src = pool_slot(a.src[row], a.num_slots, a.err, c0 == 0);
-    float o[8];
+    XT *out = static_cast<XT *>(a.out) + (int64_t)row * T * cdim + c0;
+    float o[CPT];
     if (src < 0) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = 0.0f;
-        for (int t = 0; t < T; ++t) store_k<XT, 8>(static_cast<XT *>(a.out) + ((int64_t)row * T + t) * cdim + c0, o);
+        for (int j = 0; j < CPT; ++j) o[j] = 0.0f;
+        for (int t = 0; t < T; ++t) store_k<XT, CPT>(out + (int64_t)t * cdim, o);
         return;
     }
+    // The tokens go in blocks of TB whose raw inputs are all loaded before the first is used
+    // (rows past T clamped to the last), next to the window and the weights: one round trip
+    // per block instead of one per token.
+    constexpr int TB = 4;
+    const AT *xin = static_cast<const AT *>(a.xbc) + (int64_t)row * T * cdim + c0;
     ST *pool = static_cast<ST *>(a.pool);
-    float win[W - 1][8], w[8 * W];
+    Raw<AT, CPT> ur[TB];
 #pragma unroll
-    for (int k = 0; k < W - 1; ++k) load_k<ST, 8>(pool + ((int64_t)src * (W - 1) + k) * cdim + c0, win[k]);
-    load_k<float, 8 * W>(a.w + c0 * W, w);
-    for (int t = 0; t < T; ++t) {
-        float u[8];
-        load_k<AT, 8>(static_cast<const AT *>(a.xbc) + ((int64_t)row * T + t) * cdim + c0, u);
+    for (int i = 0; i < TB; ++i) ur[i].load(xin + (int64_t)min(i, T - 1) * cdim);
+    float win[W - 1][CPT], w[CPT * W], bias[CPT];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float v = a.b ? a.b[c0 + j] : 0.0f;
+    for (int k = 0; k < W - 1; ++k) load_k<ST, CPT>(pool + ((int64_t)src * (W - 1) + k) * cdim + c0, win[k]);
+    load_k<float, CPT * W>(a.w + c0 * W, w);
 #pragma unroll
-            for (int k = 0; k < W - 1; ++k) v += w[j * W + k] * win[k][j];
-            v += w[j * W + W - 1] * u[j];
-            o[j] = silu_f(v);
-        }
-        store_k<XT, 8>(static_cast<XT *>(a.out) + ((int64_t)row * T + t) * cdim + c0, o);
+    for (int j = 0; j < CPT; ++j) bias[j] = a.b ? a.b[c0 + j] : 0.0f;
+    for (int t0 = 0; t0 < T; t0 += TB) {
+        if (t0 > 0)
 #pragma unroll
-        for (int k = 0; k < W - 2; ++k)
+            for (int i = 0; i < TB; ++i) ur[i].load(xin + (int64_t)min(t0 + i, T - 1) * cdim);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) win[k][j] = win[k + 1][j];
+        for (int i = 0; i < TB; ++i) {
+            const int t = t0 + i;
+            if (t < T) {
+                float u[CPT];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) win[W - 2][j] = u[j];
-        if (a.dst) {
-            const int d = pool_slot(a.dst[(int64_t)row * T + t], a.num_slots, a.err, c0 == 0);
-            if (d >= 0)
+                for (int j = 0; j < CPT; ++j) {
+                    u[j] = ur[i][j];
+                    float v = bias[j];  // the order of the one-token update: bias, cached taps, new input
 #pragma unroll
-                for (int k = 0; k < W - 1; ++k) store_k<ST, 8>(pool + ((int64_t)d * (W - 1) + k) * cdim + c0, win[k]);
+                    for (int k = 0; k < W - 1; ++k) v += w[j * W + k] * win[k][j];
+                    v += w[j * W + W - 1] * u[j];
+                    o[j] = silu_f(v);
+                }
+                store_k<XT, CPT>(out + (int64_t)t * cdim, o);
+#pragma unroll
+                for (int k = 0; k < W - 2; ++k)
+#pragma unroll
+                    for (int j = 0; j < CPT; ++j) win[k][j] = win[k + 1][j];
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) win[W - 2][j] = u[j];
+                if (a.dst) {
+                    const int d = pool_slot(a.dst[(int64_t)row * T + t], a.num_slots, a.err, c0 == 0);
+                    if (d >= 0)
+#pragma unroll
+                        for (int k = 0; k < W - 1; ++k) store_k<ST, CPT>(pool + ((int64_t)d * (W - 1) + k) * cdim + c0, win[k]);
+                }
+            }
         }
     }
     if (!a.dst)
 #pragma unroll
-        for (int k = 0; k < W - 1; ++k) store_k<ST, 8>(pool + ((int64_t)src * (W - 1) + k) * cdim + c0, win[k]);
+        for (int k = 0; k < W - 1; ++k) store_k<ST, CPT>(pool + ((int64_t)src * (W - 1) + k) * cdim + c0, win[k]);
+}
+
+// 4 channels per thread where 8 would give under 2,048 workgroups (256 rows at 8B dims give
+// 1,280: the kernel is a few round trips, so more, shorter threads finish sooner)
+template <typename AT, typename ST, typename XT, int CPT>
+static hipError_t launch_cum_c(const LayerShape &s, const ConvMultiArgs &a, hipStream_t stream) {
+    const int64_t cdim = s.cdim();
+    dim3 grid((unsigned)((cdim / CPT + 255) / 256), a.batch);
+    switch (s.W) {
+        case 2: hipLaunchKernelGGL((conv_update_multi_kernel<AT, ST, XT, 2, CPT>), grid, dim3(256), 0, stream, a, cdim); break;
+        case 3: hipLaunchKernelGGL((conv_update_multi_kernel<AT, ST, XT, 3, CPT>), grid, dim3(256), 0, stream, a, cdim); break;
+        case 4: hipLaunchKernelGGL((conv_update_multi_kernel<AT, ST, XT, 4, CPT>), grid, dim3(256), 0, stream, a, cdim); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 template <typename AT, typename ST, typename XT>
 static hipError_t launch_cum_w(const LayerShape &s, const ConvMultiArgs &a, hipStream_t stream) {
-    const int64_t cdim = s.cdim();
-    dim3 grid((unsigned)((cdim / 8 + 255) / 256), a.batch);
-    switch (s.W) {
-        case 2: hipLaunchKernelGGL((conv_update_multi_kernel<AT, ST, XT, 2>), grid, dim3(256), 0, stream, a, cdim); break;
-        case 3: hipLaunchKernelGGL((conv_update_multi_kernel<AT, ST, XT, 3>), grid, dim3(256), 0, stream, a, cdim); break;
-        case 4: hipLaunchKernelGGL((conv_update_multi_kernel<AT, ST, XT, 4>), grid, dim3(256), 0, stream, a, cdim); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    const int64_t wg8 = (s.cdim() / 8 + 255) / 256 * (int64_t)a.batch;
+    return wg8 < 2048 ? launch_cum_c<AT, ST, XT, 4>(s, a, stream) : launch_cum_c<AT, ST, XT, 8>(s, a, stream);
 }
 
 template <typename AT, typename ST>
