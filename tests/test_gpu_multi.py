@@ -162,3 +162,29 @@ def test_multi_token_final_state_only_full_dims(out_dtype, with_z):
         assert_close(host(y[r:r + 1]), y_ref, out_dtype, f"y row {r}")
         assert_close(host(ssm[[s]]), sp, BF16, f"final state row {r}")
         assert np.array_equal(host(conv[[s]]), cp)
+
+
+def test_multi_token_conv_wide_batch_equals_single_steps():
+    """The multi-token conv update at a batch wide enough for 8 channels per thread (512 rows at
+    Nemotron-H-8B dims; the narrow batches above take 4) and a token count past one block of 4:
+    bitwise the outputs and conv slots of T one-token conv updates."""
+    d = NEMOTRON_H_8B
+    rows, T = 512, 6
+    print(f"[multi conv] 8B dims, {rows} rows x {T} tokens", flush=True)
+    rng = np.random.Generator(np.random.PCG64(46))
+    params = synth.layer_params(d, rng)
+    pd = params_dev(params)
+    g = torch.Generator(device="cuda").manual_seed(46)
+    x = torch.randn(rows, T, d.conv_dim, generator=g, device="cuda").to(torch.bfloat16)
+    pool0 = torch.randn(rows + 8, d.conv_width - 1, d.conv_dim, generator=g, device="cuda").to(torch.bfloat16)
+    src = dev_i32(rng.permutation(rows + 8)[:rows].astype(np.int32))
+    post_m = torch.empty(rows, T, d.conv_dim, dtype=torch.bfloat16, device="cuda")
+    pool_m = pool0.clone()
+    B.mamba2_conv1d_update_multi(d, x, pd["conv_w"], None, post_m, pool_m, src, None)
+    pool_s = pool0.clone()
+    post_t = torch.empty(rows, d.conv_dim, dtype=torch.bfloat16, device="cuda")
+    for t in range(T):
+        B.mamba2_conv1d_update(d, x[:, t].contiguous(), pd["conv_w"], None, post_t, pool_s, src)
+        torch.cuda.synchronize()
+        assert torch.equal(post_t, post_m[:, t]), f"post-conv rows differ at token {t}"
+    assert torch.equal(pool_s, pool_m)
