@@ -1,5 +1,5 @@
 """Edge cases of the shapes against the oracle: conv widths 2 and 3 (every kernel is built for
-widths 2 to 4), one head per group, the largest decode batch (4,096 rows on a full 4,096-slot
+widths 2 to 4), one head per group, 80 heads in one group, the largest decode batch (4,096 rows on a full 4,096-slot
 pool) and the longest prefill sequence (131,072 tokens, whose packed rows pass 2 GiB of input,
 resumed from a saved state)."""
 from concurrent.futures import ThreadPoolExecutor
@@ -176,3 +176,17 @@ def test_prefill_longest_sequence_131072_tokens():
                      slices=lambda a: a.reshape(-1, 4096, 64))
         assert_close(host(ssm[sl, head]), hr, F32, f"state head {head}")
     assert np.array_equal(host(conv[sl]), w["xbc"][-(d.conv_width - 1):].astype(np.float64))
+
+
+def test_single_group_80_heads():
+    """Mamba-2 2.7B-class head layout at the same head shape: 80 heads sharing one B/C group.
+    The fused prefill (a 2,200-token sequence long enough for the segment mode next to a short
+    one), the unfused prefill (conv1d_fwd + chunk scan without a workspace) and decode."""
+    d = NEMOTRON_H_8B.with_(nheads=80, ngroups=1, state_dtype=F32, out_dtype=BF16)
+    print("[edges] 80 heads, one group", flush=True)
+    w = synth.prefill_batch(d, seed=82, seqlens=[2200, 300], num_slots=3, initial_state=True)
+    hi = np.array([1, 0], np.uint8)
+    prefill_check(d, w, hi, fused=True, what="80 heads fused prefill")
+    prefill_check(d, w, hi, fused=False, what="80 heads unfused prefill")
+    db = d.with_(state_dtype=BF16)
+    decode_check(db, synth.decode_batch(db, seed=83, rows=6, num_slots=9, with_z=True), "80 heads decode")
