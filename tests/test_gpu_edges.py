@@ -1,5 +1,5 @@
 """Edge cases of the shapes against the oracle: conv widths 2 and 3 (every kernel is built for
-widths 2 to 4), one head per group, 80 heads in one group, the largest decode batch (4,096 rows on a full 4,096-slot
+widths 2 to 4), one head per group, 80 heads in one group, 12 heads, the largest decode batch (4,096 rows on a full 4,096-slot
 pool) and the longest prefill sequence (131,072 tokens, whose packed rows pass 2 GiB of input,
 resumed from a saved state)."""
 from concurrent.futures import ThreadPoolExecutor
@@ -190,3 +190,13 @@ def test_single_group_80_heads():
     prefill_check(d, w, hi, fused=False, what="80 heads unfused prefill")
     db = d.with_(state_dtype=BF16)
     decode_check(db, synth.decode_batch(db, seed=83, rows=6, num_slots=9, with_z=True), "80 heads decode")
+
+
+def test_head_count_not_a_multiple_of_eight():
+    """12 heads in 3 groups: the head-to-XCD remap needs H divisible by 8 and falls back to
+    the identity. Fused prefill and decode."""
+    d = D16B.with_(nheads=12, ngroups=3)
+    print("[edges] 12 heads, 3 groups", flush=True)
+    w = synth.prefill_batch(d, seed=84, seqlens=[150, 1, 77], num_slots=4, initial_state=True)
+    prefill_check(d, w, np.array([1, 1, 0], np.uint8), fused=True, what="H = 12 fused prefill")
+    decode_check(d, synth.decode_batch(d, seed=85, rows=4, num_slots=6, with_z=True), "H = 12 decode")
