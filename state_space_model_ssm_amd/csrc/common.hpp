@@ -188,6 +188,24 @@ template <int K> __device__ __forceinline__ float group_sum_last(float v) {
     return v;
 }
 
+// Four sums over each row of 16 lanes, reduce-scattered: on return every lane of
+// quad k of the row (lanes 4k .. 4k + 3) holds the row's total of v[k]. Lanes
+// l and l ^ 8 first trade halves (rows {0, 1} stay with bit 3 clear, {2, 3}
+// with it set), then lanes l and 7 - l of each half row (they differ in bit 2),
+// then the quad sums its four partials: 11 VALU instructions for four totals,
+// against 20 for four window sums and their final adds.
+__device__ __forceinline__ float row16_sum4_scatter(const float v[4], bool bit3, bool bit2) {
+    const float k0 = bit3 ? v[2] : v[0], s0 = bit3 ? v[0] : v[2];
+    const float k1 = bit3 ? v[3] : v[1], s1 = bit3 ? v[1] : v[3];
+    const float a0 = k0 + dpp_add_src<0x128, 0xF>(s0);  // row_ror:8 (the partner l ^ 8)
+    const float a1 = k1 + dpp_add_src<0x128, 0xF>(s1);
+    const float k = bit2 ? a1 : a0, s = bit2 ? a0 : a1;
+    float t = k + dpp_add_src<0x141, 0xF>(s);           // row_half_mirror (the partner 7 - l)
+    t += dpp_add_src<0xB1, 0xF>(t);                     // quad_perm [1, 0, 3, 2]
+    t += dpp_add_src<0x4E, 0xF>(t);                     // quad_perm [2, 3, 0, 1]
+    return t;
+}
+
 // Inclusive prefix sum over the 64 lanes with DPP: shifts within rows of 16,
 // then row broadcasts of lane 15 and lane 31 (no LDS round trips).
 __device__ __forceinline__ float wave_prefix_sum(float v) {

@@ -249,6 +249,10 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
             for (int it = 0; it < ITERS; ++it) pr[it] = P - ITERS + it;
     }
     const bool ylane = lr == kLpr - 1;
+    // Final-state form with four rows per 16-lane group: y sums reduce-scattered over the group
+    // (row16_sum4_scatter) instead of four window sums; the lanes 4k (qlead) store row k's y.
+    constexpr bool kScatter = CONSEC && kLpr == 16 && ITERS == 4;
+    const bool bit3 = lr & 8, bit2 = lr & 4, qlead = (lr & 3) == 0;
     const int64_t HP = (int64_t)H * P;
     const int64_t cdim = HP + 2LL * G * N;
     const int T = a.T;
@@ -406,15 +410,29 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
                 }
                 if (d >= 0 && prow(it) < P)
                     nt_store16<ST>(reinterpret_cast<ST *>(const_cast<char *>(pool_b) + (int64_t)d * H * P * N * SS + soff[it]), h[it]);
-                acc = group_sum_last<kLpr>(acc);
-                yv[it] = fmaf(Dh, x, acc);
-                if constexpr (HasZ) yv[it] *= silu_f(zval(u, it));
-                if constexpr (!CONSEC)  // (stored at once: holding them costs registers here)
-                    if (live && ylane && prow(it) < P)
-                        store_row<1>(a.y, out_dt, ybase, (uint32_t)t * (uint32_t)HP + prow(it), &yv[it]);
+                if constexpr (kScatter) {
+                    yv[it] = acc;  // partial over the lane's kVec values, summed below
+                } else {
+                    acc = group_sum_last<kLpr>(acc);
+                    yv[it] = fmaf(Dh, x, acc);
+                    if constexpr (HasZ) yv[it] *= silu_f(zval(u, it));
+                    if constexpr (!CONSEC)  // (stored at once: holding them costs registers here)
+                        if (live && ylane && prow(it) < P)
+                            store_row<1>(a.y, out_dt, ybase, (uint32_t)t * (uint32_t)HP + prow(it), &yv[it]);
+                }
             }
-            if constexpr (CONSEC)
+            if constexpr (kScatter) {
+                // the four rows' sums reduce-scattered over the group: quad k of it finishes row k
+                const float tot = row16_sum4_scatter(yv, bit3, bit2);
+                const float xk = bit3 ? (bit2 ? xval(u, 3) : xval(u, 2)) : (bit2 ? xval(u, 1) : xval(u, 0));
+                float yk = fmaf(Dh, xk, tot);
+                if constexpr (HasZ)
+                    yk *= silu_f(bit3 ? (bit2 ? zval(u, 3) : zval(u, 2)) : (bit2 ? zval(u, 1) : zval(u, 0)));
+                if (live && qlead && prow(0) < P)
+                    store_row<1>(a.y, out_dt, ybase, (uint32_t)t * (uint32_t)HP + prow(0) + (lr >> 2), &yk);
+            } else if constexpr (CONSEC) {
                 if (live) store_y(t, yv);
+            }
         }
     }
     if (CONSEC || !a.dst)
