@@ -150,6 +150,19 @@ template <typename T> __device__ __forceinline__ void nt_load16(const T *p, floa
         }
     }
 }
+// The 16 bytes of nt_load16 as fp32 values, from raw bits loaded earlier.
+template <typename T> __device__ __forceinline__ void unpack16(const u32x4 &v, float *out) {
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(v[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(v[i] << 16);
+            out[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+        }
+    }
+}
 template <typename T> __device__ __forceinline__ void nt_store16(T *p, const float *in) {
     if constexpr (sizeof(T) == 4) {
         const f32x4 v = {in[0], in[1], in[2], in[3]};

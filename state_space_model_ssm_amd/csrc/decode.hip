@@ -363,19 +363,31 @@ state_update_multi_kernel(MultiStepArgs a, int H, int P, int G, int out_dt, int 
         }
     };
 
+    // Issue order: the first block's loads, then the state's (kept as raw bits), then the
+    // block's staging, then the state's conversion. Left to itself the compiler issued the
+    // block's x and dt loads only after converting the state, two round trips in a row.
     load_block(0);
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 hraw[ITERS];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it)
+        hraw[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(pool_b + (int64_t)src * H * P * N * SS + soff[it]));
+    __builtin_amdgcn_sched_barrier(0);
+    t_stage = 0;
+    stage_block();
+    __builtin_amdgcn_sched_barrier(0);
     float h[ITERS][kVec];
 #pragma unroll
     for (int it = 0; it < ITERS; ++it)
-        nt_load16<ST>(reinterpret_cast<const ST *>(pool_b + (int64_t)src * H * P * N * SS + soff[it]), h[it]);
+        unpack16<ST>(hraw[it], h[it]);
 
     for (int t0 = 0; t0 < T; t0 += TB) {
         if (t0 > 0) {
             __syncthreads();  // previous block's B/C fully read
             load_block(t0);
+            t_stage = t0;
+            stage_block();
         }
-        t_stage = t0;
-        stage_block();
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
