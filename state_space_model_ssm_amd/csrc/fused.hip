@@ -58,10 +58,6 @@ namespace m2 {
 
 namespace {
 
-template <typename T> __device__ __forceinline__ uint32_t ld_bits(const T *p) {
-    if constexpr (sizeof(T) == 4) return *reinterpret_cast<const uint32_t *>(p);
-    else return (uint32_t)*reinterpret_cast<const unsigned short *>(p);
-}
 template <typename T> __device__ __forceinline__ float bits_f(uint32_t v) {
     if constexpr (sizeof(T) == 4) return __uint_as_float(v);
     else return __uint_as_float(v << 16);
@@ -495,7 +491,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     struct Pre {  // one block's loads in registers: B^T, C, raw x, C.B^T and dt
         u32x4 btr[BTP], cr[CPC], xq[XP];
         f32x4 cbr[KL][MJ / 4];
-        uint32_t dtr;
+        AT dtr;  // (as its own type: held as zero-extended bits it cost a copy, and a wait, per block pair)
     };
     Pre P0, P1;  // two sets in turn, so each block's loads have two iterations to arrive
     // Loads take a wave-uniform base plus a 32-bit unsigned byte offset per lane
@@ -556,7 +552,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
         const int lo = sr > -W ? sr : -W;          // first valid row, block-relative
         const int hi = er < L + 8 ? er : L + 8;    // last valid row
         const char *dtc = static_cast<const char *>(a.dt_raw) + (bL * H + head) * AS;
-        R.dtr = ld_bits(reinterpret_cast<const AT *>(dtc + min(max(dtlane, (uint32_t)max(lo, 0) * H * AS), (uint32_t)hi * H * AS)));
+        R.dtr = *(reinterpret_cast<const AT *>(dtc + min(max(dtlane, (uint32_t)max(lo, 0) * H * AS), (uint32_t)hi * H * AS)));
         const char *cbb = static_cast<const char *>(a.cb) + ((b * G + g) * (int64_t)(TL * KL) + ttw * KL) * 512 * 4;
 #pragma unroll
         for (int m = 0; m < KL; ++m)
@@ -606,7 +602,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
         // token arrays, every wave its own copy: dt, inclusive lam, dt exp(lam_end - lam)
         {
             // (softplus for every lane, then a multiply by 0 / 1: no branch around it)
-            const float dt = softplus_fast(bits_f<AT>(R.dtr) + dtb) * (lane < L && lane >= lo && lane < hi ? 1.0f : 0.0f);
+            const float dt = softplus_fast((float)R.dtr + dtb) * (lane < L && lane >= lo && lane < hi ? 1.0f : 0.0f);
             const float v = wave_prefix_sum(dt * A2);
             const float l2end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), L - 1));
             sTok[wv][0][lane] = dt;  // lanes >= L fill padding
