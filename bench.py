@@ -590,6 +590,38 @@ def main():
             ms_b = time_region(few_step, args.prefill_steps, torch)
             few[f"{nb}x8192"] = {"ms_per_step": round(ms_b, 4), "tok_s": round(Tb / (ms_b * 1e-3), 1)}
             log(f"prefill {nb} x 8192: {ms_b * 1e3:.1f} us/step ({Tb / (ms_b * 1e-3) / 1e6:.2f} M tok/s)")
+        # the layer's gated RMSNorm (y * SiLU(z), normalised over groups of H*P/G channels): the prefill
+        # with z and the norm weight, and the norm pass alone on its output
+        zgen = torch.Generator(device="cuda")
+        zgen.manual_seed(25)
+        z2 = torch.empty(T, d2.d_inner, dtype=bf, device="cuda").normal_(0.0, 1.0, generator=zgen)
+        nw2 = dev(synth.norm_weight(d2, 25), torch.float32)
+
+        def prefill_norm_step():
+            B.mamba2_prefill_fwd(d2, xbc2, dt2, z2, cw2, None, A2, dtb2, D2, y2, pool2, convp2, cu2, idx2, hi2, ws2,
+                                 norm_w=nw2)
+
+        def norm_step():  # in place, as mamba2_prefill_fwd applies it
+            B.mamba2_gated_rmsnorm(d2, y2, z2, nw2, y2)
+
+        for _ in range(3):
+            prefill_norm_step()
+        ms_pn = time_region(prefill_norm_step, args.prefill_steps, torch)
+        ms_norm = time_region(norm_step, args.prefill_steps, torch)
+        norm_bytes = T * d2.d_inner * (2 + 2 + 2) + d2.d_inner * 4  # y and z in, out; the weights once
+        norm_gbs = norm_bytes / (ms_norm * 1e-3) / 1e9
+        log(f"prefill with the gated norm: {ms_pn * 1e3:.1f} us/step; the norm pass {ms_norm * 1e3:.1f} us "
+            f"({norm_gbs:.0f} GB/s)")
+        with_norm = {
+            "step": "mamba2_prefill_fwd with z and the norm weight (ungated scan, then the gated RMSNorm over "
+                    "groups of H*P/G = 1024 channels, in place)",
+            "ms_per_step": round(ms_pn, 4), "tok_s": round(T / (ms_pn * 1e-3), 1),
+            "norm_us": round(ms_norm * 1e3, 2),
+            "norm_roofline": {"bound": "hbm", "kernel": "gated_norm_kernel", "achieved": round(norm_gbs, 1),
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(norm_gbs / HBM_PEAK_GBS, 4),
+                              "algorithmic_bytes_per_launch": norm_bytes},
+        }
+        del z2
         # algorithmic minimum of the whole prefill: raw bf16 xBC + dt in, bf16 y out, final fp32 states;
         # flops of the chunk length each form runs (32-token blocks fused and with a workspace, 128 without)
         pb, pf = scan_algorithmic(d2, T, 4, 2, 2, 4, chunk=32)
@@ -622,6 +654,7 @@ def main():
                          "mfma_achieved_tflops": round(pre_tfs, 2),
                          "mfma_frac": round(pre_tfs / MFMA_BF16_PEAK_TFLOPS, 4)},
             "fewer_sequences": few,
+            "with_gated_norm": with_norm,
             "unfused": {
                 "ms_per_step": round(ms_unf, 4), "tok_s": round(T / (ms_unf * 1e-3), 1),
                 "step": "conv1d_fwd (fp32 post-conv xBC) + chunk_scan_fwd with a workspace",

@@ -7,14 +7,14 @@
 //
 // HBM bound (one read of y and z, one write): one wavefront per (row, group),
 // K 4-element vectors per lane kept in registers between the sum of squares
-// (a butterfly over the wavefront) and the scaling. Rows are independent, so
-// in-place use (out == y) is allowed.
+// (a butterfly over the wavefront) and the scaling; SiLU from the hardware exp2
+// and reciprocal. Rows are independent, so in-place use (out == y) is allowed.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace m2 {
 
-template <typename YT, typename ZT, typename OT, int K>
+template <typename YT, typename ZT, typename OT, int K, bool HasZ>
 __global__ __launch_bounds__(256) void gated_norm_kernel(NormArgs a, int64_t width, int gs, int ngroups_row) {
     const int lane = threadIdx.x & 63;
     const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -22,25 +22,32 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(NormArgs a, int64_t wid
     const int64_t row = item / ngroups_row;
     const int64_t c0 = row * width + (item % ngroups_row) * gs;
     const int cw0 = (int)((item % ngroups_row) * gs);
+    // Every load (y, z and the weights) is issued before any value is used, unconditionally:
+    // lanes past the group's end read its last vector and drop the values. Loads behind
+    // per-lane branches were waited for one at a time.
+    Raw<YT, 4> yr[K];
+    Raw<ZT, 4> zr[HasZ ? K : 1];
+    f32x4 wr[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int c = min((k * 64 + lane) * 4, gs - 4);
+        yr[k].load(static_cast<const YT *>(a.y) + c0 + c);
+        if constexpr (HasZ) zr[k].load(static_cast<const ZT *>(a.z) + c0 + c);
+        wr[k] = *reinterpret_cast<const f32x4 *>(a.w + cw0 + c);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // (else the compiler sinks the weight loads into the stores)
     float v[K][4];
     float ss = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const int c = (k * 64 + lane) * 4;
-        if (c < gs) {
-            load_k<YT, 4>(static_cast<const YT *>(a.y) + c0 + c, v[k]);
-            if (a.z) {
-                float zv[4];
-                load_k<ZT, 4>(static_cast<const ZT *>(a.z) + c0 + c, zv);
+        const bool live = (k * 64 + lane) * 4 < gs;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v[k][j] *= silu_f(zv[j]);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[k][j] = 0.0f;
+        for (int j = 0; j < 4; ++j) {
+            float g = yr[k][j];
+            if constexpr (HasZ) g *= silu_fast(zr[k][j]);
+            v[k][j] = live ? g : 0.0f;
+            ss += v[k][j] * v[k][j];
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ss += v[k][j] * v[k][j];
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
@@ -49,13 +56,18 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(NormArgs a, int64_t wid
     for (int k = 0; k < K; ++k) {
         const int c = (k * 64 + lane) * 4;
         if (c < gs) {
-            float w[4], o[4];
-            load_k<float, 4>(a.w + cw0 + c, w);
+            float o[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = v[k][j] * scale * w[j];
+            for (int j = 0; j < 4; ++j) o[j] = v[k][j] * scale * wr[k][j];
             store_k<OT, 4>(static_cast<OT *>(a.out) + c0 + c, o);
         }
     }
+}
+
+template <typename YT, typename ZT, typename OT, int K>
+static void launch_gn_kz(const NormArgs &a, int64_t width, int gs, int ng, dim3 grid, hipStream_t stream) {
+    if (a.z) hipLaunchKernelGGL((gated_norm_kernel<YT, ZT, OT, K, true>), grid, dim3(256), 0, stream, a, width, gs, ng);
+    else hipLaunchKernelGGL((gated_norm_kernel<YT, ZT, OT, K, false>), grid, dim3(256), 0, stream, a, width, gs, ng);
 }
 
 template <typename YT, typename ZT, typename OT>
@@ -64,11 +76,11 @@ static hipError_t launch_gn_k(const NormArgs &a, int64_t width, int gs, hipStrea
     const int64_t items = (int64_t)a.rows * ng;
     dim3 grid((unsigned)((items + 3) / 4));
     const int k = (gs + 255) / 256;
-    if (k <= 1) hipLaunchKernelGGL((gated_norm_kernel<YT, ZT, OT, 1>), grid, dim3(256), 0, stream, a, width, gs, ng);
-    else if (k <= 2) hipLaunchKernelGGL((gated_norm_kernel<YT, ZT, OT, 2>), grid, dim3(256), 0, stream, a, width, gs, ng);
-    else if (k <= 4) hipLaunchKernelGGL((gated_norm_kernel<YT, ZT, OT, 4>), grid, dim3(256), 0, stream, a, width, gs, ng);
-    else if (k <= 8) hipLaunchKernelGGL((gated_norm_kernel<YT, ZT, OT, 8>), grid, dim3(256), 0, stream, a, width, gs, ng);
-    else if (k <= 16) hipLaunchKernelGGL((gated_norm_kernel<YT, ZT, OT, 16>), grid, dim3(256), 0, stream, a, width, gs, ng);
+    if (k <= 1) launch_gn_kz<YT, ZT, OT, 1>(a, width, gs, ng, grid, stream);
+    else if (k <= 2) launch_gn_kz<YT, ZT, OT, 2>(a, width, gs, ng, grid, stream);
+    else if (k <= 4) launch_gn_kz<YT, ZT, OT, 4>(a, width, gs, ng, grid, stream);
+    else if (k <= 8) launch_gn_kz<YT, ZT, OT, 8>(a, width, gs, ng, grid, stream);
+    else if (k <= 16) launch_gn_kz<YT, ZT, OT, 16>(a, width, gs, ng, grid, stream);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

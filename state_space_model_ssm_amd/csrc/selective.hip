@@ -249,6 +249,10 @@ __global__ __launch_bounds__(256) void selective_update_kernel(SelUpdateArgs a, 
     load_k<AT, 4>(static_cast<const AT *>(a.B) + ((int64_t)row * G + g) * N + n0, b4);
     load_k<AT, 4>(static_cast<const AT *>(a.C) + ((int64_t)row * G + g) * N + n0, c4);
     const float uu = (float)static_cast<const AT *>(a.u)[ro];
+    // D and z are read here with the other loads, unconditionally (from u when absent, the
+    // value then unused): read after the state update they cost two more round trips
+    const float Dv = (a.D ? a.D : a.A)[a.D ? ch : 0];
+    const float zv = (float)static_cast<const AT *>(a.z ? a.z : a.u)[ro];
     float dl = (float)static_cast<const AT *>(a.delta)[ro] + (a.delta_bias ? a.delta_bias[ch] : 0.0f);
     if (a.delta_softplus) dl = softplus_fast(dl);
     const float du = dl * uu;
@@ -261,8 +265,8 @@ __global__ __launch_bounds__(256) void selective_update_kernel(SelUpdateArgs a, 
     acc = lane_group_sum<LPC>(acc);
     store_k<ST, 4>(hp, h);
     if (sg == 0) {
-        const float sk = a.D ? a.D[ch] * uu : 0.0f;
-        const float gt = a.z ? silu_fast((float)static_cast<const AT *>(a.z)[ro]) : 1.0f;
+        const float sk = a.D ? Dv * uu : 0.0f;
+        const float gt = a.z ? silu_fast(zv) : 1.0f;
         Io<OT>::put(y, ro, (acc + sk) * gt);
     }
 }
