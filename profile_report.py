@@ -182,10 +182,12 @@ def profiles():
                  "fused_scan_kernel (conv of x inside the scan) + conv_state_kernel; the unfused detail is "
                  "conv_fwd_kernel + conv_state_kernel, then chunk_scan_fwd with a workspace (the prep and scan "
                  "kernels instantiated with conv width 1) or without (chunk_scan_fast_kernel). "
-                 "conv_state_kernel rows include both conv paths' launches.",
+                 "conv_state_kernel rows include both conv paths' launches. gated_norm_kernel is the layer's "
+                 "gated RMSNorm (y * SiLU(z) over groups of 1024 channels) that mamba2_prefill_fwd runs after "
+                 "the scan when given the norm weight.",
          "kernels": [(FUSED_SCAN, scan_b), (FUSED_PREP, prep_b), (BLOCK_SCAN, None), (BLOCK_PREP, None),
                      ("chunk_scan_fast_kernel", blk_b), ("conv_fwd_kernel", T * cdim * (2 + 4)),
-                     ("conv_state_kernel", None)],
+                     ("conv_state_kernel", None), ("gated_norm_kernel", T * H * P * (2 + 2 + 2) + H * P * 4)],
          "records": [("mamba2_prefill_fwd", [FUSED_SCAN, FUSED_PREP], fus + ["conv.hip"]),
                      ("chunk_scan_fwd", [BLOCK_SCAN, BLOCK_PREP], fus),
                      ("chunk_scan_fast_kernel", ["chunk_scan_fast_kernel"], ["scan.hip", "common.hpp",
