@@ -628,7 +628,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
         const bool more = c0 + L < end;
         const int cl_next = more ? (int)((end - c0 - L) < L ? (end - c0 - L) : L) : 0;
-        if (more) prefetch(c0 + L, cl_next);
+        // With chunks of 128 (eight waves) the next chunk's loads go out after this chunk's outputs:
+        // issued before them, the outputs' own x loads (and the stores) queued behind the whole
+        // prefetch, and the state loop below waited for all of it (1.32 -> 1.14 ms at 4 x 8192
+        // together with the unrolled state loop). With chunks of 64 the registers do not allow it.
+        constexpr bool kLatePrefetch = NW == 8;
+        if (!kLatePrefetch && more) prefetch(c0 + L, cl_next);
 
         // ---------------- outputs of this wave's t-tiles
 #pragma unroll
@@ -702,6 +707,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             }
         }
 
+        if (kLatePrefetch && more) prefetch(c0 + L, cl_next);
+
         // ---------------- carried state: H <- exp(lam_end) H + sum_s (x dt w)^T B   (3-term split)
         {
             const float dec = __builtin_amdgcn_exp2f(l2p[L - 1]);
@@ -709,8 +716,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             for (int pt = 0; pt < TP; ++pt)
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) Hacc[pt][j] *= dec;
-#pragma unroll 1
-            for (int m = 0; m < KL; ++m) {
+            auto state_step = [&](int m) __attribute__((always_inline)) {
                 bf16x8 bh[NJ], bl[NJ];
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
@@ -734,6 +740,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                         Hacc[pt][j] = mma(xl, bh[j], Hacc[pt][j]);
                     }
                 }
+            };
+            // unrolled with chunks of 128 (a loop made the compiler wait there for every load in
+            // flight, the prefetch included); a loop with chunks of 64, whose registers are full
+            if constexpr (kLatePrefetch) {
+#pragma unroll
+                for (int m = 0; m < KL; ++m) state_step(m);
+            } else {
+#pragma unroll 1
+                for (int m = 0; m < KL; ++m) state_step(m);
             }
         }
         if (more && wave == 0) token_arrays(buf ^ 1, cl_next);
