@@ -156,29 +156,45 @@ __global__ __launch_bounds__(256) void conv_state_kernel(ConvFwdArgs a, int64_t 
     const int seq = blockIdx.y;
     const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (c0 >= cdim) return;
-    const int slot = pool_slot(a.idx[seq], a.num_slots, a.err, c0 == 0);
-    if (slot < 0) return;
+    // Two round trips: the sequence's slot, bounds and flag together, then every row either
+    // source may give (the cached rows and the sequence's last W - 1 tokens, clamped into the
+    // packed rows), selected once they arrive. Loads behind the slot test and behind per-row
+    // branches went out one round trip after another.
+    const int idx = a.idx[seq];
     const int64_t start = a.cu[seq];
     const int64_t len = a.cu[seq + 1] - start;
     const bool init = a.has_init && a.has_init[seq];
+    const int slot = pool_slot(idx, a.num_slots, a.err, c0 == 0);
+    if (slot < 0) return;
     ST *cache = static_cast<ST *>(a.pool) + (int64_t)slot * (W - 1) * cdim + c0;
     const AT *in = static_cast<const AT *>(a.xbc) + c0;
-    float old[W - 1][8], nw[W - 1][8];
+    Raw<ST, 8> oldr[W - 1];
+    Raw<AT, 8> tokr[W - 1];
 #pragma unroll
-    for (int k = 0; k < W - 1; ++k) {
-        if (init) load_k<ST, 8>(cache + k * cdim, old[k]);
-        else
+    for (int k = 0; k < W - 1; ++k) oldr[k].load(cache + k * cdim);
+    if (a.T > 0) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) old[k][j] = 0.0f;
+        for (int k = 0; k < W - 1; ++k) {
+            int64_t row = start + len + k - (W - 1);  // the token for entry k when len + k >= W - 1
+            row = row < 0 ? 0 : (row > a.T - 1 ? a.T - 1 : row);
+            tokr[k].load(in + row * cdim);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < W - 1; ++k)
+#pragma unroll
+            for (int i = 0; i < Raw<AT, 8>::kW; ++i) tokr[k].w[i] = 0u;  // (never selected: no tokens)
     }
+    float nw[W - 1][8];
 #pragma unroll
     for (int k = 0; k < W - 1; ++k) {
         const int64_t pos = len + k;  // index into [old cache (W-1) || tokens (len)]
-        if (pos < W - 1) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) nw[k][j] = old[pos][j];
-        } else {
-            load_k<AT, 8>(in + (start + pos - (W - 1)) * cdim, nw[k]);
+        for (int j = 0; j < 8; ++j) {
+            float o = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < W - 1; ++kk) o = (pos == kk && init) ? oldr[kk][j] : o;
+            nw[k][j] = pos < W - 1 ? o : tokr[k][j];
         }
     }
 #pragma unroll
