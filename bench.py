@@ -4,9 +4,10 @@
 Primary line (the metric's decode half): decode tokens/s of one layer step
 (conv1d_update + state_update) for 256 sequences drawn from a 512-slot bf16
 state pool (128 heads x headdim 64 x d_state 128, 8 groups). The prefill half
-(mamba2_prefill_fwd over 4 x 8192 tokens, chunk 128, bf16 inputs, fp32 state;
-the unfused conv1d_fwd + chunk_scan_fwd pair alongside) is reported in the
-same JSON line under "prefill".
+(mamba2_prefill_fwd over 4 x 8192 tokens, bf16 inputs, fp32 state; the layer's
+chunk_size is 128, the fused path cuts 32-token blocks; the unfused conv1d_fwd +
+chunk_scan_fwd pair and the prefill with the gated RMSNorm alongside) is
+reported in the same JSON line under "prefill".
 
 Inputs are seeded synthetic tensors already resident in HBM when timing
 starts. Per-kernel durations come from HIP events on the stream the kernels
