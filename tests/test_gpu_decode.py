@@ -21,6 +21,10 @@ CASES = {
     "mid-n64": (Dims(8, 32, 64, 2, 4, 64, BF16, BF16, BF16), 7, 11, True),
     # the full decode workload: 256 rows from a 512-slot bf16 pool
     "decode-8b": (NEMOTRON_H_8B, 256, 512, False),
+    # small batches where a workgroup takes a whole head tile in four passes (bf16: 16 rows;
+    # fp32: 12 rows, the tile then split over two workgroups)
+    "8b-bf16-16rows": (NEMOTRON_H_8B, 16, 24, True),
+    "8b-f32state-12rows": (NEMOTRON_H_8B.with_(state_dtype=F32), 12, 20, False),
 }
 
 
