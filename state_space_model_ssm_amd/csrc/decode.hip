@@ -565,14 +565,14 @@ static hipError_t launch_cu_c(const LayerShape &s, const ConvUpdateArgs &a, hipS
     return hipGetLastError();
 }
 
-// 8 channels per thread, or 4 when that grid would have under 1,024 workgroups (small
-// batches: the kernel is one round trip, so more, shorter threads finish sooner; measured on
-// the 48-layer decode stack as one graph: concurrency 1, 0.333 -> 0.294 ms per step; 16,
-// 0.847 -> 0.803; 64, 2.45 -> 2.40; unchanged at 256 rows)
+// 8 channels per thread, or 4 when that grid would have under 4,096 workgroups (up to about
+// 800 rows at 8B dims: the kernel is one round trip, so more, shorter threads finish sooner;
+// measured on the 48-layer decode stack as one graph: concurrency 1, 0.333 -> 0.294 ms per
+// step; 16, 0.847 -> 0.803; 64, 2.45 -> 2.40; and on the 256-row decode step, 192.0 -> 190.1 us)
 template <typename AT, typename ST, typename XT>
 static hipError_t launch_cu_w(const LayerShape &s, const ConvUpdateArgs &a, hipStream_t stream) {
     const int64_t wg8 = (s.cdim() / 8 + 255) / 256 * (int64_t)a.batch;
-    return wg8 < 1024 ? launch_cu_c<AT, ST, XT, 4>(s, a, stream) : launch_cu_c<AT, ST, XT, 8>(s, a, stream);
+    return wg8 < 4096 ? launch_cu_c<AT, ST, XT, 4>(s, a, stream) : launch_cu_c<AT, ST, XT, 8>(s, a, stream);
 }
 
 template <typename AT, typename ST>
